@@ -1,0 +1,151 @@
+"""Plain CPU oracle for the DDTree tree-verify step (ctypes over ddt_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg use it to produce expected values.  Nothing in the library's
+product path imports it, and it shares no code with the HIP library.
+
+Functions take and return numpy arrays (host memory).  Attention results are
+float64.  See ddt_oracle.h for the definitions and the passages they follow.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ddt_oracle.c")
+LIB_PATH = os.path.join(_HERE, "libddt_oracle.so")
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ddt_oracle.c with gcc (OpenMP, no fast-math) into LIB_PATH."""
+    if force or not os.path.exists(LIB_PATH):
+        tmp = LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+               "-fno-fast-math", "-ffp-contract=off", "-Wall", "-Wextra",
+               _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build(force=False)
+        lib = ctypes.CDLL(LIB_PATH)
+        p = ctypes.c_void_p
+        i32, i64, f32 = ctypes.c_int, ctypes.c_int64, ctypes.c_float
+        lib.ddt_oracle_tree_build.argtypes = [p, p, p, p, i32, i32, i32, i32] + [p] * 9
+        lib.ddt_oracle_verify_attn_rows.argtypes = (
+            [p, p, p, p, i64, p, i32, p, p, p, i32, i32, i32, i32, i32, f32, i64, p, p, p])
+        lib.ddt_oracle_tree_accept.argtypes = [p, p, p, p, i32, i32, p, p, p, p]
+        lib.ddt_oracle_num_threads.argtypes = []
+        for f in (lib.ddt_oracle_tree_build, lib.ddt_oracle_verify_attn_rows,
+                  lib.ddt_oracle_tree_accept, lib.ddt_oracle_num_threads):
+            f.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    return int(_load().ddt_oracle_num_threads())
+
+
+def tree_build(topk_logp, topk_ids, root_token, prefix_len, budget: int) -> dict:
+    """Best-first draft tree; returns a dict of numpy arrays (see ddt_oracle.h)."""
+    lib = _load()
+    logp, p_logp = _c(topk_logp, np.float32)
+    ids, p_ids = _c(topk_ids, np.int32)
+    root, p_root = _c(root_token, np.int32)
+    plen, p_plen = _c(prefix_len, np.int32)
+    B, D, K = logp.shape
+    Q = budget + 1
+    W = (Q + 63) // 64
+    out = {k: np.empty((B, Q), np.int32) for k in
+           ("node_token", "parent", "depth", "position", "first_child", "next_sibling")}
+    out["score"] = np.empty((B, Q), np.float32)
+    out["vis"] = np.empty((B, Q, W), np.uint64)
+    out["n_nodes"] = np.empty((B,), np.int32)
+    ptr = {k: v.ctypes.data_as(ctypes.c_void_p) for k, v in out.items()}
+    rc = lib.ddt_oracle_tree_build(
+        p_logp, p_ids, p_root, p_plen, B, D, K, budget,
+        ptr["node_token"], ptr["parent"], ptr["depth"], ptr["position"],
+        ptr["first_child"], ptr["next_sibling"], ptr["score"], ptr["vis"], ptr["n_nodes"])
+    if rc != 0:
+        raise ValueError("oracle tree_build rejected its arguments")
+    return out
+
+
+def verify_attn(q_lat, q_pe, c_kv, k_pe, req_to_slot, prefix_len, n_nodes, vis,
+                sm_scale: float, rows=None):
+    """Double-precision tree-verify attention.
+
+    Float inputs may be any dtype that upcasts exactly to float32 (float32, or a
+    bf16 tensor already converted with .float()).  Without `rows` every row is
+    evaluated and out has shape [B,Q,H,d_lat], lse [B,Q,H]; with `rows` (an
+    [n,3] array of (b, i, h)) out is [n, d_lat] and lse [n].
+    """
+    lib = _load()
+    ql, p_ql = _c(q_lat, np.float32)
+    qp, p_qp = _c(q_pe, np.float32)
+    ckv, p_ckv = _c(c_kv, np.float32)
+    kpe, p_kpe = _c(k_pe, np.float32)
+    r2s, p_r2s = _c(req_to_slot, np.int32)
+    plen, p_plen = _c(prefix_len, np.int32)
+    nn, p_nn = _c(n_nodes, np.int32)
+    vv, p_vis = _c(vis, np.uint64)
+    B, Q, H, d_lat = ql.shape
+    d_rope = qp.shape[-1]
+    num_slots = ckv.shape[0]
+    max_kv = r2s.shape[1]
+    if rows is None:
+        b, i, h = np.meshgrid(np.arange(B), np.arange(Q), np.arange(H), indexing="ij")
+        rows_arr = np.stack([b.ravel(), i.ravel(), h.ravel()], axis=1)
+        shape_out, shape_lse = (B, Q, H, d_lat), (B, Q, H)
+    else:
+        rows_arr = np.asarray(rows).reshape(-1, 3)
+        shape_out, shape_lse = (rows_arr.shape[0], d_lat), (rows_arr.shape[0],)
+    rr, p_rows = _c(rows_arr, np.int32)
+    n_rows = rr.shape[0]
+    out = np.empty((n_rows, d_lat), np.float64)
+    lse = np.empty((n_rows,), np.float64)
+    rc = lib.ddt_oracle_verify_attn_rows(
+        p_ql, p_qp, p_ckv, p_kpe, num_slots, p_r2s, max_kv, p_plen, p_nn, p_vis,
+        B, Q, H, d_lat, d_rope, float(np.float32(sm_scale)), n_rows, p_rows,
+        out.ctypes.data_as(ctypes.c_void_p), lse.ctypes.data_as(ctypes.c_void_p))
+    if rc != 0:
+        raise ValueError("oracle verify_attn rejected its arguments")
+    return out.reshape(shape_out), lse.reshape(shape_lse)
+
+
+def tree_accept(node_token, parent, n_nodes, target_argmax) -> dict:
+    """Greedy follow-the-verified-tree acceptance; returns a dict of arrays."""
+    lib = _load()
+    tok, p_tok = _c(node_token, np.int32)
+    par, p_par = _c(parent, np.int32)
+    nn, p_nn = _c(n_nodes, np.int32)
+    tgt, p_tgt = _c(target_argmax, np.int32)
+    B, Q = tok.shape
+    out = {"accept_len": np.empty((B,), np.int32),
+           "accept_nodes": np.empty((B, Q), np.int32),
+           "out_tokens": np.empty((B, Q), np.int32),
+           "next_root": np.empty((B,), np.int32)}
+    ptr = {k: v.ctypes.data_as(ctypes.c_void_p) for k, v in out.items()}
+    rc = lib.ddt_oracle_tree_accept(p_tok, p_par, p_nn, p_tgt, B, Q,
+                                    ptr["accept_len"], ptr["accept_nodes"],
+                                    ptr["out_tokens"], ptr["next_root"])
+    if rc != 0:
+        raise ValueError("oracle tree_accept rejected its arguments")
+    return out

@@ -1,0 +1,92 @@
+/*
+ * ddt_oracle.h -- plain CPU oracle for the DDTree tree-verify step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This header and ddt_oracle.c are the slow,
+ * obviously-correct reference that the GPU library is checked against.  Only
+ * the test suite, the smoke check and the benchmark's CPU-baseline leg may load
+ * it.  It shares no code, header, table or constant with the HIP library.
+ *
+ * Sources ("the pages"):
+ *   [P1] "The Architecture of a Thousand-Parameter Decision: Designing a Native
+ *        DDTree Inference Engine for Kimi K2.6", section "What to Build New"
+ *        (items 2 and 3: tree-verify MLA attention, GPU tree builder).
+ *   [P2] "The Architecture of Closure: How a Summary Message Encodes an Entire
+ *        Engineering Session", section "The Table as a Decision Artifact"
+ *        (tree_build / verify_attn / tree_accept / composition test).
+ *   [P3] "The Milestone Message: When an AI Summarizes Its Own Engineering
+ *        Triumph", sections "MLA (Multi-Head Latent Attention)" and
+ *        "Architectural Abstraction" (absorbed form; positions L+depth and the
+ *        ones|visibility mask).
+ *
+ * Every function returns 0 on success, -1 on an invalid argument.
+ * All arrays are host memory, row-major, owned by the caller.
+ */
+#ifndef DDT_ORACLE_H
+#define DDT_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Best-first draft-tree construction ([P1] item 3, [P2] tree_build row).
+ *
+ * in : topk_logp [B][D][K] f32 drafter log-probs per depth (rank 0 = best),
+ *      topk_ids  [B][D][K] i32, root_token [B], prefix_len [B].
+ * out: per request Q = budget+1 node slots:
+ *      node_token, parent, depth, position, first_child, next_sibling [B][Q] i32,
+ *      score [B][Q] f32, vis [B][Q][W] u64 (W = ceil(Q/64)), n_nodes [B]. */
+int ddt_oracle_tree_build(const float* topk_logp, const int32_t* topk_ids,
+                          const int32_t* root_token, const int32_t* prefix_len,
+                          int B, int D, int K, int budget,
+                          int32_t* node_token, int32_t* parent, int32_t* depth,
+                          int32_t* position, int32_t* first_child,
+                          int32_t* next_sibling, float* score, uint64_t* vis,
+                          int32_t* n_nodes);
+
+/* Tree-verify attention in MLA-absorbed form, evaluated in double precision
+ * for a list of rows ([P1] item 2, [P3] "MLA").
+ *
+ * in : q_lat [B][Q][H][d_lat], q_pe [B][Q][H][d_rope] (f32; bf16 inputs are
+ *      upcast exactly by the caller), c_kv [num_slots][d_lat],
+ *      k_pe [num_slots][d_rope], req_to_slot [B][max_kv], prefix_len [B],
+ *      n_nodes [B], vis [B][Q][W], sm_scale.
+ *      rows [n_rows][3] = (b, i, h) triples to evaluate.
+ * out: out [n_rows][d_lat] f64, lse [n_rows] f64 (natural log). */
+int ddt_oracle_verify_attn_rows(const float* q_lat, const float* q_pe,
+                                const float* c_kv, const float* k_pe,
+                                int64_t num_slots, const int32_t* req_to_slot,
+                                int max_kv, const int32_t* prefix_len,
+                                const int32_t* n_nodes, const uint64_t* vis,
+                                int B, int Q, int H, int d_lat, int d_rope,
+                                float sm_scale, int64_t n_rows,
+                                const int32_t* rows, double* out, double* lse);
+
+/* All B*Q*H rows: out [B][Q][H][d_lat] f64, lse [B][Q][H] f64. */
+int ddt_oracle_verify_attn(const float* q_lat, const float* q_pe,
+                           const float* c_kv, const float* k_pe,
+                           int64_t num_slots, const int32_t* req_to_slot,
+                           int max_kv, const int32_t* prefix_len,
+                           const int32_t* n_nodes, const uint64_t* vis,
+                           int B, int Q, int H, int d_lat, int d_rope,
+                           float sm_scale, double* out, double* lse);
+
+/* Greedy follow-the-verified-tree acceptance ([P2] tree_accept row).
+ *
+ * in : node_token, parent [B][Q] (from the builder), n_nodes [B],
+ *      target_argmax [B][Q] (the target model's greedy next token at each node).
+ * out: accept_len [B], accept_nodes [B][Q], out_tokens [B][Q], next_root [B]. */
+int ddt_oracle_tree_accept(const int32_t* node_token, const int32_t* parent,
+                           const int32_t* n_nodes, const int32_t* target_argmax,
+                           int B, int Q, int32_t* accept_len,
+                           int32_t* accept_nodes, int32_t* out_tokens,
+                           int32_t* next_root);
+
+/* Number of OpenMP threads the oracle runs with (1 if built without OpenMP). */
+int ddt_oracle_num_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DDT_ORACLE_H */

@@ -1,0 +1,24 @@
+"""Shared pytest configuration.
+
+Tests marked `gpu` need an MI355X (gfx950) and the built HIP library; every
+other test runs on the CPU (oracle pins, host-side argument validation, library
+loading and symbol export)."""
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an AMD GPU and the built HIP library")
+
+
+@pytest.fixture(scope="session")
+def oracle_lib():
+    import oracle
+    oracle._load()
+    return oracle
