@@ -1,0 +1,205 @@
+"""Python binding of libddt.so, the MI355X DDTree tree-verify step.
+
+The functions below only marshal arguments: they check shapes, dtypes and
+devices of torch tensors, allocate outputs/workspace with torch (device memory
+and streams are all PyTorch is used for) and call the C entry points declared in
+include/ddt.h through ctypes on the current HIP stream.  Every step of the
+computation runs in the library's HIP kernels; there is no other code path, and
+every call raises if the library is missing or returns an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libddt.so")
+
+DDT_OK, DDT_EINVAL, DDT_EUNSUPPORTED, DDT_ELAUNCH = 0, -1, -2, -3
+DDT_F32, DDT_BF16 = 0, 1
+MAX_Q = 128
+
+EXPORTED = ("ddt_version", "ddt_last_error", "ddt_tree_build",
+            "ddt_verify_attn_workspace_size", "ddt_verify_attn", "ddt_tree_accept")
+
+
+class DDTError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{msg} (code {code})")
+        self.code = code
+
+
+_lib = None
+
+
+def load_library(path: str | None = None):
+    """Load libddt.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m tree_verify_mla_ddt_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    lib.ddt_version.argtypes, lib.ddt_version.restype = [], ctypes.c_char_p
+    lib.ddt_last_error.argtypes, lib.ddt_last_error.restype = [], ctypes.c_char_p
+    lib.ddt_tree_build.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32] + [vp] * 9 + [vp]
+    lib.ddt_tree_build.restype = i32
+    lib.ddt_verify_attn_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.ddt_verify_attn_workspace_size.restype = sz
+    lib.ddt_verify_attn.argtypes = ([vp, vp, vp, vp, i64, vp, i32, vp, vp, vp, i32, i32, i32, i32,
+                                     i32, i32, f32, vp, vp, vp, sz, vp])
+    lib.ddt_verify_attn.restype = i32
+    lib.ddt_tree_accept.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp]
+    lib.ddt_tree_accept.restype = i32
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def version() -> str:
+    return load_library().ddt_version().decode()
+
+
+def last_error() -> str:
+    return load_library().ddt_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != DDT_OK:
+        raise DDTError(rc, last_error())
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype, ndim: int | None = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+    return t
+
+
+def tree_build(topk_logp: torch.Tensor, topk_ids: torch.Tensor, root_token: torch.Tensor,
+               prefix_len: torch.Tensor, budget: int, out: dict | None = None) -> dict:
+    """Best-first draft tree on the GPU (ddt_tree_build).
+
+    topk_logp [B,D,K] f32, topk_ids [B,D,K] i32, root_token [B] i32, prefix_len [B] i32.
+    Returns node_token/parent/depth/position/first_child/next_sibling [B,Q] i32,
+    score [B,Q] f32, vis [B,Q,W] int64 (bit pattern of the u64 bitsets), n_nodes [B] i32.
+    """
+    _dev(topk_logp, "topk_logp", torch.float32, 3)
+    _dev(topk_ids, "topk_ids", torch.int32, 3)
+    _dev(root_token, "root_token", torch.int32, 1)
+    _dev(prefix_len, "prefix_len", torch.int32, 1)
+    B, D, K = topk_logp.shape
+    if tuple(topk_ids.shape) != (B, D, K) or root_token.numel() != B or prefix_len.numel() != B:
+        raise ValueError("inconsistent shapes")
+    Q = budget + 1
+    W = (Q + 63) // 64
+    dev = topk_logp.device
+    if out is None:
+        out = {k: torch.empty((B, Q), dtype=torch.int32, device=dev) for k in
+               ("node_token", "parent", "depth", "position", "first_child", "next_sibling")}
+        out["score"] = torch.empty((B, Q), dtype=torch.float32, device=dev)
+        out["vis"] = torch.empty((B, Q, W), dtype=torch.int64, device=dev)
+        out["n_nodes"] = torch.empty((B,), dtype=torch.int32, device=dev)
+    rc = load_library().ddt_tree_build(
+        _ptr(topk_logp), _ptr(topk_ids), _ptr(root_token), _ptr(prefix_len), B, D, K, budget,
+        _ptr(out["node_token"]), _ptr(out["parent"]), _ptr(out["depth"]), _ptr(out["position"]),
+        _ptr(out["first_child"]), _ptr(out["next_sibling"]), _ptr(out["score"]),
+        _ptr(out["vis"]), _ptr(out["n_nodes"]), _stream())
+    _check(rc)
+    return out
+
+
+def workspace_size(B: int, Q: int, H: int, max_kv: int, d_lat: int) -> int:
+    return int(load_library().ddt_verify_attn_workspace_size(B, Q, H, max_kv, d_lat))
+
+
+def verify_attn(q_lat: torch.Tensor, q_pe: torch.Tensor, c_kv: torch.Tensor, k_pe: torch.Tensor,
+                req_to_slot: torch.Tensor, prefix_len: torch.Tensor, n_nodes: torch.Tensor,
+                vis: torch.Tensor, sm_scale: float, out: torch.Tensor | None = None,
+                lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                want_lse: bool = True):
+    """Tree-verify MLA-absorb attention (ddt_verify_attn).
+
+    q_lat [B,Q,H,d_lat], q_pe [B,Q,H,d_rope], c_kv [S,d_lat], k_pe [S,d_rope] (all bf16 or
+    all f32), req_to_slot [B,max_kv] i32, prefix_len [B] i32, n_nodes [B] i32,
+    vis [B,Q,W] int64.  Returns (out [B,Q,H,d_lat] f32, lse [B,Q,H] f32 or None)."""
+    dt = q_lat.dtype
+    if dt not in (torch.bfloat16, torch.float32):
+        raise TypeError("q_lat must be bf16 or f32")
+    _dev(q_lat, "q_lat", dt, 4)
+    _dev(q_pe, "q_pe", dt, 4)
+    _dev(c_kv, "c_kv", dt, 2)
+    _dev(k_pe, "k_pe", dt, 2)
+    _dev(req_to_slot, "req_to_slot", torch.int32, 2)
+    _dev(prefix_len, "prefix_len", torch.int32, 1)
+    _dev(n_nodes, "n_nodes", torch.int32, 1)
+    _dev(vis, "vis", torch.int64, 3)
+    B, Q, H, d_lat = q_lat.shape
+    d_rope = q_pe.shape[-1]
+    max_kv = req_to_slot.shape[1]
+    if (tuple(q_pe.shape[:3]) != (B, Q, H) or c_kv.shape[1] != d_lat or k_pe.shape[1] != d_rope
+            or k_pe.shape[0] != c_kv.shape[0] or req_to_slot.shape[0] != B
+            or tuple(vis.shape) != (B, Q, (Q + 63) // 64)):
+        raise ValueError("inconsistent shapes")
+    dev = q_lat.device
+    if out is None:
+        out = torch.empty((B, Q, H, d_lat), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Q, H), dtype=torch.float32, device=dev)
+    lib = load_library()
+    need = int(lib.ddt_verify_attn_workspace_size(B, Q, H, max_kv, d_lat))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    rc = lib.ddt_verify_attn(
+        _ptr(q_lat), _ptr(q_pe), _ptr(c_kv), _ptr(k_pe), c_kv.shape[0], _ptr(req_to_slot), max_kv,
+        _ptr(prefix_len), _ptr(n_nodes), _ptr(vis), B, Q, H, d_lat, d_rope,
+        DDT_BF16 if dt == torch.bfloat16 else DDT_F32, float(sm_scale), _ptr(out), _ptr(lse),
+        _ptr(workspace), workspace.numel(), _stream())
+    _check(rc)
+    return out, lse
+
+
+def tree_accept(node_token: torch.Tensor, parent: torch.Tensor, n_nodes: torch.Tensor,
+                target_argmax: torch.Tensor, out: dict | None = None) -> dict:
+    """Greedy follow-the-verified-tree acceptance (ddt_tree_accept)."""
+    _dev(node_token, "node_token", torch.int32, 2)
+    _dev(parent, "parent", torch.int32, 2)
+    _dev(n_nodes, "n_nodes", torch.int32, 1)
+    _dev(target_argmax, "target_argmax", torch.int32, 2)
+    B, Q = node_token.shape
+    dev = node_token.device
+    if out is None:
+        out = {"accept_len": torch.empty((B,), dtype=torch.int32, device=dev),
+               "accept_nodes": torch.empty((B, Q), dtype=torch.int32, device=dev),
+               "out_tokens": torch.empty((B, Q), dtype=torch.int32, device=dev),
+               "next_root": torch.empty((B,), dtype=torch.int32, device=dev)}
+    rc = load_library().ddt_tree_accept(
+        _ptr(node_token), _ptr(parent), _ptr(n_nodes), _ptr(target_argmax), B, Q,
+        _ptr(out["accept_len"]), _ptr(out["accept_nodes"]), _ptr(out["out_tokens"]),
+        _ptr(out["next_root"]), _stream())
+    _check(rc)
+    return out
+
+
+def default_sm_scale(d_qk_nope: int = 128, d_rope: int = 64) -> float:
+    return 1.0 / math.sqrt(d_qk_nope + d_rope)

@@ -1,0 +1,45 @@
+"""Compile the HIP sources under csrc/ into libddt.so (gfx950) next to this file.
+
+Usage: python -m tree_verify_mla_ddt_amd.build [--verbose]
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB_PATH = os.path.join(HERE, "libddt.so")
+SOURCES = ["api.hip", "tree_build.hip", "tree_accept.hip", "verify_attn.hip"]
+ARCH = os.environ.get("DDT_OFFLOAD_ARCH", "gfx950")
+
+
+def hipcc_command(out_path: str, resource_report: bool = False) -> list[str]:
+    cmd = ["hipcc", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+           "-fno-gpu-flush-denormals-to-zero",
+           # packed fp32 VALU forms are left to nobody: see the design notes
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Wall", "-I", os.path.join(HERE, "..", "include")]
+    if resource_report:
+        cmd.append("-Rpass-analysis=kernel-resource-usage")
+    cmd += [os.path.join(CSRC, s) for s in SOURCES] + ["-o", out_path]
+    return cmd
+
+
+def build(verbose: bool = False, resource_report: bool = False) -> str:
+    tmp = LIB_PATH + ".tmp"
+    res = subprocess.run(hipcc_command(tmp, resource_report), capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    log = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{log}")
+    if verbose and log.strip():
+        print(log)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    v = "--verbose" in sys.argv
+    print(build(verbose=v, resource_report="--resources" in sys.argv))

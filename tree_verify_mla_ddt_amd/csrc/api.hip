@@ -1,0 +1,138 @@
+// api.hip -- the exported C entry points of libddt.so (declared in ddt.h).
+//
+// Each entry point validates its scalar arguments and pointers on the host,
+// then enqueues its kernels on the caller's stream.  No entry point
+// synchronizes, reads device memory on the host or allocates, so all of them
+// may be captured into a HIP graph.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/ddt.h"
+#include "ddt_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return DDT_OK;
+}
+
+int launch_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(DDT_ELAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+int device_cu_count() {
+  int dev = 0, cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return cu;
+}
+
+bool attn_variant_supported(int dtype, int d_lat, int d_rope) {
+  return (dtype == DDT_BF16 && d_lat == 512 && d_rope == 64) ||
+         (dtype == DDT_BF16 && d_lat == 64 && d_rope == 16) ||
+         (dtype == DDT_F32 && d_lat == 64 && d_rope == 16);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ddt_version(void) { return "ddt 0.1.0 gfx950"; }
+
+const char* ddt_last_error(void) { return g_err; }
+
+int ddt_tree_build(const float* topk_logp, const int32_t* topk_ids, const int32_t* root_token,
+                   const int32_t* prefix_len, int B, int D, int K, int budget,
+                   int32_t* node_token, int32_t* parent, int32_t* depth, int32_t* position,
+                   int32_t* first_child, int32_t* next_sibling, float* score, uint64_t* vis,
+                   int32_t* n_nodes, void* stream) {
+  if (B < 1) return fail(DDT_EINVAL, "ddt_tree_build: B=%d must be >= 1", B);
+  if (D < 0 || D > DDT_MAX_DEPTH)
+    return fail(DDT_EINVAL, "ddt_tree_build: D=%d outside [0, %d]", D, DDT_MAX_DEPTH);
+  if (K < 0 || K > DDT_MAX_TOPK)
+    return fail(DDT_EINVAL, "ddt_tree_build: K=%d outside [0, %d]", K, DDT_MAX_TOPK);
+  if (D * K > DDT_MAX_DK)
+    return fail(DDT_EINVAL, "ddt_tree_build: D*K=%d exceeds %d", D * K, DDT_MAX_DK);
+  if (budget < 0 || budget + 1 > DDT_MAX_Q)
+    return fail(DDT_EINVAL, "ddt_tree_build: budget=%d outside [0, %d]", budget, DDT_MAX_Q - 1);
+  if ((D * K > 0 && (!topk_logp || !topk_ids)) || !root_token || !prefix_len || !node_token ||
+      !parent || !depth || !position || !first_child || !next_sibling || !score || !vis ||
+      !n_nodes)
+    return fail(DDT_EINVAL, "ddt_tree_build: NULL array argument");
+  const hipError_t e = ddt::launch_tree_build(
+      topk_logp, topk_ids, root_token, prefix_len, B, D, K, budget + 1, node_token, parent,
+      depth, position, first_child, next_sibling, score, vis, n_nodes,
+      static_cast<hipStream_t>(stream));
+  return launch_status(e, "ddt_tree_build");
+}
+
+size_t ddt_verify_attn_workspace_size(int B, int Q, int H, int max_kv, int d_lat) {
+  if (B < 1 || Q < 1 || H < 1 || max_kv < 1 || d_lat < 1) return 0;
+  return ddt::plan_verify_attn(B, Q, H, max_kv, d_lat, device_cu_count()).ws_bytes;
+}
+
+int ddt_verify_attn(const void* q_lat, const void* q_pe, const void* c_kv, const void* k_pe,
+                    int64_t num_slots, const int32_t* req_to_slot, int max_kv,
+                    const int32_t* prefix_len, const int32_t* n_nodes, const uint64_t* vis,
+                    int B, int Q, int H, int d_lat, int d_rope, int dtype, float sm_scale,
+                    float* out, float* lse, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  if (B < 1 || B > DDT_MAX_BATCH_ATTN)
+    return fail(DDT_EINVAL, "ddt_verify_attn: B=%d outside [1, %d]", B, DDT_MAX_BATCH_ATTN);
+  if (Q < 1 || Q > DDT_MAX_Q)
+    return fail(DDT_EINVAL, "ddt_verify_attn: Q=%d outside [1, %d]", Q, DDT_MAX_Q);
+  if (H < 1) return fail(DDT_EINVAL, "ddt_verify_attn: H=%d must be >= 1", H);
+  if (max_kv < 1) return fail(DDT_EINVAL, "ddt_verify_attn: max_kv=%d must be >= 1", max_kv);
+  if (num_slots < 1)
+    return fail(DDT_EINVAL, "ddt_verify_attn: num_slots=%lld must be >= 1", (long long)num_slots);
+  if (dtype != DDT_F32 && dtype != DDT_BF16)
+    return fail(DDT_EINVAL, "ddt_verify_attn: dtype=%d is not DDT_F32 or DDT_BF16", dtype);
+  if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY)
+    return fail(DDT_EINVAL, "ddt_verify_attn: sm_scale must be finite");
+  if (!attn_variant_supported(dtype, d_lat, d_rope))
+    return fail(DDT_EUNSUPPORTED,
+                "ddt_verify_attn: (dtype=%d, d_lat=%d, d_rope=%d) not compiled in; supported: "
+                "(bf16,512,64) (bf16,64,16) (f32,64,16)", dtype, d_lat, d_rope);
+  if (!q_lat || !q_pe || !c_kv || !k_pe || !req_to_slot || !prefix_len || !n_nodes || !vis ||
+      !out)
+    return fail(DDT_EINVAL, "ddt_verify_attn: NULL array argument");
+  const ddt::AttnPlan plan = ddt::plan_verify_attn(B, Q, H, max_kv, d_lat, device_cu_count());
+  if (!workspace || workspace_bytes < plan.ws_bytes)
+    return fail(DDT_EINVAL, "ddt_verify_attn: workspace of %zu bytes given, %zu needed",
+                workspace ? workspace_bytes : (size_t)0, plan.ws_bytes);
+  const hipError_t e = ddt::launch_verify_attn(
+      dtype, d_lat, d_rope, q_lat, q_pe, c_kv, k_pe, num_slots, req_to_slot, max_kv, prefix_len,
+      n_nodes, vis, B, Q, H, sm_scale, out, lse, workspace, plan,
+      static_cast<hipStream_t>(stream));
+  return launch_status(e, "ddt_verify_attn");
+}
+
+int ddt_tree_accept(const int32_t* node_token, const int32_t* parent, const int32_t* n_nodes,
+                    const int32_t* target_argmax, int B, int Q, int32_t* accept_len,
+                    int32_t* accept_nodes, int32_t* out_tokens, int32_t* next_root,
+                    void* stream) {
+  if (B < 1) return fail(DDT_EINVAL, "ddt_tree_accept: B=%d must be >= 1", B);
+  if (Q < 1 || Q > DDT_MAX_Q)
+    return fail(DDT_EINVAL, "ddt_tree_accept: Q=%d outside [1, %d]", Q, DDT_MAX_Q);
+  if (!node_token || !parent || !n_nodes || !target_argmax || !accept_len || !accept_nodes ||
+      !out_tokens || !next_root)
+    return fail(DDT_EINVAL, "ddt_tree_accept: NULL array argument");
+  const hipError_t e = ddt::launch_tree_accept(node_token, parent, n_nodes, target_argmax, B, Q,
+                                               accept_len, accept_nodes, out_tokens, next_root,
+                                               static_cast<hipStream_t>(stream));
+  return launch_status(e, "ddt_tree_accept");
+}
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// ddt_internal.h -- declarations shared by the HIP sources of libddt.so.
+//
+// Kernels are written for gfx950 (CDNA4): 64-lane wavefronts, MFMA matrix
+// cores, 160 KiB of LDS per compute unit.  Only the C entry points in api.hip
+// are exported; everything here has internal visibility.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ddt {
+
+constexpr int kWave = 64;
+
+// Launchers: enqueue on `stream`, return the launch status.  Arguments were
+// validated by the C entry points.
+hipError_t launch_tree_build(const float* topk_logp, const int32_t* topk_ids,
+                             const int32_t* root_token, const int32_t* prefix_len,
+                             int B, int D, int K, int Q, int32_t* node_token,
+                             int32_t* parent, int32_t* depth, int32_t* position,
+                             int32_t* first_child, int32_t* next_sibling,
+                             float* score, uint64_t* vis, int32_t* n_nodes,
+                             hipStream_t stream);
+
+hipError_t launch_tree_accept(const int32_t* node_token, const int32_t* parent,
+                              const int32_t* n_nodes, const int32_t* target_argmax,
+                              int B, int Q, int32_t* accept_len,
+                              int32_t* accept_nodes, int32_t* out_tokens,
+                              int32_t* next_root, hipStream_t stream);
+
+// Verify attention: rows of a request are (node, head) pairs, row = i*H + h.
+// The key range of every 128-row tile is split across a fixed grid of
+// workgroups (see verify_attn.hip); partial results go to the workspace and a
+// merge kernel combines them.
+struct AttnPlan {
+  int grid;          // attention workgroups (multiple of 8)
+  int row_tiles;     // ceil(Q*H / 128)
+  size_t ws_bytes;   // workspace bytes needed
+};
+AttnPlan plan_verify_attn(int B, int Q, int H, int max_kv, int d_lat, int num_cu);
+
+hipError_t launch_verify_attn(int dtype, int d_lat, int d_rope, const void* q_lat,
+                              const void* q_pe, const void* c_kv, const void* k_pe,
+                              int64_t num_slots, const int32_t* req_to_slot,
+                              int max_kv, const int32_t* prefix_len,
+                              const int32_t* n_nodes, const uint64_t* vis, int B,
+                              int Q, int H, float sm_scale, float* out, float* lse,
+                              void* workspace, const AttnPlan& plan,
+                              hipStream_t stream);
+
+}  // namespace ddt

@@ -1,0 +1,781 @@
+// verify_attn.hip -- tree-verify attention in absorbed MLA form for gfx950.
+//
+// Computes what "The Architecture of a Thousand-Parameter Decision ..." ("What
+// to Build New", item 2) asks of the tree-verify kernel, in the absorbed form
+// of "The Milestone Message ..." ("MLA"): every tree node of every request
+// attends over the request's latent prefix (always visible) and over the tree
+// entries its visibility bitset allows (ancestors and itself, "Architectural
+// Abstraction").  Keys are the 576-wide [c_kv | k_pe] rows, values the 512-wide
+// c_kv rows, and the output stays in latent space.
+//
+// Mapping to CDNA4:
+//  * Rows of a request are (node, head) pairs, row = i*H + h, so one request is
+//    an M = Q*H by 576 query matrix against its shared keys.  A workgroup owns a
+//    tile of 128 rows and streams 32-key tiles.  Its 8 waves form 4 pairs; a
+//    pair shares 32 rows and splits both contractions in half: each wave holds
+//    half of the query dimensions (QK^T) and half of the output columns (PV),
+//    so a wave keeps 72 + 128 registers of state and two waves fit per SIMD.
+//    The two partial score blocks of a pair are summed through LDS.
+//  * One key-major LDS tile per stage serves both products.  Scores are
+//    computed transposed, S^T = K Q^T, with the 32x32x16 bf16 MFMA (fp32
+//    inputs: 32x32x2 f32): the query rows stay in registers as the B operand,
+//    the key rows are the A operand (16-byte LDS reads).  In the accumulator
+//    layout each lane then owns one row and 16 of the 32 keys -- exactly the B
+//    operand layout of O^T = V^T P^T -- so probabilities never leave registers.
+//    The V^T operand comes from the same key-major tile through the gfx950
+//    transposing LDS read (ds_read_b64_tr_b16): in each 16-lane group, lanes
+//    4e..4e+3 point at 4-column pieces of key row k0+e and lane i receives
+//    column i of keys k0..k0+3.
+//  * Tiles are loaded global -> LDS directly (16 bytes per lane, no register
+//    staging), one tile ahead, into two LDS stages; the pool slot ids of each
+//    tile are fetched two tiles ahead into a small LDS ring.
+//  * Online softmax in the exp2 domain with fp32 statistics; probabilities are
+//    rounded to bf16 (round to nearest even) for the value product.  When a
+//    tile holds a key whose weight is a sizeable share of its row's running sum
+//    (concentrated attention, short contexts), the bf16 rounding residual of
+//    the probabilities goes through a second MFMA against the same value
+//    operand, which brings the value product to ~2^-17 relative accuracy.
+//  * The mask: prefix keys are always visible; a tree key k is visible when bit
+//    k of the row's node bitset is set; keys beyond the request or with a slot
+//    id outside the pool are invisible (their tile rows hold pool row 0, which
+//    a zero probability then ignores).
+//  * Work split: the (request, row tile, key tile) space is cut into equal
+//    contiguous ranges, one per workgroup of a grid sized to the chip, so
+//    ragged prefixes stay balanced.  A row tile whose key range is cut writes
+//    normalised partial outputs plus their log-sum-exp to the workspace and a
+//    merge kernel combines them; uncut tiles write the output directly.
+//    Logical workgroup ids are remapped so that consecutive ranges (same
+//    request, same keys) land on the same XCD and share its L2.
+#include <type_traits>
+
+#include "ddt_internal.h"
+
+namespace ddt {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x4_lds_t __attribute__((__vector_size__(4 * sizeof(__bf16))));
+#define DDT_LDS __attribute__((address_space(3)))
+
+constexpr int kTileKeys = 32;
+#ifndef DDT_ATTN_SPLIT
+#define DDT_ATTN_SPLIT 2
+#endif
+constexpr int kSplit = DDT_ATTN_SPLIT;   // waves sharing one 32-row block
+constexpr int kWaves = 4 * kSplit;
+constexpr int kThreads = kWaves * kWave;
+constexpr int kRowsPerWG = 128;
+constexpr int kMaxBatch = 512;
+constexpr int kXcds = 8;
+constexpr int kRing = 3;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// A tile takes the residual pass when some key's probability exceeds this share
+// of its row's running sum (an upper bound on the key's final weight).
+constexpr float kHeavyShare = 1.0f / 64.0f;
+
+// T is the storage type: uint16_t for bf16, float for fp32.
+template <typename T, int DL, int DR>
+struct Geo {
+  static constexpr bool kBF16 = std::is_same<T, uint16_t>::value;
+  static constexpr int kElt = sizeof(T);
+  static constexpr int kDK = DL + DR;
+  static constexpr int kPerChunk = 16 / kElt;               // elements per 16-byte chunk
+  static constexpr int kLatChunks = DL / kPerChunk;         // 16-byte chunks of a latent row
+  static constexpr int kPeChunks = DR / kPerChunk;          // ... of a rope row
+  // Latent region: one key row per load instruction when a row is 64 chunks,
+  // padded to a pitch whose dword stride is 36 (mod 64) so that the 16-byte
+  // operand reads of 16 keys and the transposing reads of 4 keys hit distinct
+  // banks; smaller rows pack several keys per instruction without padding.
+  static constexpr int kKeysPerInstr = kLatChunks >= kWave ? 1 : kWave / kLatChunks;
+  static constexpr int kLatPitchB = kLatChunks >= kWave ? kLatChunks * 16 + 144 : kLatChunks * 16;
+  static constexpr int kLatPitch = kLatPitchB / kElt;       // in elements
+  static constexpr int kLatInstr = kTileKeys / kKeysPerInstr * (kLatChunks >= kWave ? kLatChunks / kWave : 1);
+  // Rope region: keys back to back; 8-chunk rows are XOR-swizzled by key.
+  static constexpr int kPeInstr = (kTileKeys * kPeChunks + kWave - 1) / kWave;
+  static constexpr int kLatBytes = kTileKeys * kLatPitchB;
+  static constexpr int kStageBytes = kLatBytes + kPeInstr * kWave * 16;
+  static constexpr int kStageElems = kStageBytes / kElt;
+  static constexpr int kInstr = kLatInstr + kPeInstr;       // load instructions per tile
+  static_assert(kLatChunks <= kWave || kLatChunks == kWave, "latent row size");
+  static constexpr int kKStep = kBF16 ? 16 : 2;             // contraction depth of one MFMA
+  static constexpr int kNK = kDK / kKStep;                  // MFMAs per 32x32 score block
+  static constexpr int kNK0 = (kNK + kSplit - 1) / kSplit;  // ... done by each wave of a group
+  static constexpr int kNCB = DL / 32;                      // 32-wide output column blocks
+  static constexpr int kNCBh = kNCB / kSplit;               // ... owned by each wave of a group
+  static constexpr int kIssuePerWave = (kInstr + kWaves - 1) / kWaves;
+  static_assert(kNCB % kSplit == 0, "column split");
+  static_assert(DL % 32 == 0 && DR % 16 == 0, "head dims");
+  static_assert(kDK % kKStep == 0, "contraction depth");
+};
+
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Eight probabilities as a bf16x8 operand; with kResidual, the bf16 rounding
+// residuals p - bf16(p) instead.
+template <bool kResidual>
+__device__ __forceinline__ bf16x8_t pack_p(const float* p) {
+  uint32_t w[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t h0 = bf16_rne(p[2 * k]), h1 = bf16_rne(p[2 * k + 1]);
+    if constexpr (kResidual) {
+      h0 = bf16_rne(p[2 * k] - bf16_to_f32(h0));
+      h1 = bf16_rne(p[2 * k + 1] - bf16_to_f32(h1));
+    }
+    w[k] = h0 | (h1 << 16);
+  }
+  return __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+}
+
+__device__ __forceinline__ int clampi(int v, int lo, int hi) {
+  return v < lo ? lo : (v > hi ? hi : v);
+}
+
+// Wave-uniform values read from LDS or derived from them are moved to scalar
+// registers so they do not occupy vector registers.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ long long uni(long long v) {
+  const int lo = __builtin_amdgcn_readfirstlane((int)(v & 0xFFFFFFFFll));
+  const int hi = __builtin_amdgcn_readfirstlane((int)(v >> 32));
+  return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
+}
+
+// Per-request quantities shared by the attention and merge kernels.
+struct ReqInfo {
+  int L;      // prefix length
+  int nb;     // tree entries
+  int nkb;    // key tiles
+  int vt;     // row tiles holding at least one live row
+};
+
+__device__ __forceinline__ ReqInfo req_info(const int32_t* prefix_len, const int32_t* n_nodes,
+                                            int b, int Q, int H, int max_kv, int RT) {
+  ReqInfo r;
+  r.L = clampi(prefix_len[b], 0, max_kv);
+  const int cap = Q < max_kv - r.L ? Q : max_kv - r.L;
+  r.nb = clampi(n_nodes[b], 0, cap);
+  r.nkb = (r.L + r.nb + kTileKeys - 1) / kTileKeys;
+  const long long live_rows = (long long)r.nb * H;
+  long long vt = (live_rows + kRowsPerWG - 1) / kRowsPerWG;
+  r.vt = (int)(vt > RT ? RT : vt);
+  return r;
+}
+
+// Exclusive prefix of work (key tiles) over requests into s_pref[0..B].
+__device__ void work_prefix(long long* s_pref, long long* s_wsum, const int32_t* prefix_len,
+                            const int32_t* n_nodes, int B, int Q, int H, int max_kv, int RT) {
+  constexpr int kPer = (kMaxBatch + kThreads - 1) / kThreads;  // requests per thread
+  const int t = threadIdx.x;
+  long long w[kPer];
+  long long mine = 0;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int b = kPer * t + k;
+    w[k] = 0;
+    if (b < B) {
+      const ReqInfo r = req_info(prefix_len, n_nodes, b, Q, H, max_kv, RT);
+      w[k] = (long long)r.vt * r.nkb;
+    }
+    mine += w[k];
+  }
+  long long incl = mine;
+  const int lane = t & 63, wv = t >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const long long o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) s_wsum[wv] = incl;
+  __syncthreads();
+  long long before = 0;
+  for (int k = 0; k < wv; ++k) before += s_wsum[k];
+  long long run = before + incl - mine;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    if (kPer * t + k < B) s_pref[kPer * t + k] = run;
+    run += w[k];
+  }
+  if (t == 0) {
+    long long tot = 0;
+    for (int k = 0; k < kWaves; ++k) tot += s_wsum[k];
+    s_pref[B] = tot;
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ long long range_start(long long g, long long W, long long G) {
+  return (g * W) / G;
+}
+// The workgroup whose range holds key tile t (0 <= t < W).
+__device__ __forceinline__ long long range_owner(long long t, long long W, long long G) {
+  return ((t + 1) * G - 1) / W;
+}
+
+template <typename T, int DL, int DR>
+struct Smem {
+  using G = Geo<T, DL, DR>;
+  alignas(16) unsigned char stage[2][G::kStageBytes];
+  int32_t slot[kRing][kTileKeys];   // pool slot of each key of a tile (0 when invalid)
+  uint32_t valid[kRing];            // bit m: key m of the tile is in range with a valid slot
+  float4 xs[kSplit > 1 ? kWaves : 1][4][kWave];  // partial scores exchanged within a group
+  long long pref[kMaxBatch + 1];
+  long long wsum[kWaves];
+};
+
+// Pool slot of key `j` of the request, or -1 when the key is past the request
+// or its slot id is outside the pool.
+__device__ __forceinline__ int32_t fetch_slot(const int32_t* __restrict__ slots_b,
+                                              int64_t num_slots, int j, int nkeys) {
+  if (j >= nkeys) return -1;
+  const int32_t s = slots_b[j];
+  return (s >= 0 && (int64_t)s < num_slots) ? s : -1;
+}
+
+// Physical chunk of logical rope chunk c of key `key` (8-chunk rows only).
+template <int kPeChunks>
+__device__ __forceinline__ int pe_swz(int c, int key) {
+  if constexpr (kPeChunks == 8) return c ^ (key & 7);
+  else return c;
+}
+
+// Enqueue the direct global->LDS loads of one key tile.  Latent instruction r
+// fills key row(s) r*kKeysPerInstr..; rope instruction r fills 64 consecutive
+// rope chunks.  Invalid keys carry slot 0 (pool row 0), which the mask ignores.
+template <typename T, int DL, int DR>
+__device__ __forceinline__ void issue_tile(unsigned char* stage, const int32_t* ring_slots,
+                                           const T* __restrict__ c_kv,
+                                           const T* __restrict__ k_pe, int wave, int lane) {
+  using G = Geo<T, DL, DR>;
+#pragma unroll
+  for (int it = 0; it < G::kIssuePerWave; ++it) {
+    const int r = wave + it * kWaves;
+    if (r >= G::kInstr) break;
+    if (r < G::kLatInstr) {
+      int key, ch;
+      unsigned char* dst;
+      if constexpr (G::kLatChunks >= kWave) {
+        constexpr int kPerKey = G::kLatChunks / kWave;
+        key = r / kPerKey;
+        ch = (r % kPerKey) * kWave + lane;
+        dst = stage + key * G::kLatPitchB + (r % kPerKey) * kWave * 16;
+      } else {
+        key = r * G::kKeysPerInstr + lane / G::kLatChunks;
+        ch = lane % G::kLatChunks;
+        dst = stage + r * kWave * 16;
+      }
+      long long row;
+      if constexpr (G::kLatChunks >= kWave) row = uni(ring_slots[key]);
+      else row = ring_slots[key];
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(c_kv + row * DL + ch * G::kPerChunk),
+                                       (DDT_LDS void*)dst, 16, 0, 0);
+    } else {
+      const int rp = r - G::kLatInstr;
+      const T* src = k_pe;                      // slack lanes past the tile
+      if constexpr (G::kPeChunks == 8) {
+        // 8 keys x 8 chunks per instruction; key & 7 == lane / 8, so the
+        // swizzled chunk depends on the lane only.
+        const int key = rp * 8 + (lane >> 3);
+        const long long row = ring_slots[key];
+        src = k_pe + row * DR + (((lane & 7) ^ (lane >> 3)) * G::kPerChunk);
+      } else {
+        const int s = rp * kWave + lane;        // rope chunk slot
+        const int key = s / G::kPeChunks;
+        const int p = s % G::kPeChunks;
+        if (key < kTileKeys) {
+          const long long row = ring_slots[key];
+          src = k_pe + row * DR + pe_swz<G::kPeChunks>(p, key) * G::kPerChunk;
+        }
+      }
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src),
+                                       (DDT_LDS void*)(stage + G::kLatBytes + rp * kWave * 16),
+                                       16, 0, 0);
+    }
+  }
+}
+
+// Query operand of one lane: row `n` of the wave, contraction slots of group g.
+template <typename T, int DL, int DR>
+struct QRegs {
+  using G = Geo<T, DL, DR>;
+  using V = typename std::conditional<G::kBF16, bf16x8_t, float>::type;
+  V q[G::kNK0];
+};
+
+template <typename T, int DL, int DR>
+__device__ __forceinline__ void load_q(QRegs<T, DL, DR>& qr, const T* __restrict__ q_lat,
+                                       const T* __restrict__ q_pe, long long row, bool valid,
+                                       int g, int half) {
+  using G = Geo<T, DL, DR>;
+#pragma unroll
+  for (int kk = 0; kk < G::kNK0; ++kk) {
+    const int step = half * G::kNK0 + kk;
+    const bool in = valid && step < G::kNK;
+    const int d = step * G::kKStep + g * (G::kBF16 ? 8 : 1);
+    if constexpr (G::kBF16) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (in) {
+        v = d < DL ? *reinterpret_cast<const uint4*>(q_lat + row * DL + d)
+                   : *reinterpret_cast<const uint4*>(q_pe + row * DR + (d - DL));
+      }
+      qr.q[kk] = __builtin_bit_cast(bf16x8_t, v);
+    } else {
+      float v = 0.0f;
+      if (in) v = d < DL ? q_lat[row * DL + d] : q_pe[row * DR + (d - DL)];
+      qr.q[kk] = v;
+    }
+  }
+}
+
+// Two transposing reads give the 8-key A operand of one value-product MFMA:
+// keys k0..k0+3 and k0+8..k0+11 of column `col` for this lane.
+__device__ __forceinline__ bf16x8_t read_vt(const uint16_t* kt, int pitch, int k0, int col0,
+                                            int lane) {
+  const int j = lane & 15;
+  const uint16_t* pa = kt + (k0 + (j >> 2)) * pitch + col0 + 4 * (j & 3);
+  const uint16_t* pb = pa + 8 * pitch;
+  const bf16x4_lds_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((DDT_LDS bf16x4_lds_t*)pa);
+  const bf16x4_lds_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((DDT_LDS bf16x4_lds_t*)pb);
+  const uint2 ulo = __builtin_bit_cast(uint2, lo);
+  const uint2 uhi = __builtin_bit_cast(uint2, hi);
+  return __builtin_bit_cast(bf16x8_t, make_uint4(ulo.x, ulo.y, uhi.x, uhi.y));
+}
+
+// Workgroup barrier that orders LDS traffic only: it does not wait for the
+// direct global->LDS tile loads still in flight (a __syncthreads() fence would).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads/writes are done
+  __asm__ __volatile__("s_barrier" ::: "memory");
+}
+
+// Lanes 0..31 of wave 0 store the slot ids of one tile (invalid -> pool row 0)
+// and its validity bitmask.
+__device__ __forceinline__ void publish_slots(int32_t* ring, uint32_t* valid, int32_t slot,
+                                              int key) {
+  ring[key] = slot < 0 ? 0 : slot;
+  const uint64_t ok = __ballot(slot >= 0);
+  if (key == 0) *valid = (uint32_t)ok;
+}
+
+// Visibility of the 32 keys of a tile for one row: bit m is set when key m is a
+// prefix key (tree index jb + m < 0) or the row's bitset has bit jb + m.
+// jb > -32 (the tile reaches the tree part) and jb < 128.
+__device__ __forceinline__ uint32_t tree_window(uint64_t v0, uint64_t v1, int jb) {
+  if (jb < 0) {
+    const int pc = -jb;  // 1..31 prefix keys at the start of the tile
+    return ((1u << pc) - 1u) | (uint32_t)(v0 << pc);
+  }
+  if (jb == 0) return (uint32_t)v0;
+  if (jb < 64) return (uint32_t)((v0 >> jb) | (v1 << (64 - jb)));
+  return (uint32_t)(v1 >> (jb - 64));
+}
+
+template <typename T, int DL, int DR>
+__global__ __launch_bounds__(kThreads) void verify_attn_kernel(
+    const T* __restrict__ q_lat, const T* __restrict__ q_pe, const T* __restrict__ c_kv,
+    const T* __restrict__ k_pe, int64_t num_slots, const int32_t* __restrict__ req_to_slot,
+    int max_kv, const int32_t* __restrict__ prefix_len, const int32_t* __restrict__ n_nodes,
+    const uint64_t* __restrict__ vis, int B, int Q, int H, int RT, float sm_scale,
+    float* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o,
+    float* __restrict__ ws_lse) {
+  using G = Geo<T, DL, DR>;
+  __shared__ Smem<T, DL, DR> sm;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int rb = wave / kSplit;    // 32-row block of the group
+  const int half = wave % kSplit;  // which share of the dims / columns this wave owns
+  const int n = lane & 31;     // row of the block (and key index of the A operand)
+  const int g = lane >> 5;     // lane group
+  const int W = (Q + 63) >> 6;
+  const long long QH = (long long)Q * H;
+
+  work_prefix(sm.pref, sm.wsum, prefix_len, n_nodes, B, Q, H, max_kv, RT);
+  const long long Wtot = uni(sm.pref[B]);
+  const long long Gn = gridDim.x;
+  const long long gid = (long long)(blockIdx.x % kXcds) * (Gn / kXcds) + blockIdx.x / kXcds;
+  const long long start = range_start(gid, Wtot, Gn);
+  const long long end = range_start(gid + 1, Wtot, Gn);
+  if (start >= end) return;
+
+  // Request holding `start`: the last b with pref[b] <= start (it has work).
+  int b = 0;
+  {
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (sm.pref[mid] <= start) lo = mid; else hi = mid - 1;
+    }
+    b = uni(lo);
+  }
+  const float sl2 = sm_scale * kLog2e;
+
+  long long pos = start;
+  while (pos < end) {
+    while (uni(sm.pref[b + 1]) <= pos) ++b;
+    b = uni(b);
+    const ReqInfo ri = req_info(prefix_len, n_nodes, b, Q, H, max_kv, RT);
+    const long long off = pos - uni(sm.pref[b]);
+    const int rt = (int)(off / ri.nkb);
+    const int kb0 = (int)(off % ri.nkb);
+    const long long left = end - pos;
+    const int kb1 = (long long)(ri.nkb - kb0) < left ? ri.nkb : kb0 + (int)left;
+    const bool complete = kb0 == 0 && kb1 == ri.nkb;
+    const long long slot = 2 * gid + (pos == start ? 0 : 1);
+    pos += kb1 - kb0;
+
+    const int nkeys = ri.L + ri.nb;
+    const int32_t* slots_b = req_to_slot + (long long)b * max_kv;
+
+    // This lane's row.
+    const long long r_loc = (long long)rt * kRowsPerWG + rb * 32 + n;  // row in request
+    const int node = (int)(r_loc / H);
+    const bool row_exists = r_loc < QH;
+    const bool row_live = row_exists && node < ri.nb;
+    const bool wave_live = __ballot(row_live) != 0;
+    const long long grow = (long long)b * QH + r_loc;                    // global row
+    QRegs<T, DL, DR> qr;
+    load_q<T, DL, DR>(qr, q_lat, q_pe, grow, row_live, g, half);
+    uint64_t v0 = 0, v1 = 0;
+    if (row_live) {
+      const uint64_t* vr = vis + ((long long)b * Q + node) * W;
+      v0 = vr[0];
+      if (W > 1) v1 = vr[1];
+    }
+
+    f32x16_t o[G::kNCBh];
+#pragma unroll
+    for (int cb = 0; cb < G::kNCBh; ++cb) o[cb] = f32x16_t{};
+    float m_run = -INFINITY, l_run = 0.0f;
+
+    // Prologue: slot ids of the first two tiles, then the first tile.
+    if (tid < kTileKeys) {
+      publish_slots(sm.slot[kb0 % kRing], &sm.valid[kb0 % kRing],
+                    fetch_slot(slots_b, num_slots, kb0 * kTileKeys + tid, nkeys), tid);
+      if (kb0 + 1 < kb1)
+        publish_slots(sm.slot[(kb0 + 1) % kRing], &sm.valid[(kb0 + 1) % kRing],
+                      fetch_slot(slots_b, num_slots, (kb0 + 1) * kTileKeys + tid, nkeys), tid);
+    }
+    __syncthreads();
+    issue_tile<T, DL, DR>(sm.stage[0], sm.slot[kb0 % kRing], c_kv, k_pe, wave, lane);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    for (int kb = kb0; kb < kb1; ++kb) {
+      const int st = (kb - kb0) & 1;
+      int32_t ahead = -1;
+      if (tid < kTileKeys && kb + 2 < kb1)
+        ahead = fetch_slot(slots_b, num_slots, (kb + 2) * kTileKeys + tid, nkeys);
+      if (kb + 1 < kb1)
+        issue_tile<T, DL, DR>(sm.stage[st ^ 1], sm.slot[(kb + 1) % kRing], c_kv, k_pe, wave, lane);
+
+      // Partial S^T = K Q^T over this wave's half of the contraction.
+      const T* kt = reinterpret_cast<const T*>(sm.stage[st]);
+      const T* kpe = reinterpret_cast<const T*>(sm.stage[st] + G::kLatBytes);
+      f32x16_t s = f32x16_t{};
+      if (wave_live) {
+#pragma unroll
+        for (int kk = 0; kk < G::kNK0; ++kk) {
+          const int step = half * G::kNK0 + kk;
+          if (step >= G::kNK) break;
+          const int d = step * G::kKStep + g * (G::kBF16 ? 8 : 1);  // this lane's dims
+          const T* src;
+          if (d < DL) {
+            src = kt + n * G::kLatPitch + d;
+          } else {
+            const int dp = d - DL;
+            src = kpe + n * DR + pe_swz<G::kPeChunks>(dp / G::kPerChunk, n) * G::kPerChunk +
+                  dp % G::kPerChunk;
+          }
+          if constexpr (G::kBF16) {
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(src);
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr.q[kk], s, 0, 0, 0);
+          } else {
+            s = __builtin_amdgcn_mfma_f32_32x32x2f32(*src, qr.q[kk], s, 0, 0, 0);
+          }
+        }
+        if constexpr (kSplit > 1) {
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4)
+            sm.xs[wave][i4][lane] =
+                make_float4(s[4 * i4], s[4 * i4 + 1], s[4 * i4 + 2], s[4 * i4 + 3]);
+        }
+      }
+      if constexpr (kSplit > 1) lds_barrier();
+      if (wave_live) {
+        if constexpr (kSplit > 1) {
+          // Full scores: own share plus the partner's (addition commutes, so both
+          // waves of the pair hold bit-identical sums).
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const float4 o4 = sm.xs[wave ^ 1][i4][lane];
+            s[4 * i4] += o4.x;
+            s[4 * i4 + 1] += o4.y;
+            s[4 * i4 + 2] += o4.z;
+            s[4 * i4 + 3] += o4.w;
+          }
+        }
+        // Lane owns row n and keys 8*(i/4) + 4*g + (i%4), i = 0..15.
+        const int key0 = kb * kTileKeys;
+        uint32_t okm = (uint32_t)uni((int)sm.valid[kb % kRing]);
+        if (key0 + kTileKeys > ri.L) okm &= tree_window(v0, v1, key0 - ri.L);
+        okm >>= 4 * g;  // now bit 8*(i/4) + (i%4) is key m of register i
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          s[i] = ((okm >> (8 * (i >> 2) + (i & 3))) & 1u) ? s[i] * sl2 : -INFINITY;
+          mx = fmaxf(mx, s[i]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        float alpha = 1.0f, mref = 0.0f;
+        if (m_new != -INFINITY) {
+          alpha = exp2f(m_run - m_new);
+          mref = m_new;
+        }
+        float psum = 0.0f;
+        float p[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          p[i] = exp2f(s[i] - mref);
+          psum += p[i];
+        }
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+        if (alpha != 1.0f) {
+#pragma unroll
+          for (int cb = 0; cb < G::kNCBh; ++cb) o[cb] *= alpha;
+        }
+        // O^T += V^T P^T.
+        if constexpr (G::kBF16) {
+          const bf16x8_t p0 = pack_p<false>(p);
+          const bf16x8_t p1 = pack_p<false>(p + 8);
+          // Residual pass when some row of this wave has a heavy key here.
+          float pmax = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) pmax = fmaxf(pmax, p[i]);
+          pmax = fmaxf(pmax, __shfl_xor(pmax, 32));
+          const float lrow = l_run + __shfl_xor(l_run, 32);
+          const bool heavy = __ballot(pmax > kHeavyShare * lrow) != 0;
+          const int colh = 16 * ((lane >> 4) & 1);
+#pragma unroll
+          for (int cb = 0; cb < G::kNCBh; ++cb) {
+            const int c0 = (half * G::kNCBh + cb) * 32 + colh;
+            const bf16x8_t a0 = read_vt(kt, G::kLatPitch, 4 * g, c0, lane);
+            const bf16x8_t a1 = read_vt(kt, G::kLatPitch, 16 + 4 * g, c0, lane);
+            o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, p0, o[cb], 0, 0, 0);
+            o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, p1, o[cb], 0, 0, 0);
+          }
+          if (heavy) {
+            const bf16x8_t r0 = pack_p<true>(p);
+            const bf16x8_t r1 = pack_p<true>(p + 8);
+#pragma unroll
+            for (int cb = 0; cb < G::kNCBh; ++cb) {
+              const int c0 = (half * G::kNCBh + cb) * 32 + colh;
+              const bf16x8_t a0 = read_vt(kt, G::kLatPitch, 4 * g, c0, lane);
+              const bf16x8_t a1 = read_vt(kt, G::kLatPitch, 16 + 4 * g, c0, lane);
+              o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, r0, o[cb], 0, 0, 0);
+              o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, r1, o[cb], 0, 0, 0);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int cb = 0; cb < G::kNCBh; ++cb) {
+            const int c0 = (half * G::kNCBh + cb) * 32;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int m = 8 * (i >> 2) + 4 * g + (i & 3);
+              o[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kt[m * G::kLatPitch + c0 + n], p[i],
+                                                            o[cb], 0, 0, 0);
+            }
+          }
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's tile loads have landed in LDS
+      if (tid < kTileKeys && kb + 2 < kb1)
+        publish_slots(sm.slot[(kb + 2) % kRing], &sm.valid[(kb + 2) % kRing], ahead, tid);
+      __syncthreads();
+    }
+
+    // Normalise and write: this lane holds row n, columns
+    // (half*kNCBh + cb)*32 + 8*t + 4*g + {0..3} in o[cb][4t..4t+3].
+    const float l = l_run + __shfl_xor(l_run, 32);
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    const float lse_v = l > 0.0f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+    float* dst = nullptr;
+    float* dst_lse = nullptr;
+    if (complete) {
+      if (row_exists) {
+        dst = out + grow * DL;
+        dst_lse = lse ? lse + grow : nullptr;
+      }
+    } else if (row_live) {
+      const long long rr = slot * kRowsPerWG + rb * 32 + n;
+      dst = ws_o + rr * DL;
+      dst_lse = ws_lse + rr;
+    }
+    if (dst) {
+#pragma unroll
+      for (int cb = 0; cb < G::kNCBh; ++cb) {
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) {
+          float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (row_live)
+            v = make_float4(o[cb][4 * t4] * inv, o[cb][4 * t4 + 1] * inv,
+                            o[cb][4 * t4 + 2] * inv, o[cb][4 * t4 + 3] * inv);
+          *reinterpret_cast<float4*>(dst + (half * G::kNCBh + cb) * 32 + 8 * t4 + 4 * g) = v;
+        }
+      }
+      if (dst_lse && g == 0 && half == 0) *dst_lse = row_live ? lse_v : -INFINITY;
+    }
+  }
+}
+
+// Combines the partial results of row tiles whose key range was cut, and writes
+// the padding output of row tiles with no live row.
+template <int DL>
+__global__ __launch_bounds__(kThreads) void verify_merge_kernel(
+    const int32_t* __restrict__ prefix_len, const int32_t* __restrict__ n_nodes, int B, int Q,
+    int H, int RT, int max_kv, int grid_attn, float* __restrict__ out, float* __restrict__ lse,
+    const float* __restrict__ ws_o, const float* __restrict__ ws_lse) {
+  __shared__ long long s_pref[kMaxBatch + 1];
+  __shared__ long long s_wsum[kWaves];
+  work_prefix(s_pref, s_wsum, prefix_len, n_nodes, B, Q, H, max_kv, RT);
+  const int u = blockIdx.x;
+  const int b = u / RT, rt = u % RT;
+  const ReqInfo ri = req_info(prefix_len, n_nodes, b, Q, H, max_kv, RT);
+  const long long QH = (long long)Q * H;
+  const long long r_begin = (long long)rt * kRowsPerWG;
+  const int nrows = (int)((QH - r_begin) < kRowsPerWG ? (QH - r_begin) : kRowsPerWG);
+  const long long Wtot = s_pref[B];
+  const long long Gn = grid_attn;
+  constexpr int kChunks = DL / 4;
+  constexpr int kRowsPerPass = kThreads / kChunks > 0 ? kThreads / kChunks : 1;
+  const int chunk = threadIdx.x % kChunks;
+  const int rsub = threadIdx.x / kChunks;
+
+  const bool has_work = rt < ri.vt;
+  long long g_first = 0, g_last = 0, S_u = 0;
+  if (has_work) {
+    S_u = s_pref[b] + (long long)rt * ri.nkb;
+    g_first = range_owner(S_u, Wtot, Gn);
+    g_last = range_owner(S_u + ri.nkb - 1, Wtot, Gn);
+    if (g_first == g_last) return;  // written directly by the attention kernel
+  }
+  for (int r0 = 0; r0 < nrows; r0 += kRowsPerPass) {
+    const int rr = r0 + rsub;
+    if (rsub >= kRowsPerPass || rr >= nrows) continue;
+    const long long r_loc = r_begin + rr;
+    const long long grow = (long long)b * QH + r_loc;
+    const bool live = has_work && (int)(r_loc / H) < ri.nb;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float lse_tot = -INFINITY;
+    if (live) {
+      // Each contributing workgroup (one with a non-empty range) wrote its
+      // partial for this tile into slot 2g when the tile holds the start of its
+      // range, else into slot 2g+1.
+      float mx = -INFINITY;
+      for (long long gg = g_first; gg <= g_last; ++gg) {
+        const long long s0 = range_start(gg, Wtot, Gn);
+        if (s0 == range_start(gg + 1, Wtot, Gn)) continue;
+        const long long sl = 2 * gg + (s0 >= S_u ? 0 : 1);
+        mx = fmaxf(mx, ws_lse[sl * kRowsPerWG + rr]);
+      }
+      if (mx != -INFINITY) {
+        float z = 0.0f;
+        for (long long gg = g_first; gg <= g_last; ++gg) {
+          const long long s0 = range_start(gg, Wtot, Gn);
+          if (s0 == range_start(gg + 1, Wtot, Gn)) continue;
+          const long long sl = 2 * gg + (s0 >= S_u ? 0 : 1);
+          z += expf(ws_lse[sl * kRowsPerWG + rr] - mx);
+        }
+        lse_tot = mx + logf(z);
+        for (long long gg = g_first; gg <= g_last; ++gg) {
+          const long long s0 = range_start(gg, Wtot, Gn);
+          if (s0 == range_start(gg + 1, Wtot, Gn)) continue;
+          const long long sl = 2 * gg + (s0 >= S_u ? 0 : 1);
+          const float w = expf(ws_lse[sl * kRowsPerWG + rr] - lse_tot);
+          const float4 v = *reinterpret_cast<const float4*>(
+              ws_o + (sl * kRowsPerWG + rr) * DL + chunk * 4);
+          acc.x += w * v.x;
+          acc.y += w * v.y;
+          acc.z += w * v.z;
+          acc.w += w * v.w;
+        }
+      }
+    }
+    *reinterpret_cast<float4*>(out + grow * DL + chunk * 4) = acc;
+    if (lse && chunk == 0) lse[grow] = lse_tot;
+  }
+}
+
+template <typename T, int DL, int DR>
+hipError_t launch_impl(const void* q_lat, const void* q_pe, const void* c_kv, const void* k_pe,
+                       int64_t num_slots, const int32_t* req_to_slot, int max_kv,
+                       const int32_t* prefix_len, const int32_t* n_nodes, const uint64_t* vis,
+                       int B, int Q, int H, float sm_scale, float* out, float* lse,
+                       void* workspace, const AttnPlan& plan, hipStream_t stream) {
+  float* ws_o = static_cast<float*>(workspace);
+  float* ws_lse = ws_o + (size_t)2 * plan.grid * kRowsPerWG * DL;
+  hipLaunchKernelGGL((verify_attn_kernel<T, DL, DR>), dim3(plan.grid), dim3(kThreads), 0,
+                     stream, static_cast<const T*>(q_lat), static_cast<const T*>(q_pe),
+                     static_cast<const T*>(c_kv), static_cast<const T*>(k_pe), num_slots,
+                     req_to_slot, max_kv, prefix_len, n_nodes, vis, B, Q, H, plan.row_tiles,
+                     sm_scale, out, lse, ws_o, ws_lse);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((verify_merge_kernel<DL>), dim3(B * plan.row_tiles), dim3(kThreads), 0,
+                     stream, prefix_len, n_nodes, B, Q, H, plan.row_tiles, max_kv, plan.grid,
+                     out, lse, ws_o, ws_lse);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+AttnPlan plan_verify_attn(int B, int Q, int H, int max_kv, int d_lat, int num_cu) {
+  AttnPlan p;
+  const long long rows = (long long)Q * H;
+  p.row_tiles = (int)((rows + kRowsPerWG - 1) / kRowsPerWG);
+  const long long nkb = ((long long)max_kv + kTileKeys - 1) / kTileKeys;
+  const long long work = (long long)B * p.row_tiles * nkb;
+  // One resident workgroup per CU (register-bound); at least a few key tiles each.
+  long long g = num_cu > 0 ? num_cu : 256;
+  const long long by_work = (work + 3) / 4;
+  if (by_work < g) g = by_work;
+  g = ((g + kXcds - 1) / kXcds) * kXcds;
+  if (g < kXcds) g = kXcds;
+  p.grid = (int)g;
+  p.ws_bytes = (size_t)2 * p.grid * kRowsPerWG * ((size_t)d_lat + 1) * sizeof(float);
+  return p;
+}
+
+hipError_t launch_verify_attn(int dtype, int d_lat, int d_rope, const void* q_lat,
+                              const void* q_pe, const void* c_kv, const void* k_pe,
+                              int64_t num_slots, const int32_t* req_to_slot, int max_kv,
+                              const int32_t* prefix_len, const int32_t* n_nodes,
+                              const uint64_t* vis, int B, int Q, int H, float sm_scale,
+                              float* out, float* lse, void* workspace, const AttnPlan& plan,
+                              hipStream_t stream) {
+  // dtype: 0 = f32, 1 = bf16 (validated by the caller).
+  if (dtype == 1 && d_lat == 512 && d_rope == 64)
+    return launch_impl<uint16_t, 512, 64>(q_lat, q_pe, c_kv, k_pe, num_slots, req_to_slot,
+                                          max_kv, prefix_len, n_nodes, vis, B, Q, H, sm_scale,
+                                          out, lse, workspace, plan, stream);
+  if (dtype == 1 && d_lat == 64 && d_rope == 16)
+    return launch_impl<uint16_t, 64, 16>(q_lat, q_pe, c_kv, k_pe, num_slots, req_to_slot,
+                                         max_kv, prefix_len, n_nodes, vis, B, Q, H, sm_scale,
+                                         out, lse, workspace, plan, stream);
+  if (dtype == 0 && d_lat == 64 && d_rope == 16)
+    return launch_impl<float, 64, 16>(q_lat, q_pe, c_kv, k_pe, num_slots, req_to_slot, max_kv,
+                                      prefix_len, n_nodes, vis, B, Q, H, sm_scale, out, lse,
+                                      workspace, plan, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ddt
