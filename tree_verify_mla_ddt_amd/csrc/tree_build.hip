@@ -12,9 +12,11 @@
 // whose unsigned order is the pop order: the fp32 score mapped to an
 // order-preserving integer in the high word, then 0xFFFF - parent and
 // 0xFFFF - rank in the low word, so a wave-wide max is "highest score, then
-// lowest parent index, then lowest rank".  Every pop is one 64-bit max
-// reduction plus one ballot to find the owning slot; the popped slot is reused
-// for the child and a fresh slot takes the sibling.
+// lowest parent index, then lowest rank".  Every pop is one DPP max reduction
+// plus one ballot to find the owning slot; the popped slot is reused for the
+// child and a fresh slot takes the sibling.  Node i's fields live in lane i%64
+// (register i/64) and are read back with readlane; its visibility row is its
+// parent's row plus its own bit, set when it is popped.
 #include "ddt_internal.h"
 
 namespace ddt {
@@ -38,13 +40,43 @@ __device__ __forceinline__ uint64_t frontier_key(float s, int parent, int rank) 
          ((uint64_t)(uint32_t)(0xFFFF - parent) << 16) | (uint64_t)(uint32_t)(0xFFFF - rank);
 }
 
+// One DPP step of a 64-bit max: combine with the lane selected by CTRL (rows
+// outside ROW_MASK, and lanes whose source is out of range, keep their value).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t max_dpp(uint64_t v) {
+  const int lo = (int)(uint32_t)v, hi = (int)(uint32_t)(v >> 32);
+  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROW_MASK, 0xF, false);
+  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROW_MASK, 0xF, false);
+  const uint64_t o = ((uint64_t)ohi << 32) | olo;
+  return o > v ? o : v;
+}
+
+// Wave-wide max: pair swaps, quad swaps, half-row and row mirrors give every
+// lane its row's max; two row broadcasts carry it to lane 63.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const uint64_t o = __shfl_xor(v, off);
-    v = o > v ? o : v;
-  }
-  return v;
+  v = max_dpp<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v = max_dpp<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v = max_dpp<0x141, 0xF>(v);  // row_half_mirror
+  v = max_dpp<0x140, 0xF>(v);  // row_mirror
+  v = max_dpp<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
+  v = max_dpp<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ int read_i(int v0, int v1, int idx) {
+  const int a = __builtin_amdgcn_readlane(v0, idx & 63);
+  const int b = __builtin_amdgcn_readlane(v1, idx & 63);
+  return idx < 64 ? a : b;
+}
+__device__ __forceinline__ float read_f(float v0, float v1, int idx) {
+  return __int_as_float(read_i(__float_as_int(v0), __float_as_int(v1), idx));
+}
+__device__ __forceinline__ uint64_t read_u64(uint64_t v0, uint64_t v1, int idx) {
+  const uint32_t lo = (uint32_t)read_i((int)(uint32_t)v0, (int)(uint32_t)v1, idx);
+  const uint32_t hi = (uint32_t)read_i((int)(uint32_t)(v0 >> 32), (int)(uint32_t)(v1 >> 32), idx);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 __global__ __launch_bounds__(kWave) void tree_build_kernel(
@@ -56,10 +88,7 @@ __global__ __launch_bounds__(kWave) void tree_build_kernel(
     float* __restrict__ score, uint64_t* __restrict__ vis, int32_t* __restrict__ n_nodes) {
   __shared__ float s_logp[kMaxDK];
   __shared__ int32_t s_ids[kMaxDK];
-  __shared__ int32_t s_par[kMaxQ];
-  __shared__ int32_t s_dep[kMaxQ];
-  __shared__ int32_t s_tok[kMaxQ];
-  __shared__ float s_sc[kMaxQ];
+  __shared__ unsigned long long s_kids[kMaxQ][2];  // children of each node, as bitsets
 
   const int b = blockIdx.x;
   const int lane = threadIdx.x;
@@ -69,24 +98,32 @@ __global__ __launch_bounds__(kWave) void tree_build_kernel(
     s_logp[t] = topk_logp[in0 + t];
     s_ids[t] = topk_ids[in0 + t];
   }
-  if (lane == 0) {
-    s_par[0] = -1;
-    s_dep[0] = 0;
-    s_tok[0] = root_token[b];
-    s_sc[0] = 0.0f;
-  }
+  s_kids[lane][0] = s_kids[lane][1] = 0;
+  s_kids[lane + kWave][0] = s_kids[lane + kWave][1] = 0;
   __syncthreads();
+
+  // Node fields: node `lane` in the *0 registers, node `lane + 64` in the *1.
+  int par0 = -1, par1 = -1, dep0 = -1, dep1 = -1, tok0 = -1, tok1 = -1;
+  float sc0 = -INFINITY, sc1 = -INFINITY;
+  uint64_t va0 = 0, vb0 = 0, va1 = 0, vb1 = 0;  // visibility words 0 and 1
+  if (lane == 0) {
+    par0 = -1;
+    dep0 = 0;
+    tok0 = root_token[b];
+    sc0 = 0.0f;
+    va0 = 1;
+  }
 
   // Frontier slot s lives in lane (s & 63), register (s >> 6); key 0 = empty.
   uint64_t key0 = 0, key1 = 0;
-  int dep0 = 0, dep1 = 0;  // depth of the candidate held in the slot
-  int used = 0;            // slots handed out so far (never exceeds n <= Q)
+  int fd0 = 0, fd1 = 0;  // depth of the candidate held in the slot
+  int used = 0;          // slots handed out so far (never exceeds n <= Q)
   if (D >= 1 && K >= 1) {
     const float s = __fadd_rn(0.0f, s_logp[0]);
     if (s > -INFINITY) {
       if (lane == 0) {
         key0 = frontier_key(s, 0, 0);
-        dep0 = 1;
+        fd0 = 1;
       }
       used = 1;
     }
@@ -100,13 +137,22 @@ __global__ __launch_bounds__(kWave) void tree_build_kernel(
     const uint64_t m1 = __ballot(key1 == best);
     const int slot = m0 ? (__ffsll((unsigned long long)m0) - 1)
                         : (64 + __ffsll((unsigned long long)m1) - 1);
-    const int d0 = __shfl(dep0, slot & 63);
-    const int d1 = __shfl(dep1, slot & 63);
-    const int cdep = slot < 64 ? d0 : d1;
+    const int cdep = read_i(fd0, fd1, slot);
     const float csc = unorder_bits((uint32_t)(best >> 32));
     const int cpar = 0xFFFF - (int)((best >> 16) & 0xFFFFu);
     const int crank = 0xFFFF - (int)(best & 0xFFFFu);
     const int i = n++;
+
+    // The new node: fields into its owner lane, visibility = parent's + self.
+    const uint64_t pva = read_u64(va0, va1, cpar);
+    const uint64_t pvb = read_u64(vb0, vb1, cpar);
+    const int ctok = s_ids[(cdep - 1) * K + crank];
+    if (lane == (i & 63)) {
+      const uint64_t nva = pva | (i < 64 ? (1ull << i) : 0ull);
+      const uint64_t nvb = pvb | (i >= 64 ? (1ull << (i - 64)) : 0ull);
+      if (i < 64) { par0 = cpar; dep0 = cdep; tok0 = ctok; sc0 = csc; va0 = nva; vb0 = nvb; }
+      else        { par1 = cpar; dep1 = cdep; tok1 = ctok; sc1 = csc; va1 = nva; vb1 = nvb; }
+    }
 
     // Offer the new node's rank-0 child and its next-ranked sibling.
     uint64_t kc = 0, ks = 0;
@@ -115,17 +161,10 @@ __global__ __launch_bounds__(kWave) void tree_build_kernel(
       if (s > -INFINITY) kc = frontier_key(s, i, 0);
     }
     if (crank + 1 < K) {
-      const float s = __fadd_rn(s_sc[cpar], s_logp[(cdep - 1) * K + crank + 1]);
+      const float psc = read_f(sc0, sc1, cpar);
+      const float s = __fadd_rn(psc, s_logp[(cdep - 1) * K + crank + 1]);
       if (s > -INFINITY) ks = frontier_key(s, cpar, crank + 1);
     }
-    if (lane == 0) {
-      s_par[i] = cpar;
-      s_dep[i] = cdep;
-      s_tok[i] = s_ids[(cdep - 1) * K + crank];
-      s_sc[i] = csc;
-    }
-    __syncthreads();
-
     int slot_a = slot, slot_b = -1, dep_a = 0, dep_b = cdep;
     uint64_t key_a = 0, key_b = 0;
     if (kc) {
@@ -140,40 +179,47 @@ __global__ __launch_bounds__(kWave) void tree_build_kernel(
       dep_a = cdep;
     }
     if (lane == (slot_a & 63)) {
-      if (slot_a < 64) { key0 = key_a; dep0 = dep_a; } else { key1 = key_a; dep1 = dep_a; }
+      if (slot_a < 64) { key0 = key_a; fd0 = dep_a; } else { key1 = key_a; fd1 = dep_a; }
     }
     if (slot_b >= 0 && lane == (slot_b & 63)) {
-      if (slot_b < 64) { key0 = key_b; dep0 = dep_b; } else { key1 = key_b; dep1 = dep_b; }
+      if (slot_b < 64) { key0 = key_b; fd0 = dep_b; } else { key1 = key_b; fd1 = dep_b; }
     }
   }
+
+  // Children bitsets, then the links: first child = lowest child index; next
+  // sibling = lowest child of the same parent above this node.
+  if (lane > 0 && lane < n) atomicOr(&s_kids[par0][lane >> 6], 1ull << (lane & 63));
+  if (lane + kWave < n) atomicOr(&s_kids[par1][1], 1ull << lane);
   __syncthreads();
 
-  // Derived arrays, one node per lane (two passes for Q > 64).
   const int W = (Q + 63) >> 6;
   const int32_t L = prefix_len[b];
-  for (int i = lane; i < Q; i += kWave) {
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int i = lane + k * kWave;
+    if (i >= Q) break;
     const size_t o = (size_t)b * Q + i;
     if (i < n) {
-      const int p = s_par[i], d = s_dep[i];
-      int fc = -1, ns = -1;
-      for (int c = i + 1; c < n; ++c)
-        if (s_par[c] == i) { fc = c; break; }
-      if (i > 0)
-        for (int c = i + 1; c < n; ++c)
-          if (s_par[c] == p) { ns = c; break; }
-      uint64_t v0 = 0, v1 = 0;
-      for (int a = i; a >= 0; a = s_par[a]) {
-        if (a < 64) v0 |= 1ull << a; else v1 |= 1ull << (a - 64);
+      const int p = k ? par1 : par0, d = k ? dep1 : dep0;
+      const unsigned long long c0 = s_kids[i][0], c1 = s_kids[i][1];
+      int fc = c0 ? __ffsll(c0) - 1 : (c1 ? 64 + __ffsll(c1) - 1 : -1);
+      int ns = -1;
+      if (i > 0) {
+        unsigned long long s0 = s_kids[p][0], s1 = s_kids[p][1];
+        // keep siblings with index > i
+        if (i < 63) s0 &= ~0ull << (i + 1); else s0 = 0;
+        if (i >= 64) s1 &= (i - 64 < 63) ? (~0ull << (i - 63)) : 0ull;
+        ns = s0 ? __ffsll(s0) - 1 : (s1 ? 64 + __ffsll(s1) - 1 : -1);
       }
-      node_token[o] = s_tok[i];
+      node_token[o] = k ? tok1 : tok0;
       parent[o] = p;
       depth[o] = d;
       position[o] = (int32_t)((uint32_t)L + (uint32_t)d);
       first_child[o] = fc;
       next_sibling[o] = ns;
-      score[o] = s_sc[i];
-      vis[o * W] = v0;
-      if (W > 1) vis[o * W + 1] = v1;
+      score[o] = k ? sc1 : sc0;
+      vis[o * W] = k ? va1 : va0;
+      if (W > 1) vis[o * W + 1] = k ? vb1 : vb0;
     } else {
       node_token[o] = parent[o] = depth[o] = position[o] = -1;
       first_child[o] = next_sibling[o] = -1;

@@ -29,8 +29,10 @@
 //  * Tiles are loaded global -> LDS directly (16 bytes per lane, no register
 //    staging), one tile ahead, into two LDS stages; the pool slot ids of each
 //    tile are fetched two tiles ahead into a small LDS ring.
-//  * Online softmax in the exp2 domain with fp32 statistics; probabilities are
-//    rounded to bf16 (round to nearest even) for the value product.  When a
+//  * Online softmax in the exp2 domain with fp32 statistics and a lazily moved
+//    reference max (accumulators are rescaled only when a row's max grows by
+//    more than 2^8, so in steady state there is no per-tile rescale); the
+//    probabilities are rounded to bf16 (round to nearest even) for the value product.  When a
 //    tile holds a key whose weight is a sizeable share of its row's running sum
 //    (concentrated attention, short contexts), the bf16 rounding residual of
 //    the probabilities goes through a second MFMA against the same value
@@ -69,11 +71,17 @@ constexpr int kRowsPerWG = 128;
 constexpr int kMaxBatch = 512;
 constexpr int kXcds = 8;
 constexpr int kRing = 3;
+constexpr int kMergeThreads = 256;
+constexpr int kMergeRows = 16;           // rows per merge workgroup
+constexpr int kMaxGrid = 1024;           // upper bound of the attention grid
+constexpr int kMinTilesPerWG = 8;        // key tiles per workgroup before splitting further
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // A tile takes the residual pass when some key's probability exceeds this share
 // of its row's running sum (an upper bound on the key's final weight).
 constexpr float kHeavyShare = 1.0f / 64.0f;
+// Reference-max slack of the online softmax, in log2 units.
+constexpr float kRescaleLog2 = 8.0f;
 
 // T is the storage type: uint16_t for bf16, float for fp32.
 template <typename T, int DL, int DR>
@@ -167,10 +175,12 @@ __device__ __forceinline__ ReqInfo req_info(const int32_t* prefix_len, const int
   return r;
 }
 
-// Exclusive prefix of work (key tiles) over requests into s_pref[0..B].
+// Exclusive prefix of work (key tiles) over requests into s_pref[0..B]; called
+// by all kBlock threads of a workgroup.
+template <int kBlock>
 __device__ void work_prefix(long long* s_pref, long long* s_wsum, const int32_t* prefix_len,
                             const int32_t* n_nodes, int B, int Q, int H, int max_kv, int RT) {
-  constexpr int kPer = (kMaxBatch + kThreads - 1) / kThreads;  // requests per thread
+  constexpr int kPer = (kMaxBatch + kBlock - 1) / kBlock;  // requests per thread
   const int t = threadIdx.x;
   long long w[kPer];
   long long mine = 0;
@@ -203,7 +213,7 @@ __device__ void work_prefix(long long* s_pref, long long* s_wsum, const int32_t*
   }
   if (t == 0) {
     long long tot = 0;
-    for (int k = 0; k < kWaves; ++k) tot += s_wsum[k];
+    for (int k = 0; k < kBlock / kWave; ++k) tot += s_wsum[k];
     s_pref[B] = tot;
   }
   __syncthreads();
@@ -224,6 +234,7 @@ struct Smem {
   int32_t slot[kRing][kTileKeys];   // pool slot of each key of a tile (0 when invalid)
   uint32_t valid[kRing];            // bit m: key m of the tile is in range with a valid slot
   float4 xs[kSplit > 1 ? kWaves : 1][4][kWave];  // partial scores exchanged within a group
+  uint64_t visrow[kRowsPerWG][2];   // visibility bitset of each row's tree node
   long long pref[kMaxBatch + 1];
   long long wsum[kWaves];
 };
@@ -244,90 +255,71 @@ __device__ __forceinline__ int pe_swz(int c, int key) {
   else return c;
 }
 
-// Enqueue the direct global->LDS loads of one key tile.  Latent instruction r
-// fills key row(s) r*kKeysPerInstr..; rope instruction r fills 64 consecutive
-// rope chunks.  Invalid keys carry slot 0 (pool row 0), which the mask ignores.
+// Enqueue the direct global->LDS loads of one key tile.  With 64-chunk latent
+// rows, wave w loads latent rows of keys kLatInstr/kWaves*w.. (one row per
+// instruction, slot read as a scalar) and, for w < kPeInstr, one instruction of
+// 8 keys x 8 rope chunks; otherwise instructions are dealt round-robin.
+// Invalid keys carry slot 0 (pool row 0), which the mask ignores.
 template <typename T, int DL, int DR>
 __device__ __forceinline__ void issue_tile(unsigned char* stage, const int32_t* ring_slots,
                                            const T* __restrict__ c_kv,
                                            const T* __restrict__ k_pe, int wave, int lane) {
   using G = Geo<T, DL, DR>;
+  if constexpr (G::kLatChunks == kWave && G::kPeChunks == 8 && G::kLatInstr % kWaves == 0) {
+    constexpr int kPerWave = G::kLatInstr / kWaves;
 #pragma unroll
-  for (int it = 0; it < G::kIssuePerWave; ++it) {
-    const int r = wave + it * kWaves;
-    if (r >= G::kInstr) break;
-    if (r < G::kLatInstr) {
-      int key, ch;
-      unsigned char* dst;
-      if constexpr (G::kLatChunks >= kWave) {
-        constexpr int kPerKey = G::kLatChunks / kWave;
-        key = r / kPerKey;
-        ch = (r % kPerKey) * kWave + lane;
-        dst = stage + key * G::kLatPitchB + (r % kPerKey) * kWave * 16;
-      } else {
-        key = r * G::kKeysPerInstr + lane / G::kLatChunks;
-        ch = lane % G::kLatChunks;
-        dst = stage + r * kWave * 16;
-      }
-      long long row;
-      if constexpr (G::kLatChunks >= kWave) row = uni(ring_slots[key]);
-      else row = ring_slots[key];
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(c_kv + row * DL + ch * G::kPerChunk),
-                                       (DDT_LDS void*)dst, 16, 0, 0);
-    } else {
-      const int rp = r - G::kLatInstr;
-      const T* src = k_pe;                      // slack lanes past the tile
-      if constexpr (G::kPeChunks == 8) {
-        // 8 keys x 8 chunks per instruction; key & 7 == lane / 8, so the
-        // swizzled chunk depends on the lane only.
-        const int key = rp * 8 + (lane >> 3);
+    for (int it = 0; it < kPerWave; ++it) {
+      const int key = wave * kPerWave + it;
+      const long long row = uni(ring_slots[key]);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(c_kv + row * DL + lane * G::kPerChunk),
+                                       (DDT_LDS void*)(stage + key * G::kLatPitchB), 16, 0, 0);
+    }
+    if (wave < G::kPeInstr) {
+      // 8 keys x 8 chunks; key & 7 == lane / 8, so the swizzled chunk depends
+      // on the lane only.
+      const int key = wave * 8 + (lane >> 3);
+      const long long row = ring_slots[key];
+      const T* src = k_pe + row * DR + (((lane & 7) ^ (lane >> 3)) * G::kPerChunk);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src),
+                                       (DDT_LDS void*)(stage + G::kLatBytes + wave * kWave * 16),
+                                       16, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int it = 0; it < G::kIssuePerWave; ++it) {
+      const int r = wave + it * kWaves;
+      if (r >= G::kInstr) break;
+      if (r < G::kLatInstr) {
+        int key, ch;
+        unsigned char* dst;
+        if constexpr (G::kLatChunks >= kWave) {
+          constexpr int kPerKey = G::kLatChunks / kWave;
+          key = r / kPerKey;
+          ch = (r % kPerKey) * kWave + lane;
+          dst = stage + key * G::kLatPitchB + (r % kPerKey) * kWave * 16;
+        } else {
+          key = r * G::kKeysPerInstr + lane / G::kLatChunks;
+          ch = lane % G::kLatChunks;
+          dst = stage + r * kWave * 16;
+        }
         const long long row = ring_slots[key];
-        src = k_pe + row * DR + (((lane & 7) ^ (lane >> 3)) * G::kPerChunk);
+        __builtin_amdgcn_global_load_lds(
+            static_cast<const void*>(c_kv + row * DL + ch * G::kPerChunk), (DDT_LDS void*)dst,
+            16, 0, 0);
       } else {
-        const int s = rp * kWave + lane;        // rope chunk slot
+        const int rp = r - G::kLatInstr;
+        const int s = rp * kWave + lane;  // rope chunk slot
         const int key = s / G::kPeChunks;
         const int p = s % G::kPeChunks;
+        const T* src = k_pe;              // slack lanes past the tile
         if (key < kTileKeys) {
           const long long row = ring_slots[key];
           src = k_pe + row * DR + pe_swz<G::kPeChunks>(p, key) * G::kPerChunk;
         }
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(src),
+                                         (DDT_LDS void*)(stage + G::kLatBytes + rp * kWave * 16),
+                                         16, 0, 0);
       }
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src),
-                                       (DDT_LDS void*)(stage + G::kLatBytes + rp * kWave * 16),
-                                       16, 0, 0);
-    }
-  }
-}
-
-// Query operand of one lane: row `n` of the wave, contraction slots of group g.
-template <typename T, int DL, int DR>
-struct QRegs {
-  using G = Geo<T, DL, DR>;
-  using V = typename std::conditional<G::kBF16, bf16x8_t, float>::type;
-  V q[G::kNK0];
-};
-
-template <typename T, int DL, int DR>
-__device__ __forceinline__ void load_q(QRegs<T, DL, DR>& qr, const T* __restrict__ q_lat,
-                                       const T* __restrict__ q_pe, long long row, bool valid,
-                                       int g, int half) {
-  using G = Geo<T, DL, DR>;
-#pragma unroll
-  for (int kk = 0; kk < G::kNK0; ++kk) {
-    const int step = half * G::kNK0 + kk;
-    const bool in = valid && step < G::kNK;
-    const int d = step * G::kKStep + g * (G::kBF16 ? 8 : 1);
-    if constexpr (G::kBF16) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (in) {
-        v = d < DL ? *reinterpret_cast<const uint4*>(q_lat + row * DL + d)
-                   : *reinterpret_cast<const uint4*>(q_pe + row * DR + (d - DL));
-      }
-      qr.q[kk] = __builtin_bit_cast(bf16x8_t, v);
-    } else {
-      float v = 0.0f;
-      if (in) v = d < DL ? q_lat[row * DL + d] : q_pe[row * DR + (d - DL)];
-      qr.q[kk] = v;
     }
   }
 }
@@ -344,13 +336,6 @@ __device__ __forceinline__ bf16x8_t read_vt(const uint16_t* kt, int pitch, int k
   const uint2 ulo = __builtin_bit_cast(uint2, lo);
   const uint2 uhi = __builtin_bit_cast(uint2, hi);
   return __builtin_bit_cast(bf16x8_t, make_uint4(ulo.x, ulo.y, uhi.x, uhi.y));
-}
-
-// Workgroup barrier that orders LDS traffic only: it does not wait for the
-// direct global->LDS tile loads still in flight (a __syncthreads() fence would).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads/writes are done
-  __asm__ __volatile__("s_barrier" ::: "memory");
 }
 
 // Lanes 0..31 of wave 0 store the slot ids of one tile (invalid -> pool row 0)
@@ -375,6 +360,309 @@ __device__ __forceinline__ uint32_t tree_window(uint64_t v0, uint64_t v1, int jb
   return (uint32_t)(v1 >> (jb - 64));
 }
 
+// Workgroup barrier that orders LDS traffic only: it does not wait for the
+// direct global->LDS tile loads still in flight (a __syncthreads() fence would).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads/writes are done
+  __asm__ __volatile__("s_barrier" ::: "memory");
+}
+
+// Everything one workgroup needs to process one row tile over a key range.
+struct Unit {
+  int b, rt, kb0, kb1, nkeys;
+  ReqInfo ri;
+  bool complete;
+  long long slot;  // workspace slot when the key range is cut
+};
+
+struct Args {
+  const void* q_lat;
+  const void* q_pe;
+  const void* c_kv;
+  const void* k_pe;
+  int64_t num_slots;
+  const int32_t* req_to_slot;
+  int max_kv;
+  const uint64_t* vis;
+  int Q, H;
+  float sl2;  // softmax scale in log2 units
+  float* out;
+  float* lse;
+  float* ws_o;
+  float* ws_lse;
+};
+
+// One row tile over key tiles [kb0, kb1) by the waves owning share HALF of the
+// contraction dimensions and output columns (compile time, so every LDS operand
+// address is one base register plus an immediate).
+template <typename T, int DL, int DR, int HALF>
+__device__ __forceinline__ void run_unit(Smem<T, DL, DR>& sm, const Args& a, const Unit& u) {
+  using G = Geo<T, DL, DR>;
+  constexpr int kStep0 = HALF * G::kNK0;
+  constexpr int kStep1 = (HALF + 1) * G::kNK0 < G::kNK ? (HALF + 1) * G::kNK0 : G::kNK;
+  constexpr int kCb0 = HALF * G::kNCBh;
+  const int tid = threadIdx.x;
+  const int wave = uni(tid >> 6);  // wave-uniform: keep it (and what derives from it) scalar
+  const int lane = tid & 63;
+  const int rb = wave / kSplit;
+  const int n = lane & 31;
+  const int g = lane >> 5;
+  const int W = (a.Q + 63) >> 6;
+  const long long QH = (long long)a.Q * a.H;
+  const T* q_lat = static_cast<const T*>(a.q_lat);
+  const T* q_pe = static_cast<const T*>(a.q_pe);
+  const T* c_kv = static_cast<const T*>(a.c_kv);
+  const T* k_pe = static_cast<const T*>(a.k_pe);
+  const int32_t* slots_b = a.req_to_slot + (long long)u.b * a.max_kv;
+
+  // This lane's row.
+  const long long r_loc = (long long)u.rt * kRowsPerWG + rb * 32 + n;  // row in request
+  const int node = (int)(r_loc / a.H);
+  const bool row_exists = r_loc < QH;
+  const bool row_live = row_exists && node < u.ri.nb;
+  const bool wave_live = __ballot(row_live) != 0;
+  const long long grow = (long long)u.b * QH + r_loc;
+
+  // Query operand: B slots of this lane's row for contraction steps of HALF.
+  using QV = typename std::conditional<G::kBF16, bf16x8_t, float>::type;
+  QV q[kStep1 - kStep0];
+#pragma unroll
+  for (int kk = 0; kk < kStep1 - kStep0; ++kk) {
+    const int d = (kStep0 + kk) * G::kKStep + g * (G::kBF16 ? 8 : 1);
+    if constexpr (G::kBF16) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (row_live)
+        v = d < DL ? *reinterpret_cast<const uint4*>(q_lat + grow * DL + d)
+                   : *reinterpret_cast<const uint4*>(q_pe + grow * DR + (d - DL));
+      q[kk] = __builtin_bit_cast(bf16x8_t, v);
+    } else {
+      float v = 0.0f;
+      if (row_live) v = d < DL ? q_lat[grow * DL + d] : q_pe[grow * DR + (d - DL)];
+      q[kk] = v;
+    }
+  }
+  if (HALF == 0 && g == 0) {
+    uint64_t v0 = 0, v1 = 0;
+    if (row_live) {
+      const uint64_t* vr = a.vis + ((long long)u.b * a.Q + node) * W;
+      v0 = vr[0];
+      if (W > 1) v1 = vr[1];
+    }
+    sm.visrow[rb * 32 + n][0] = v0;
+    sm.visrow[rb * 32 + n][1] = v1;
+  }
+
+  f32x16_t o[G::kNCBh];
+#pragma unroll
+  for (int cb = 0; cb < G::kNCBh; ++cb) o[cb] = f32x16_t{};
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  // Prologue: slot ids of the first two tiles, then the first tile.
+  if (tid < kTileKeys) {
+    publish_slots(sm.slot[u.kb0 % kRing], &sm.valid[u.kb0 % kRing],
+                  fetch_slot(slots_b, a.num_slots, u.kb0 * kTileKeys + tid, u.nkeys), tid);
+    if (u.kb0 + 1 < u.kb1)
+      publish_slots(sm.slot[(u.kb0 + 1) % kRing], &sm.valid[(u.kb0 + 1) % kRing],
+                    fetch_slot(slots_b, a.num_slots, (u.kb0 + 1) * kTileKeys + tid, u.nkeys),
+                    tid);
+  }
+  __syncthreads();
+  issue_tile<T, DL, DR>(sm.stage[0], sm.slot[u.kb0 % kRing], c_kv, k_pe, wave, lane);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  for (int kb = u.kb0; kb < u.kb1; ++kb) {
+    const int st = (kb - u.kb0) & 1;
+    // Lane-derived offsets are recomputed every tile from an opaque copy of the
+    // lane id: a handful of VALU ops instead of registers held across the loop.
+    int lane_it = lane;
+    __asm__ __volatile__("" : "+v"(lane_it));
+    const int n = lane_it & 31;
+    const int g = lane_it >> 5;
+    int32_t ahead = -1;
+    if (tid < kTileKeys && kb + 2 < u.kb1)
+      ahead = fetch_slot(slots_b, a.num_slots, (kb + 2) * kTileKeys + tid, u.nkeys);
+    if (kb + 1 < u.kb1)
+      issue_tile<T, DL, DR>(sm.stage[st ^ 1], sm.slot[(kb + 1) % kRing], c_kv, k_pe, wave,
+                            lane_it);
+
+    const T* kt = reinterpret_cast<const T*>(sm.stage[st]);
+    const T* kpe = reinterpret_cast<const T*>(sm.stage[st] + G::kLatBytes);
+    f32x16_t s = f32x16_t{};
+    if (wave_live) {
+      // Partial S^T = K Q^T over this wave's share of the contraction.
+      const T* krow = kt + n * G::kLatPitch + g * (G::kBF16 ? 8 : 1);
+      const T* prow = kpe + n * DR;
+      const int xswz = g ^ (n & 7);  // rope: physical chunk = logical chunk ^ (n & 7)
+#pragma unroll
+      for (int kk = 0; kk < kStep1 - kStep0; ++kk) {
+        constexpr int kLatSteps = DL / G::kKStep;
+        const int step = kStep0 + kk;
+        if constexpr (G::kBF16) {
+          const T* src;
+          if (step < kLatSteps) {
+            src = krow + step * 16;
+          } else if constexpr (G::kPeChunks == 8) {
+            src = prow + ((2 * (step - kLatSteps)) ^ xswz) * 8;
+          } else {
+            src = prow + (step - kLatSteps) * 16 + g * 8;
+          }
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t*>(src),
+                                                      q[kk], s, 0, 0, 0);
+        } else {
+          const T* src = step < kLatSteps ? krow + step * 2 : prow + (step - kLatSteps) * 2 + g;
+          s = __builtin_amdgcn_mfma_f32_32x32x2f32(*src, q[kk], s, 0, 0, 0);
+        }
+      }
+      if constexpr (kSplit > 1) {
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4)
+          sm.xs[wave][i4][lane_it] =
+              make_float4(s[4 * i4], s[4 * i4 + 1], s[4 * i4 + 2], s[4 * i4 + 3]);
+      }
+    }
+    if constexpr (kSplit > 1) lds_barrier();
+    if (wave_live) {
+      if constexpr (kSplit > 1) {
+        // Full scores: own share plus the partner's (addition commutes, so both
+        // waves of the pair hold bit-identical sums).
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const float4 o4 = sm.xs[wave ^ 1][i4][lane_it];
+          s[4 * i4] += o4.x;
+          s[4 * i4 + 1] += o4.y;
+          s[4 * i4 + 2] += o4.z;
+          s[4 * i4 + 3] += o4.w;
+        }
+      }
+      // Lane owns row n and keys 8*(i/4) + 4*g + (i%4), i = 0..15.
+      const int key0 = kb * kTileKeys;
+      uint32_t okm = (uint32_t)uni((int)sm.valid[kb % kRing]);
+      if (key0 + kTileKeys > u.ri.L) {
+        const uint64_t* vr = sm.visrow[rb * 32 + n];
+        okm &= tree_window(vr[0], vr[1], key0 - u.ri.L);
+      }
+      okm >>= 4 * g;  // now bit 8*(i/4) + (i%4) is key m of register i
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[i] = ((okm >> (8 * (i >> 2) + (i & 3))) & 1u) ? s[i] * a.sl2 : -INFINITY;
+        mx = fmaxf(mx, s[i]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      // Lazy rescaling: the reference max m_run moves only on the first
+      // visible key (accumulators still zero) or when the tile's max exceeds
+      // it by more than kRescaleLog2, so probabilities stay below
+      // 2^kRescaleLog2 and the accumulators are rescaled only on such jumps.
+      if (m_run == -INFINITY) m_run = mx;
+      const bool jump = mx > m_run + kRescaleLog2;
+      if (__ballot(jump) != 0) {
+        const float alpha = jump ? exp2f(m_run - mx) : 1.0f;
+        if (jump) {
+          l_run *= alpha;
+          m_run = mx;
+        }
+#pragma unroll
+        for (int cb = 0; cb < G::kNCBh; ++cb) o[cb] *= alpha;
+      }
+      const float mref = m_run == -INFINITY ? 0.0f : m_run;
+      float psum = 0.0f;
+      float p[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        p[i] = exp2f(s[i] - mref);
+        psum += p[i];
+      }
+      l_run += psum;
+      // O^T += V^T P^T over this wave's output columns.
+      if constexpr (G::kBF16) {
+        const bf16x8_t p0 = pack_p<false>(p);
+        const bf16x8_t p1 = pack_p<false>(p + 8);
+        // Residual pass when some row of this wave has a heavy key here.
+        float pmax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pmax = fmaxf(pmax, p[i]);
+        pmax = fmaxf(pmax, __shfl_xor(pmax, 32));
+        const float lrow = l_run + __shfl_xor(l_run, 32);
+        const bool heavy = __ballot(pmax > kHeavyShare * lrow) != 0;
+        // Pack the residual operands now so the fp32 probabilities die here.
+        bf16x8_t r0 = bf16x8_t{}, r1 = bf16x8_t{};
+        if (heavy) {
+          r0 = pack_p<true>(p);
+          r1 = pack_p<true>(p + 8);
+        }
+        const uint16_t* vbase = reinterpret_cast<const uint16_t*>(kt);
+        const int colh = 16 * ((lane_it >> 4) & 1);
+#pragma unroll
+        for (int cb = 0; cb < G::kNCBh; ++cb) {
+          const int c0 = (kCb0 + cb) * 32 + colh;
+          const bf16x8_t a0 = read_vt(vbase, G::kLatPitch, 4 * g, c0, lane_it);
+          const bf16x8_t a1 = read_vt(vbase, G::kLatPitch, 16 + 4 * g, c0, lane_it);
+          o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, p0, o[cb], 0, 0, 0);
+          o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, p1, o[cb], 0, 0, 0);
+        }
+        if (heavy) {
+#pragma unroll
+          for (int cb = 0; cb < G::kNCBh; ++cb) {
+            const int c0 = (kCb0 + cb) * 32 + colh;
+            const bf16x8_t a0 = read_vt(vbase, G::kLatPitch, 4 * g, c0, lane_it);
+            const bf16x8_t a1 = read_vt(vbase, G::kLatPitch, 16 + 4 * g, c0, lane_it);
+            o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, r0, o[cb], 0, 0, 0);
+            o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, r1, o[cb], 0, 0, 0);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int cb = 0; cb < G::kNCBh; ++cb) {
+          const int c0 = (kCb0 + cb) * 32;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int m = 8 * (i >> 2) + 4 * g + (i & 3);
+            o[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kt[m * G::kLatPitch + c0 + n], p[i],
+                                                          o[cb], 0, 0, 0);
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's tile loads have landed in LDS
+    if (tid < kTileKeys && kb + 2 < u.kb1)
+      publish_slots(sm.slot[(kb + 2) % kRing], &sm.valid[(kb + 2) % kRing], ahead, tid);
+    __syncthreads();
+  }
+
+  // Normalise and write: this lane holds row n, columns
+  // (kCb0 + cb)*32 + 8*t + 4*g + {0..3} in o[cb][4t..4t+3].
+  const float l = l_run + __shfl_xor(l_run, 32);
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  const float lse_v = l > 0.0f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+  float* dst = nullptr;
+  float* dst_lse = nullptr;
+  if (u.complete) {
+    if (row_exists) {
+      dst = a.out + grow * DL;
+      dst_lse = a.lse ? a.lse + grow : nullptr;
+    }
+  } else if (row_live) {
+    const long long rr = u.slot * kRowsPerWG + rb * 32 + n;
+    dst = a.ws_o + rr * DL;
+    dst_lse = a.ws_lse + rr;
+  }
+  if (dst) {
+#pragma unroll
+    for (int cb = 0; cb < G::kNCBh; ++cb) {
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4) {
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (row_live)
+          v = make_float4(o[cb][4 * t4] * inv, o[cb][4 * t4 + 1] * inv,
+                          o[cb][4 * t4 + 2] * inv, o[cb][4 * t4 + 3] * inv);
+        *reinterpret_cast<float4*>(dst + (kCb0 + cb) * 32 + 8 * t4 + 4 * g) = v;
+      }
+    }
+    if (dst_lse && g == 0 && HALF == 0) *dst_lse = row_live ? lse_v : -INFINITY;
+  }
+}
+
 template <typename T, int DL, int DR>
 __global__ __launch_bounds__(kThreads) void verify_attn_kernel(
     const T* __restrict__ q_lat, const T* __restrict__ q_pe, const T* __restrict__ c_kv,
@@ -383,20 +671,12 @@ __global__ __launch_bounds__(kThreads) void verify_attn_kernel(
     const uint64_t* __restrict__ vis, int B, int Q, int H, int RT, float sm_scale,
     float* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o,
     float* __restrict__ ws_lse) {
-  using G = Geo<T, DL, DR>;
   __shared__ Smem<T, DL, DR> sm;
+  const Args args{q_lat, q_pe, c_kv, k_pe, num_slots, req_to_slot, max_kv, vis, Q, H,
+                  sm_scale * kLog2e, out, lse, ws_o, ws_lse};
+  const int half = uni((int)(threadIdx.x >> 6) % kSplit);
 
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int rb = wave / kSplit;    // 32-row block of the group
-  const int half = wave % kSplit;  // which share of the dims / columns this wave owns
-  const int n = lane & 31;     // row of the block (and key index of the A operand)
-  const int g = lane >> 5;     // lane group
-  const int W = (Q + 63) >> 6;
-  const long long QH = (long long)Q * H;
-
-  work_prefix(sm.pref, sm.wsum, prefix_len, n_nodes, B, Q, H, max_kv, RT);
+  work_prefix<kThreads>(sm.pref, sm.wsum, prefix_len, n_nodes, B, Q, H, max_kv, RT);
   const long long Wtot = uni(sm.pref[B]);
   const long long Gn = gridDim.x;
   const long long gid = (long long)(blockIdx.x % kXcds) * (Gn / kXcds) + blockIdx.x / kXcds;
@@ -414,304 +694,118 @@ __global__ __launch_bounds__(kThreads) void verify_attn_kernel(
     }
     b = uni(lo);
   }
-  const float sl2 = sm_scale * kLog2e;
 
   long long pos = start;
   while (pos < end) {
     while (uni(sm.pref[b + 1]) <= pos) ++b;
     b = uni(b);
-    const ReqInfo ri = req_info(prefix_len, n_nodes, b, Q, H, max_kv, RT);
+    Unit u;
+    u.b = b;
+    u.ri = req_info(prefix_len, n_nodes, b, Q, H, max_kv, RT);
     const long long off = pos - uni(sm.pref[b]);
-    const int rt = (int)(off / ri.nkb);
-    const int kb0 = (int)(off % ri.nkb);
+    u.rt = (int)(off / u.ri.nkb);
+    u.kb0 = (int)(off % u.ri.nkb);
     const long long left = end - pos;
-    const int kb1 = (long long)(ri.nkb - kb0) < left ? ri.nkb : kb0 + (int)left;
-    const bool complete = kb0 == 0 && kb1 == ri.nkb;
-    const long long slot = 2 * gid + (pos == start ? 0 : 1);
-    pos += kb1 - kb0;
-
-    const int nkeys = ri.L + ri.nb;
-    const int32_t* slots_b = req_to_slot + (long long)b * max_kv;
-
-    // This lane's row.
-    const long long r_loc = (long long)rt * kRowsPerWG + rb * 32 + n;  // row in request
-    const int node = (int)(r_loc / H);
-    const bool row_exists = r_loc < QH;
-    const bool row_live = row_exists && node < ri.nb;
-    const bool wave_live = __ballot(row_live) != 0;
-    const long long grow = (long long)b * QH + r_loc;                    // global row
-    QRegs<T, DL, DR> qr;
-    load_q<T, DL, DR>(qr, q_lat, q_pe, grow, row_live, g, half);
-    uint64_t v0 = 0, v1 = 0;
-    if (row_live) {
-      const uint64_t* vr = vis + ((long long)b * Q + node) * W;
-      v0 = vr[0];
-      if (W > 1) v1 = vr[1];
-    }
-
-    f32x16_t o[G::kNCBh];
-#pragma unroll
-    for (int cb = 0; cb < G::kNCBh; ++cb) o[cb] = f32x16_t{};
-    float m_run = -INFINITY, l_run = 0.0f;
-
-    // Prologue: slot ids of the first two tiles, then the first tile.
-    if (tid < kTileKeys) {
-      publish_slots(sm.slot[kb0 % kRing], &sm.valid[kb0 % kRing],
-                    fetch_slot(slots_b, num_slots, kb0 * kTileKeys + tid, nkeys), tid);
-      if (kb0 + 1 < kb1)
-        publish_slots(sm.slot[(kb0 + 1) % kRing], &sm.valid[(kb0 + 1) % kRing],
-                      fetch_slot(slots_b, num_slots, (kb0 + 1) * kTileKeys + tid, nkeys), tid);
-    }
-    __syncthreads();
-    issue_tile<T, DL, DR>(sm.stage[0], sm.slot[kb0 % kRing], c_kv, k_pe, wave, lane);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
-    for (int kb = kb0; kb < kb1; ++kb) {
-      const int st = (kb - kb0) & 1;
-      int32_t ahead = -1;
-      if (tid < kTileKeys && kb + 2 < kb1)
-        ahead = fetch_slot(slots_b, num_slots, (kb + 2) * kTileKeys + tid, nkeys);
-      if (kb + 1 < kb1)
-        issue_tile<T, DL, DR>(sm.stage[st ^ 1], sm.slot[(kb + 1) % kRing], c_kv, k_pe, wave, lane);
-
-      // Partial S^T = K Q^T over this wave's half of the contraction.
-      const T* kt = reinterpret_cast<const T*>(sm.stage[st]);
-      const T* kpe = reinterpret_cast<const T*>(sm.stage[st] + G::kLatBytes);
-      f32x16_t s = f32x16_t{};
-      if (wave_live) {
-#pragma unroll
-        for (int kk = 0; kk < G::kNK0; ++kk) {
-          const int step = half * G::kNK0 + kk;
-          if (step >= G::kNK) break;
-          const int d = step * G::kKStep + g * (G::kBF16 ? 8 : 1);  // this lane's dims
-          const T* src;
-          if (d < DL) {
-            src = kt + n * G::kLatPitch + d;
-          } else {
-            const int dp = d - DL;
-            src = kpe + n * DR + pe_swz<G::kPeChunks>(dp / G::kPerChunk, n) * G::kPerChunk +
-                  dp % G::kPerChunk;
-          }
-          if constexpr (G::kBF16) {
-            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(src);
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr.q[kk], s, 0, 0, 0);
-          } else {
-            s = __builtin_amdgcn_mfma_f32_32x32x2f32(*src, qr.q[kk], s, 0, 0, 0);
-          }
-        }
-        if constexpr (kSplit > 1) {
-#pragma unroll
-          for (int i4 = 0; i4 < 4; ++i4)
-            sm.xs[wave][i4][lane] =
-                make_float4(s[4 * i4], s[4 * i4 + 1], s[4 * i4 + 2], s[4 * i4 + 3]);
-        }
-      }
-      if constexpr (kSplit > 1) lds_barrier();
-      if (wave_live) {
-        if constexpr (kSplit > 1) {
-          // Full scores: own share plus the partner's (addition commutes, so both
-          // waves of the pair hold bit-identical sums).
-#pragma unroll
-          for (int i4 = 0; i4 < 4; ++i4) {
-            const float4 o4 = sm.xs[wave ^ 1][i4][lane];
-            s[4 * i4] += o4.x;
-            s[4 * i4 + 1] += o4.y;
-            s[4 * i4 + 2] += o4.z;
-            s[4 * i4 + 3] += o4.w;
-          }
-        }
-        // Lane owns row n and keys 8*(i/4) + 4*g + (i%4), i = 0..15.
-        const int key0 = kb * kTileKeys;
-        uint32_t okm = (uint32_t)uni((int)sm.valid[kb % kRing]);
-        if (key0 + kTileKeys > ri.L) okm &= tree_window(v0, v1, key0 - ri.L);
-        okm >>= 4 * g;  // now bit 8*(i/4) + (i%4) is key m of register i
-        float mx = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          s[i] = ((okm >> (8 * (i >> 2) + (i & 3))) & 1u) ? s[i] * sl2 : -INFINITY;
-          mx = fmaxf(mx, s[i]);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        float alpha = 1.0f, mref = 0.0f;
-        if (m_new != -INFINITY) {
-          alpha = exp2f(m_run - m_new);
-          mref = m_new;
-        }
-        float psum = 0.0f;
-        float p[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          p[i] = exp2f(s[i] - mref);
-          psum += p[i];
-        }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-        if (alpha != 1.0f) {
-#pragma unroll
-          for (int cb = 0; cb < G::kNCBh; ++cb) o[cb] *= alpha;
-        }
-        // O^T += V^T P^T.
-        if constexpr (G::kBF16) {
-          const bf16x8_t p0 = pack_p<false>(p);
-          const bf16x8_t p1 = pack_p<false>(p + 8);
-          // Residual pass when some row of this wave has a heavy key here.
-          float pmax = 0.0f;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) pmax = fmaxf(pmax, p[i]);
-          pmax = fmaxf(pmax, __shfl_xor(pmax, 32));
-          const float lrow = l_run + __shfl_xor(l_run, 32);
-          const bool heavy = __ballot(pmax > kHeavyShare * lrow) != 0;
-          const int colh = 16 * ((lane >> 4) & 1);
-#pragma unroll
-          for (int cb = 0; cb < G::kNCBh; ++cb) {
-            const int c0 = (half * G::kNCBh + cb) * 32 + colh;
-            const bf16x8_t a0 = read_vt(kt, G::kLatPitch, 4 * g, c0, lane);
-            const bf16x8_t a1 = read_vt(kt, G::kLatPitch, 16 + 4 * g, c0, lane);
-            o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, p0, o[cb], 0, 0, 0);
-            o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, p1, o[cb], 0, 0, 0);
-          }
-          if (heavy) {
-            const bf16x8_t r0 = pack_p<true>(p);
-            const bf16x8_t r1 = pack_p<true>(p + 8);
-#pragma unroll
-            for (int cb = 0; cb < G::kNCBh; ++cb) {
-              const int c0 = (half * G::kNCBh + cb) * 32 + colh;
-              const bf16x8_t a0 = read_vt(kt, G::kLatPitch, 4 * g, c0, lane);
-              const bf16x8_t a1 = read_vt(kt, G::kLatPitch, 16 + 4 * g, c0, lane);
-              o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, r0, o[cb], 0, 0, 0);
-              o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, r1, o[cb], 0, 0, 0);
-            }
-          }
-        } else {
-#pragma unroll
-          for (int cb = 0; cb < G::kNCBh; ++cb) {
-            const int c0 = (half * G::kNCBh + cb) * 32;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int m = 8 * (i >> 2) + 4 * g + (i & 3);
-              o[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kt[m * G::kLatPitch + c0 + n], p[i],
-                                                            o[cb], 0, 0, 0);
-            }
-          }
-        }
-      }
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's tile loads have landed in LDS
-      if (tid < kTileKeys && kb + 2 < kb1)
-        publish_slots(sm.slot[(kb + 2) % kRing], &sm.valid[(kb + 2) % kRing], ahead, tid);
-      __syncthreads();
-    }
-
-    // Normalise and write: this lane holds row n, columns
-    // (half*kNCBh + cb)*32 + 8*t + 4*g + {0..3} in o[cb][4t..4t+3].
-    const float l = l_run + __shfl_xor(l_run, 32);
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    const float lse_v = l > 0.0f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
-    float* dst = nullptr;
-    float* dst_lse = nullptr;
-    if (complete) {
-      if (row_exists) {
-        dst = out + grow * DL;
-        dst_lse = lse ? lse + grow : nullptr;
-      }
-    } else if (row_live) {
-      const long long rr = slot * kRowsPerWG + rb * 32 + n;
-      dst = ws_o + rr * DL;
-      dst_lse = ws_lse + rr;
-    }
-    if (dst) {
-#pragma unroll
-      for (int cb = 0; cb < G::kNCBh; ++cb) {
-#pragma unroll
-        for (int t4 = 0; t4 < 4; ++t4) {
-          float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-          if (row_live)
-            v = make_float4(o[cb][4 * t4] * inv, o[cb][4 * t4 + 1] * inv,
-                            o[cb][4 * t4 + 2] * inv, o[cb][4 * t4 + 3] * inv);
-          *reinterpret_cast<float4*>(dst + (half * G::kNCBh + cb) * 32 + 8 * t4 + 4 * g) = v;
-        }
-      }
-      if (dst_lse && g == 0 && half == 0) *dst_lse = row_live ? lse_v : -INFINITY;
-    }
+    u.kb1 = (long long)(u.ri.nkb - u.kb0) < left ? u.ri.nkb : u.kb0 + (int)left;
+    u.complete = u.kb0 == 0 && u.kb1 == u.ri.nkb;
+    u.slot = 2 * gid + (pos == start ? 0 : 1);
+    u.nkeys = u.ri.L + u.ri.nb;
+    pos += u.kb1 - u.kb0;
+    if (kSplit == 1 || half == 0) run_unit<T, DL, DR, 0>(sm, args, u);
+    else run_unit<T, DL, DR, (kSplit > 1 ? 1 : 0)>(sm, args, u);
   }
 }
 
 // Combines the partial results of row tiles whose key range was cut, and writes
-// the padding output of row tiles with no live row.
+// the padding output of row tiles with no live row.  One workgroup per 16 rows
+// of a row tile: the contributing partial slots are listed once in LDS, each
+// row's total log-sum-exp is computed once, then every thread accumulates
+// weighted float4 chunks of the partial outputs.
 template <int DL>
-__global__ __launch_bounds__(kThreads) void verify_merge_kernel(
+__global__ __launch_bounds__(kMergeThreads) void verify_merge_kernel(
     const int32_t* __restrict__ prefix_len, const int32_t* __restrict__ n_nodes, int B, int Q,
     int H, int RT, int max_kv, int grid_attn, float* __restrict__ out, float* __restrict__ lse,
     const float* __restrict__ ws_o, const float* __restrict__ ws_lse) {
   __shared__ long long s_pref[kMaxBatch + 1];
-  __shared__ long long s_wsum[kWaves];
-  work_prefix(s_pref, s_wsum, prefix_len, n_nodes, B, Q, H, max_kv, RT);
+  __shared__ long long s_wsum[kMergeThreads / kWave];
+  __shared__ int s_src[kMaxGrid];
+  __shared__ float s_lse[kMergeRows];
+  work_prefix<kMergeThreads>(s_pref, s_wsum, prefix_len, n_nodes, B, Q, H, max_kv, RT);
+  const int tid = threadIdx.x;
   const int u = blockIdx.x;
   const int b = u / RT, rt = u % RT;
   const ReqInfo ri = req_info(prefix_len, n_nodes, b, Q, H, max_kv, RT);
   const long long QH = (long long)Q * H;
-  const long long r_begin = (long long)rt * kRowsPerWG;
-  const int nrows = (int)((QH - r_begin) < kRowsPerWG ? (QH - r_begin) : kRowsPerWG);
+  const int r0 = blockIdx.y * kMergeRows;                  // first row within the tile
+  const long long r_begin = (long long)rt * kRowsPerWG + r0;
+  if (r_begin >= QH) return;
   const long long Wtot = s_pref[B];
   const long long Gn = grid_attn;
-  constexpr int kChunks = DL / 4;
-  constexpr int kRowsPerPass = kThreads / kChunks > 0 ? kThreads / kChunks : 1;
-  const int chunk = threadIdx.x % kChunks;
-  const int rsub = threadIdx.x / kChunks;
 
   const bool has_work = rt < ri.vt;
-  long long g_first = 0, g_last = 0, S_u = 0;
+  long long S_u = 0;
+  int cnt = 0;
   if (has_work) {
     S_u = s_pref[b] + (long long)rt * ri.nkb;
-    g_first = range_owner(S_u, Wtot, Gn);
-    g_last = range_owner(S_u + ri.nkb - 1, Wtot, Gn);
+    const long long g_first = range_owner(S_u, Wtot, Gn);
+    const long long g_last = range_owner(S_u + ri.nkb - 1, Wtot, Gn);
     if (g_first == g_last) return;  // written directly by the attention kernel
+    cnt = (int)(g_last - g_first + 1);
+    // Each contributing workgroup (non-empty range) wrote its partial for this
+    // tile into slot 2g when the tile holds the start of its range, else 2g+1.
+    for (int k = tid; k < cnt; k += kMergeThreads) {
+      const long long gg = g_first + k;
+      const long long s0 = range_start(gg, Wtot, Gn);
+      const long long s1 = range_start(gg + 1, Wtot, Gn);
+      s_src[k] = s0 == s1 ? -1 : (int)(2 * gg + (s0 >= S_u ? 0 : 1));
+    }
   }
-  for (int r0 = 0; r0 < nrows; r0 += kRowsPerPass) {
-    const int rr = r0 + rsub;
-    if (rsub >= kRowsPerPass || rr >= nrows) continue;
-    const long long r_loc = r_begin + rr;
-    const long long grow = (long long)b * QH + r_loc;
-    const bool live = has_work && (int)(r_loc / H) < ri.nb;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    float lse_tot = -INFINITY;
-    if (live) {
-      // Each contributing workgroup (one with a non-empty range) wrote its
-      // partial for this tile into slot 2g when the tile holds the start of its
-      // range, else into slot 2g+1.
-      float mx = -INFINITY;
-      for (long long gg = g_first; gg <= g_last; ++gg) {
-        const long long s0 = range_start(gg, Wtot, Gn);
-        if (s0 == range_start(gg + 1, Wtot, Gn)) continue;
-        const long long sl = 2 * gg + (s0 >= S_u ? 0 : 1);
-        mx = fmaxf(mx, ws_lse[sl * kRowsPerWG + rr]);
-      }
-      if (mx != -INFINITY) {
-        float z = 0.0f;
-        for (long long gg = g_first; gg <= g_last; ++gg) {
-          const long long s0 = range_start(gg, Wtot, Gn);
-          if (s0 == range_start(gg + 1, Wtot, Gn)) continue;
-          const long long sl = 2 * gg + (s0 >= S_u ? 0 : 1);
-          z += expf(ws_lse[sl * kRowsPerWG + rr] - mx);
-        }
-        lse_tot = mx + logf(z);
-        for (long long gg = g_first; gg <= g_last; ++gg) {
-          const long long s0 = range_start(gg, Wtot, Gn);
-          if (s0 == range_start(gg + 1, Wtot, Gn)) continue;
-          const long long sl = 2 * gg + (s0 >= S_u ? 0 : 1);
-          const float w = expf(ws_lse[sl * kRowsPerWG + rr] - lse_tot);
-          const float4 v = *reinterpret_cast<const float4*>(
-              ws_o + (sl * kRowsPerWG + rr) * DL + chunk * 4);
-          acc.x += w * v.x;
-          acc.y += w * v.y;
-          acc.z += w * v.z;
-          acc.w += w * v.w;
+  __syncthreads();
+  if (tid < kMergeRows) {
+    const int rr = r0 + tid;
+    const long long r_loc = (long long)rt * kRowsPerWG + rr;
+    float m = -INFINITY, z = 0.0f;
+    if (has_work && r_loc < QH && (int)(r_loc / H) < ri.nb) {
+      for (int k = 0; k < cnt; ++k) {
+        const int src = s_src[k];
+        if (src < 0) continue;
+        const float v = ws_lse[(long long)src * kRowsPerWG + rr];
+        if (v == -INFINITY) continue;
+        if (v > m) {
+          z = z * expf(m - v) + 1.0f;
+          m = v;
+        } else {
+          z += expf(v - m);
         }
       }
     }
+    s_lse[tid] = z > 0.0f ? m + logf(z) : -INFINITY;
+  }
+  __syncthreads();
+  constexpr int kChunks = DL / 4;
+  for (int idx = tid; idx < kMergeRows * kChunks; idx += kMergeThreads) {
+    const int rl = idx / kChunks, chunk = idx % kChunks;
+    const int rr = r0 + rl;
+    const long long r_loc = (long long)rt * kRowsPerWG + rr;
+    if (r_loc >= QH) continue;
+    const long long grow = (long long)b * QH + r_loc;
+    const float lt = s_lse[rl];
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (lt != -INFINITY) {
+      for (int k = 0; k < cnt; ++k) {
+        const int src = s_src[k];
+        if (src < 0) continue;
+        const long long sr = (long long)src * kRowsPerWG + rr;
+        const float w = expf(ws_lse[sr] - lt);
+        const float4 v = *reinterpret_cast<const float4*>(ws_o + sr * DL + chunk * 4);
+        acc.x += w * v.x;
+        acc.y += w * v.y;
+        acc.z += w * v.z;
+        acc.w += w * v.w;
+      }
+    }
     *reinterpret_cast<float4*>(out + grow * DL + chunk * 4) = acc;
-    if (lse && chunk == 0) lse[grow] = lse_tot;
+    if (lse && chunk == 0) lse[grow] = lt;
   }
 }
 
@@ -730,7 +824,8 @@ hipError_t launch_impl(const void* q_lat, const void* q_pe, const void* c_kv, co
                      sm_scale, out, lse, ws_o, ws_lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((verify_merge_kernel<DL>), dim3(B * plan.row_tiles), dim3(kThreads), 0,
+  hipLaunchKernelGGL((verify_merge_kernel<DL>), dim3(B * plan.row_tiles, kRowsPerWG / kMergeRows),
+                     dim3(kMergeThreads), 0,
                      stream, prefix_len, n_nodes, B, Q, H, plan.row_tiles, max_kv, plan.grid,
                      out, lse, ws_o, ws_lse);
   return hipGetLastError();
@@ -744,12 +839,15 @@ AttnPlan plan_verify_attn(int B, int Q, int H, int max_kv, int d_lat, int num_cu
   p.row_tiles = (int)((rows + kRowsPerWG - 1) / kRowsPerWG);
   const long long nkb = ((long long)max_kv + kTileKeys - 1) / kTileKeys;
   const long long work = (long long)B * p.row_tiles * nkb;
-  // One resident workgroup per CU (register-bound); at least a few key tiles each.
+  // One resident workgroup per CU (register-bound), but at least kMinTilesPerWG
+  // key tiles each so that query loads and partial outputs stay a small share.
   long long g = num_cu > 0 ? num_cu : 256;
-  const long long by_work = (work + 3) / 4;
+  if (g > kMaxGrid) g = kMaxGrid;
+  const long long by_work = (work + kMinTilesPerWG - 1) / kMinTilesPerWG;
   if (by_work < g) g = by_work;
   g = ((g + kXcds - 1) / kXcds) * kXcds;
   if (g < kXcds) g = kXcds;
+  if (g > kMaxGrid) g = kMaxGrid;
   p.grid = (int)g;
   p.ws_bytes = (size_t)2 * p.grid * kRowsPerWG * ((size_t)d_lat + 1) * sizeof(float);
   return p;
