@@ -227,6 +227,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only-primary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager launches instead of HIP graph replays (for profilers)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (reference for byte counters)")
     ap.add_argument("--workload", default=PRIMARY,
                     help="headline workload (default: the batch-1 configuration)")
     args = ap.parse_args()
@@ -243,11 +247,23 @@ def main():
 
     primary = args.workload
     runner = StepRunner(primary, torch, ddt, workloads)
-    g_step = runner.capture(runner.step)
-    g_attn = runner.capture(runner.attn)
-    torch.cuda.synchronize()
-    ms_step = runner.time_graph(g_step, args.steps, args.warmup)
-    ms_attn = runner.time_graph(g_attn, args.steps, args.warmup)
+    if args.copy_calibration:
+        src = torch.empty((256 << 20,), dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    if args.eager:
+        ms_step = runner.time_eager(runner.step, args.steps, args.warmup)
+        ms_attn = runner.time_eager(runner.attn, args.steps, args.warmup)
+    else:
+        g_step = runner.capture(runner.step)
+        g_attn = runner.capture(runner.attn)
+        torch.cuda.synchronize()
+        ms_step = runner.time_graph(g_step, args.steps, args.warmup)
+        ms_attn = runner.time_graph(g_attn, args.steps, args.warmup)
     ms_eager = runner.time_eager(runner.step, min(args.steps, 100), 5)
     log(f"[bench] {primary}: step {ms_step * 1e3:.1f} us (graph), {ms_eager * 1e3:.1f} us "
         f"(eager), attention {ms_attn * 1e3:.1f} us")

@@ -122,7 +122,7 @@ int ddt_tree_build(const float* topk_logp, const int32_t* topk_ids,
  * Scalars: 1 <= B <= DDT_MAX_BATCH_ATTN, 1 <= Q <= DDT_MAX_Q, H >= 1,
  *   max_kv >= 1, num_slots >= 1, (dtype, d_lat, d_rope) one of
  *   (DDT_BF16, 512, 64), (DDT_BF16, 64, 16), (DDT_F32, 64, 16);
- *   sm_scale finite.
+ *   sm_scale finite and > 0.
  * Outputs (device): out [B][Q][H][d_lat] f32 (latent-space attention output),
  *   lse [B][Q][H] f32 natural-log sum-exp of the scaled scores (may be NULL).
  * Workspace: device scratch of at least

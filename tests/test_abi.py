@@ -87,6 +87,8 @@ def call_attn(lib, B=1, Q=9, H=64, d_lat=512, d_rope=64, dtype=ddt.DDT_BF16, sca
     (dict(dtype=7), ddt.DDT_EINVAL, "dtype=7"),
     (dict(scale=float("nan")), ddt.DDT_EINVAL, "sm_scale"),
     (dict(scale=float("inf")), ddt.DDT_EINVAL, "sm_scale"),
+    (dict(scale=0.0), ddt.DDT_EINVAL, "sm_scale"),
+    (dict(scale=-0.1), ddt.DDT_EINVAL, "sm_scale"),
     (dict(d_lat=256), ddt.DDT_EUNSUPPORTED, "not compiled in"),
     (dict(dtype=ddt.DDT_F32), ddt.DDT_EUNSUPPORTED, "not compiled in"),
     (dict(null_q=True), ddt.DDT_EINVAL, "NULL"),

@@ -99,8 +99,8 @@ int ddt_verify_attn(const void* q_lat, const void* q_pe, const void* c_kv, const
     return fail(DDT_EINVAL, "ddt_verify_attn: num_slots=%lld must be >= 1", (long long)num_slots);
   if (dtype != DDT_F32 && dtype != DDT_BF16)
     return fail(DDT_EINVAL, "ddt_verify_attn: dtype=%d is not DDT_F32 or DDT_BF16", dtype);
-  if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY)
-    return fail(DDT_EINVAL, "ddt_verify_attn: sm_scale must be finite");
+  if (!(sm_scale > 0.0f) || sm_scale == INFINITY)
+    return fail(DDT_EINVAL, "ddt_verify_attn: sm_scale must be finite and > 0");
   if (!attn_variant_supported(dtype, d_lat, d_rope))
     return fail(DDT_EUNSUPPORTED,
                 "ddt_verify_attn: (dtype=%d, d_lat=%d, d_rope=%d) not compiled in; supported: "

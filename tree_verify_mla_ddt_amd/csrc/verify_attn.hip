@@ -118,25 +118,21 @@ struct Geo {
   static_assert(kDK % kKStep == 0, "contraction depth");
 };
 
-__device__ __forceinline__ uint32_t bf16_rne(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-// Eight probabilities as a bf16x8 operand; with kResidual, the bf16 rounding
-// residuals p - bf16(p) instead.
+// Eight probabilities as a bf16x8 operand (round to nearest even, v_cvt_pk_bf16_f32);
+// with kResidual, the rounding residuals p - bf16(p) instead, which are exact
+// in fp32 and rounded to bf16 once more.
 template <bool kResidual>
 __device__ __forceinline__ bf16x8_t pack_p(const float* p) {
   uint32_t w[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    uint32_t h0 = bf16_rne(p[2 * k]), h1 = bf16_rne(p[2 * k + 1]);
-    if constexpr (kResidual) {
-      h0 = bf16_rne(p[2 * k] - bf16_to_f32(h0));
-      h1 = bf16_rne(p[2 * k + 1] - bf16_to_f32(h1));
-    }
-    w[k] = h0 | (h1 << 16);
+    const f32x2_t v = {p[2 * k], p[2 * k + 1]};
+    bf16x2_t h = __builtin_convertvector(v, bf16x2_t);
+    if constexpr (kResidual) h = __builtin_convertvector(v - __builtin_convertvector(h, f32x2_t), bf16x2_t);
+    w[k] = __builtin_bit_cast(uint32_t, h);
   }
   return __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
 }
@@ -535,10 +531,13 @@ __device__ __forceinline__ void run_unit(Smem<T, DL, DR>& sm, const Args& a, con
           s[4 * i4 + 3] += o4.w;
         }
       }
-      // Lane owns row n and keys 8*(i/4) + 4*g + (i%4), i = 0..15.
+      // Lane owns row n and keys 8*(i/4) + 4*g + (i%4), i = 0..15.  Invisible
+      // keys get -inf; the scale (> 0) is applied inside the exponent.
       const int key0 = kb * kTileKeys;
-      uint32_t okm = (uint32_t)uni((int)sm.valid[kb % kRing]);
-      if (key0 + kTileKeys > u.ri.L) {
+      const uint32_t valid = (uint32_t)uni((int)sm.valid[kb % kRing]);
+      const bool tree_tile = key0 + kTileKeys > u.ri.L;
+      uint32_t okm = valid;
+      if (tree_tile) {
         const uint64_t* vr = sm.visrow[rb * 32 + n];
         okm &= tree_window(vr[0], vr[1], key0 - u.ri.L);
       }
@@ -546,10 +545,10 @@ __device__ __forceinline__ void run_unit(Smem<T, DL, DR>& sm, const Args& a, con
       float mx = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        s[i] = ((okm >> (8 * (i >> 2) + (i & 3))) & 1u) ? s[i] * a.sl2 : -INFINITY;
+        s[i] = ((okm >> (8 * (i >> 2) + (i & 3))) & 1u) ? s[i] : -INFINITY;
         mx = fmaxf(mx, s[i]);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.sl2;  // row max of this tile, log2 units
       // Lazy rescaling: the reference max m_run moves only on the first
       // visible key (accumulators still zero) or when the tile's max exceeds
       // it by more than kRescaleLog2, so probabilities stay below
@@ -557,7 +556,7 @@ __device__ __forceinline__ void run_unit(Smem<T, DL, DR>& sm, const Args& a, con
       if (m_run == -INFINITY) m_run = mx;
       const bool jump = mx > m_run + kRescaleLog2;
       if (__ballot(jump) != 0) {
-        const float alpha = jump ? exp2f(m_run - mx) : 1.0f;
+        const float alpha = jump ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f;
         if (jump) {
           l_run *= alpha;
           m_run = mx;
@@ -570,7 +569,7 @@ __device__ __forceinline__ void run_unit(Smem<T, DL, DR>& sm, const Args& a, con
       float p[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        p[i] = exp2f(s[i] - mref);
+        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], a.sl2, -mref));
         psum += p[i];
       }
       l_run += psum;
@@ -578,11 +577,9 @@ __device__ __forceinline__ void run_unit(Smem<T, DL, DR>& sm, const Args& a, con
       if constexpr (G::kBF16) {
         const bf16x8_t p0 = pack_p<false>(p);
         const bf16x8_t p1 = pack_p<false>(p + 8);
-        // Residual pass when some row of this wave has a heavy key here.
-        float pmax = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) pmax = fmaxf(pmax, p[i]);
-        pmax = fmaxf(pmax, __shfl_xor(pmax, 32));
+        // Residual pass when some row of this wave has a heavy key here (the
+        // largest probability of the row in this tile is exp2(mx - mref)).
+        const float pmax = __builtin_amdgcn_exp2f(mx - mref);
         const float lrow = l_run + __shfl_xor(l_run, 32);
         const bool heavy = __ballot(pmax > kHeavyShare * lrow) != 0;
         // Pack the residual operands now so the fp32 probabilities die here.
