@@ -61,18 +61,15 @@ typedef __bf16 bf16x4_lds_t __attribute__((__vector_size__(4 * sizeof(__bf16))))
 #define DDT_LDS __attribute__((address_space(3)))
 
 constexpr int kTileKeys = 32;
-#ifndef DDT_ATTN_SPLIT
-#define DDT_ATTN_SPLIT 2
-#endif
-constexpr int kSplit = DDT_ATTN_SPLIT;   // waves sharing one 32-row block
+constexpr int kSplit = 2;                // waves sharing one 32-row block
 constexpr int kWaves = 4 * kSplit;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kRowsPerWG = 128;
 constexpr int kMaxBatch = 512;
 constexpr int kXcds = 8;
-constexpr int kRing = 3;
+constexpr int kRing = 3;                 // slot-id ring (tiles kb .. kb+2)
+constexpr int kStages = 3;               // key-tile stages in LDS (tiles kb-1 .. kb+1)
 constexpr int kMergeThreads = 256;
-constexpr int kMergeRows = 16;           // rows per merge workgroup
 constexpr int kMaxGrid = 1024;           // upper bound of the attention grid
 constexpr int kMinTilesPerWG = 8;        // key tiles per workgroup before splitting further
 constexpr float kLog2e = 1.4426950408889634f;
@@ -92,12 +89,14 @@ struct Geo {
   static constexpr int kPerChunk = 16 / kElt;               // elements per 16-byte chunk
   static constexpr int kLatChunks = DL / kPerChunk;         // 16-byte chunks of a latent row
   static constexpr int kPeChunks = DR / kPerChunk;          // ... of a rope row
-  // Latent region: one key row per load instruction when a row is 64 chunks,
-  // padded to a pitch whose dword stride is 36 (mod 64) so that the 16-byte
-  // operand reads of 16 keys and the transposing reads of 4 keys hit distinct
-  // banks; smaller rows pack several keys per instruction without padding.
+  // Latent region.  A 64-chunk row (bf16, 512 wide) is one load instruction
+  // and sits at a 1 KiB pitch with its 16-byte chunks permuted per key (see
+  // swz()), which keeps both the operand reads of QK^T and the transposing
+  // reads of PV free of bank conflicts; smaller rows pack several keys per
+  // instruction, unpermuted.
+  static constexpr bool kSwz = kLatChunks == kWave;
   static constexpr int kKeysPerInstr = kLatChunks >= kWave ? 1 : kWave / kLatChunks;
-  static constexpr int kLatPitchB = kLatChunks >= kWave ? kLatChunks * 16 + 144 : kLatChunks * 16;
+  static constexpr int kLatPitchB = kLatChunks * 16;
   static constexpr int kLatPitch = kLatPitchB / kElt;       // in elements
   static constexpr int kLatInstr = kTileKeys / kKeysPerInstr * (kLatChunks >= kWave ? kLatChunks / kWave : 1);
   // Rope region: keys back to back; 8-chunk rows are XOR-swizzled by key.
@@ -226,22 +225,41 @@ __device__ __forceinline__ long long range_owner(long long t, long long W, long 
 template <typename T, int DL, int DR>
 struct Smem {
   using G = Geo<T, DL, DR>;
-  alignas(16) unsigned char stage[2][G::kStageBytes];
+  alignas(1024) unsigned char stage[kStages][G::kStageBytes];
   int32_t slot[kRing][kTileKeys];   // pool slot of each key of a tile (0 when invalid)
   uint32_t valid[kRing];            // bit m: key m of the tile is in range with a valid slot
-  float4 xs[kSplit > 1 ? kWaves : 1][4][kWave];  // partial scores exchanged within a group
+  float4 xs[kWaves][2][kWave];      // partial scores of the partner's keys
+  float4 xp[kWaves][G::kBF16 ? 1 : 2][kWave];  // probabilities of own keys (bf16: packed)
+  uint4 xr[kWaves][kWave];          // bf16 rounding residuals of own keys
+  float xm[kWaves][kWave];          // row max over own keys
+  float xl[kWaves][kWave];          // row sum over own keys
+  int xflag[kWaves];                // posted sequence numbers
+  uint32_t xheavy[kWaves];          // residuals posted with the latest probabilities
   uint64_t visrow[kRowsPerWG][2];   // visibility bitset of each row's tree node
   long long pref[kMaxBatch + 1];
   long long wsum[kWaves];
 };
 
-// Pool slot of key `j` of the request, or -1 when the key is past the request
-// or its slot id is outside the pool.
-__device__ __forceinline__ int32_t fetch_slot(const int32_t* __restrict__ slots_b,
-                                              int64_t num_slots, int j, int nkeys) {
-  if (j >= nkeys) return -1;
-  const int32_t s = slots_b[j];
-  return (s >= 0 && (int64_t)s < num_slots) ? s : -1;
+// Raw pool slot id of key `j` of the request (-1 past the request); its range
+// is checked when it is published, so the load's latency is not waited for
+// where it is issued.
+__device__ __forceinline__ int32_t fetch_slot(const int32_t* __restrict__ slots_b, int j,
+                                              int nkeys) {
+  return j < nkeys ? slots_b[j] : -1;
+}
+
+// Latent chunk permutation of the 1 KiB-pitch layout: logical 16-byte chunk c
+// of key row r is stored at chunk c ^ swz(r), swz(r) = A[r & 3] ^ ((r >> 2) & 3)
+// with A = {0, 4, 10, 14}.  Over each aligned group of 16 keys swz takes 16
+// distinct values, and their low 3 bits differ within each aligned group of 8
+// keys (operand reads of one chunk by 8 or 16 keys cover distinct banks); bits
+// 2..3 differ within each aligned group of 4 keys (transposing reads of 4 keys
+// x 64 bytes cover all banks).
+__device__ __forceinline__ int swz_a(int r) { return (0xEA40 >> (4 * (r & 3))) & 15; }
+__device__ __forceinline__ int swz(int r) { return swz_a(r) ^ ((r >> 2) & 3); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const DDT_LDS void*)p;
 }
 
 // Physical chunk of logical rope chunk c of key `key` (8-chunk rows only).
@@ -250,6 +268,22 @@ __device__ __forceinline__ int pe_swz(int c, int key) {
   if constexpr (kPeChunks == 8) return c ^ (key & 7);
   else return c;
 }
+
+// Direct global -> LDS load of 16 bytes per lane: lane l's bytes land at LDS
+// address lds + 16*l.  Issued as inline assembly: the compiler's wait-count
+// pass would otherwise make every later LDS read wait for these loads (it
+// cannot tell that they target the other stage), which would serialise each
+// tile behind the next tile's memory latency.  The kernel waits for them
+// itself (s_waitcnt vmcnt(0) before the barrier that publishes a stage).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  __asm__ __volatile__("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                       :
+                       : "v"(src), "s"(lds)
+                       : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 // Enqueue the direct global->LDS loads of one key tile.  With 64-chunk latent
 // rows, wave w loads latent rows of keys kLatInstr/kWaves*w.. (one row per
@@ -267,8 +301,8 @@ __device__ __forceinline__ void issue_tile(unsigned char* stage, const int32_t* 
     for (int it = 0; it < kPerWave; ++it) {
       const int key = wave * kPerWave + it;
       const long long row = uni(ring_slots[key]);
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(c_kv + row * DL + lane * G::kPerChunk),
-                                       (DDT_LDS void*)(stage + key * G::kLatPitchB), 16, 0, 0);
+      // Lane l fills physical chunk l, i.e. logical chunk l ^ swz(key).
+      dma16(static_cast<const void*>(c_kv + row * DL + (lane ^ swz(key)) * G::kPerChunk), lds_addr((stage + key * G::kLatPitchB)));
     }
     if (wave < G::kPeInstr) {
       // 8 keys x 8 chunks; key & 7 == lane / 8, so the swizzled chunk depends
@@ -276,9 +310,7 @@ __device__ __forceinline__ void issue_tile(unsigned char* stage, const int32_t* 
       const int key = wave * 8 + (lane >> 3);
       const long long row = ring_slots[key];
       const T* src = k_pe + row * DR + (((lane & 7) ^ (lane >> 3)) * G::kPerChunk);
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src),
-                                       (DDT_LDS void*)(stage + G::kLatBytes + wave * kWave * 16),
-                                       16, 0, 0);
+      dma16(static_cast<const void*>(src), lds_addr((stage + G::kLatBytes + wave * kWave * 16)));
     }
   } else {
 #pragma unroll
@@ -299,9 +331,7 @@ __device__ __forceinline__ void issue_tile(unsigned char* stage, const int32_t* 
           dst = stage + r * kWave * 16;
         }
         const long long row = ring_slots[key];
-        __builtin_amdgcn_global_load_lds(
-            static_cast<const void*>(c_kv + row * DL + ch * G::kPerChunk), (DDT_LDS void*)dst,
-            16, 0, 0);
+        dma16(static_cast<const void*>(c_kv + row * DL + ch * G::kPerChunk), lds_addr(dst));
       } else {
         const int rp = r - G::kLatInstr;
         const int s = rp * kWave + lane;  // rope chunk slot
@@ -312,9 +342,7 @@ __device__ __forceinline__ void issue_tile(unsigned char* stage, const int32_t* 
           const long long row = ring_slots[key];
           src = k_pe + row * DR + pe_swz<G::kPeChunks>(p, key) * G::kPerChunk;
         }
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(src),
-                                         (DDT_LDS void*)(stage + G::kLatBytes + rp * kWave * 16),
-                                         16, 0, 0);
+        dma16(static_cast<const void*>(src), lds_addr((stage + G::kLatBytes + rp * kWave * 16)));
       }
     }
   }
@@ -334,10 +362,40 @@ __device__ __forceinline__ bf16x8_t read_vt(const uint16_t* kt, int pitch, int k
   return __builtin_bit_cast(bf16x8_t, make_uint4(ulo.x, ulo.y, uhi.x, uhi.y));
 }
 
-// Lanes 0..31 of wave 0 store the slot ids of one tile (invalid -> pool row 0)
-// and its validity bitmask.
-__device__ __forceinline__ void publish_slots(int32_t* ring, uint32_t* valid, int32_t slot,
-                                              int key) {
+// Transposing reads of the permuted 1 KiB-pitch latent rows.  Lane (j = l % 16,
+// q = l / 16, g = l / 32) reads key row kbase + j/4 at logical column
+// 32*cb + 16*(q%2) + 4*(j%4), i.e. logical chunk 4*cb + x (x = 2*(q%2) + (j%4)/2),
+// half-chunk j%2.  For kbase = 4g + 8t + 16*k1 the row's swz is f0 = A[j/4] ^ g
+// (t = 0) or f0 ^ 2 (t = 1), so with cb = 4h + c the byte address is
+// (P_t ^ 64c) + 256h + 8192t + 16384*k1, P_t holding the row, the low chunk
+// bits and the lane's half-chunk.
+struct VtAddr {
+  uint32_t p0, p1;
+  __device__ __forceinline__ VtAddr(uint32_t tile, int lane) {
+    const int j = lane & 15, q = lane >> 4, g = lane >> 5;
+    const int x = 2 * (q & 1) + ((j & 3) >> 1);
+    const int f0 = swz_a(j >> 2) ^ g, f1 = f0 ^ 2;
+    const uint32_t rb = tile + (4 * g + (j >> 2)) * 1024 + 8 * (j & 1);
+    p0 = rb + 16 * ((x ^ f0) & 3) + 64 * (f0 >> 2);
+    p1 = rb + 16 * ((x ^ f1) & 3) + 64 * (f1 >> 2);
+  }
+  __device__ __forceinline__ bf16x8_t read(int cb, int k1) const {
+    const uint32_t c = 64 * (cb & 3), h = 256 * (cb >> 2) + 16384 * k1;
+    const bf16x4_lds_t lo =
+        __builtin_amdgcn_ds_read_tr16_b64_v4bf16((DDT_LDS bf16x4_lds_t*)(uintptr_t)((p0 ^ c) + h));
+    const bf16x4_lds_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (DDT_LDS bf16x4_lds_t*)(uintptr_t)((p1 ^ c) + h + 8192));
+    const uint2 ulo = __builtin_bit_cast(uint2, lo);
+    const uint2 uhi = __builtin_bit_cast(uint2, hi);
+    return __builtin_bit_cast(bf16x8_t, make_uint4(ulo.x, ulo.y, uhi.x, uhi.y));
+  }
+};
+
+// Lanes 0..31 of wave 0 store the slot ids of one tile (a key past the request
+// or with a slot id outside the pool -> pool row 0) and its validity bitmask.
+__device__ __forceinline__ void publish_slots(int32_t* ring, uint32_t* valid, int32_t raw,
+                                              int64_t num_slots, int key) {
+  const int32_t slot = (raw >= 0 && (int64_t)raw < num_slots) ? raw : -1;
   ring[key] = slot < 0 ? 0 : slot;
   const uint64_t ok = __ballot(slot >= 0);
   if (key == 0) *valid = (uint32_t)ok;
@@ -388,17 +446,71 @@ struct Args {
   float* ws_lse;
 };
 
-// One row tile over key tiles [kb0, kb1) by the waves owning share HALF of the
-// contraction dimensions and output columns (compile time, so every LDS operand
-// address is one base register plus an immediate).
-template <typename T, int DL, int DR, int HALF>
-__device__ __forceinline__ void run_unit(Smem<T, DL, DR>& sm, const Args& a, const Unit& u) {
+// Sums / maxima of a value over lanes l and l ^ 32 (the two lanes of one row),
+// bit-identical in both lanes.
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Pair synchronisation through LDS.  A wave posts an increasing sequence number
+// once its LDS writes have completed; its partner waits until it sees that
+// number.  Both waves of a pair take the same path, so they post the same
+// sequence.  The wait is bounded so that it always ends.
+constexpr int kSpinLimit = 1 << 16;  // polls of ~100 cycles: milliseconds, far beyond a tile
+
+__device__ __forceinline__ void pair_post(int* flag, int seq) {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+  __asm__ __volatile__("" ::: "memory");
+  __hip_atomic_store(flag, seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+__device__ __forceinline__ void pair_wait(int* flag, int seq) {
+  for (int i = 0; i < kSpinLimit; ++i) {
+    if (uni(__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) >= seq) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  __asm__ __volatile__("" ::: "memory");
+}
+
+// One row tile over key tiles [kb0, kb1) by the waves of share HALF of group
+// GRP (both compile time, so every LDS operand address is one base register
+// plus an immediate and every phase decision is static).
+// The two waves of a pair split the work of each tile three ways:
+//   QK^T  over their half of the 576 contraction dimensions (partial scores of
+//         all 32 keys), then exchange the partial scores of the partner's keys;
+//   softmax over their own 16 keys (HALF 0: keys 0..15, HALF 1: keys 16..31),
+//         then exchange the bf16 probabilities of those keys and the row max;
+//   PV    over their half of the 512 output columns with all 32 keys.
+// The reference max of each row is the same in both waves: it only moves on
+// the pair's combined tile max.  Probabilities are computed against the
+// current reference before the maxima are exchanged; in the rare tiles where
+// the reference moves, both waves recompute and exchange them again.
+// Ping-pong: group 0 (pairs 0, 1: waves 0..3, one per SIMD) and group 1 (pairs
+// 2, 3: waves 4..7) run half a tile apart, so that on every SIMD one wave
+// issues matrix instructions while the other does the exchange and softmax:
+//   iteration t, first half:   group 0: PV(t-1), QK(t)   group 1: softmax(t-1)
+//   iteration t, second half:  group 0: softmax(t)       group 1: PV(t-1), QK(t)
+// Tiles t-1 and t are read during iteration t while tile t+1 loads, so the
+// key tiles rotate through three LDS stages (stage of tile t = t mod 3).
+template <typename T, int DL, int DR, int HALF, int GRP>
+__device__ __forceinline__ void run_unit(Smem<T, DL, DR>& sm, const Args& a, const Unit& u,
+                                         int& seq) {
   using G = Geo<T, DL, DR>;
   constexpr int kStep0 = HALF * G::kNK0;
   constexpr int kStep1 = (HALF + 1) * G::kNK0 < G::kNK ? (HALF + 1) * G::kNK0 : G::kNK;
   constexpr int kCb0 = HALF * G::kNCBh;
+  constexpr int kOwn = 8 * HALF;    // first score register of this wave's keys
+  constexpr int kMate = 8 - kOwn;   // first score register of the partner's keys
   const int tid = threadIdx.x;
   const int wave = uni(tid >> 6);  // wave-uniform: keep it (and what derives from it) scalar
+  const int mate = wave ^ 1;
   const int lane = tid & 63;
   const int rb = wave / kSplit;
   const int n = lane & 31;
@@ -416,7 +528,7 @@ __device__ __forceinline__ void run_unit(Smem<T, DL, DR>& sm, const Args& a, con
   const int node = (int)(r_loc / a.H);
   const bool row_exists = r_loc < QH;
   const bool row_live = row_exists && node < u.ri.nb;
-  const bool wave_live = __ballot(row_live) != 0;
+  const bool wave_live = __ballot(row_live) != 0;  // the same in both waves of the pair
   const long long grow = (long long)u.b * QH + r_loc;
 
   // Query operand: B slots of this lane's row for contraction steps of HALF.
@@ -451,185 +563,302 @@ __device__ __forceinline__ void run_unit(Smem<T, DL, DR>& sm, const Args& a, con
   f32x16_t o[G::kNCBh];
 #pragma unroll
   for (int cb = 0; cb < G::kNCBh; ++cb) o[cb] = f32x16_t{};
+  // m_run: the row's reference max (log2 units), identical in both waves of the
+  // pair; l_run: this lane's share of the row sum (own keys, its 8 of them).
   float m_run = -INFINITY, l_run = 0.0f;
 
   // Prologue: slot ids of the first two tiles, then the first tile.
   if (tid < kTileKeys) {
     publish_slots(sm.slot[u.kb0 % kRing], &sm.valid[u.kb0 % kRing],
-                  fetch_slot(slots_b, a.num_slots, u.kb0 * kTileKeys + tid, u.nkeys), tid);
+                  fetch_slot(slots_b, u.kb0 * kTileKeys + tid, u.nkeys), a.num_slots, tid);
     if (u.kb0 + 1 < u.kb1)
       publish_slots(sm.slot[(u.kb0 + 1) % kRing], &sm.valid[(u.kb0 + 1) % kRing],
-                    fetch_slot(slots_b, a.num_slots, (u.kb0 + 1) * kTileKeys + tid, u.nkeys),
+                    fetch_slot(slots_b, (u.kb0 + 1) * kTileKeys + tid, u.nkeys), a.num_slots,
                     tid);
   }
   __syncthreads();
-  issue_tile<T, DL, DR>(sm.stage[0], sm.slot[u.kb0 % kRing], c_kv, k_pe, wave, lane);
+  issue_tile<T, DL, DR>(sm.stage[u.kb0 % kStages], sm.slot[u.kb0 % kRing], c_kv, k_pe, wave,
+                        lane);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int kb = u.kb0; kb < u.kb1; ++kb) {
-    const int st = (kb - u.kb0) & 1;
-    // Lane-derived offsets are recomputed every tile from an opaque copy of the
-    // lane id: a handful of VALU ops instead of registers held across the loop.
-    int lane_it = lane;
-    __asm__ __volatile__("" : "+v"(lane_it));
+  // State carried between the phases of one tile: the partial scores (QK ->
+  // softmax) and the value-product operands (softmax -> PV).
+  f32x16_t s = f32x16_t{};
+  float p[8];                               // fp32 probabilities of own keys (fp32 inputs)
+  bf16x8_t p0 = bf16x8_t{}, p1 = bf16x8_t{};  // keys 0..15 / 16..31 (bf16 inputs)
+  bf16x8_t r0 = bf16x8_t{}, r1 = bf16x8_t{};  // their rounding residuals
+  bool heavy0 = false, heavy1 = false;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) p[j] = 0.0f;
+
+  // Partial S^T = K Q^T of tile kb over this wave's share of the contraction.
+  auto do_qk = [&](int kb, int lane_it) __attribute__((always_inline)) {
     const int n = lane_it & 31;
     const int g = lane_it >> 5;
-    int32_t ahead = -1;
-    if (tid < kTileKeys && kb + 2 < u.kb1)
-      ahead = fetch_slot(slots_b, a.num_slots, (kb + 2) * kTileKeys + tid, u.nkeys);
-    if (kb + 1 < u.kb1)
-      issue_tile<T, DL, DR>(sm.stage[st ^ 1], sm.slot[(kb + 1) % kRing], c_kv, k_pe, wave,
-                            lane_it);
-
-    const T* kt = reinterpret_cast<const T*>(sm.stage[st]);
-    const T* kpe = reinterpret_cast<const T*>(sm.stage[st] + G::kLatBytes);
-    f32x16_t s = f32x16_t{};
-    if (wave_live) {
-      // Partial S^T = K Q^T over this wave's share of the contraction.
-      const T* krow = kt + n * G::kLatPitch + g * (G::kBF16 ? 8 : 1);
-      const T* prow = kpe + n * DR;
-      const int xswz = g ^ (n & 7);  // rope: physical chunk = logical chunk ^ (n & 7)
+    const unsigned char* stg = sm.stage[kb % kStages];
+    const T* kt = reinterpret_cast<const T*>(stg);
+    const T* kpe = reinterpret_cast<const T*>(stg + G::kLatBytes);
+    s = f32x16_t{};
+    const T* krow = kt + n * G::kLatPitch + g * (G::kBF16 ? 8 : 1);
+    const T* prow = kpe + n * DR;
+    const int xswz = g ^ (n & 7);  // rope: physical chunk = logical chunk ^ (n & 7)
+    // Permuted latent rows: logical chunk 2*step + g of key n is at byte
+    // n*1024 + 16*((2*step + g) ^ swz(n)) = (base ^ 32*(step % 8)) + 256*(step / 8).
+    const uint32_t qk_base = lds_addr(kt) + n * G::kLatPitchB + 16 * (g ^ swz(n));
 #pragma unroll
-      for (int kk = 0; kk < kStep1 - kStep0; ++kk) {
-        constexpr int kLatSteps = DL / G::kKStep;
-        const int step = kStep0 + kk;
-        if constexpr (G::kBF16) {
-          const T* src;
-          if (step < kLatSteps) {
-            src = krow + step * 16;
-          } else if constexpr (G::kPeChunks == 8) {
-            src = prow + ((2 * (step - kLatSteps)) ^ xswz) * 8;
-          } else {
-            src = prow + (step - kLatSteps) * 16 + g * 8;
-          }
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t*>(src),
-                                                      q[kk], s, 0, 0, 0);
+    for (int kk = 0; kk < kStep1 - kStep0; ++kk) {
+      constexpr int kLatSteps = DL / G::kKStep;
+      const int step = kStep0 + kk;
+      if constexpr (G::kBF16) {
+        bf16x8_t kop;
+        if (step < kLatSteps) {
+          if constexpr (G::kSwz)
+            kop = *(const DDT_LDS bf16x8_t*)(uintptr_t)((qk_base ^ ((step & 7) << 5)) +
+                                                        256 * (step >> 3));
+          else
+            kop = *reinterpret_cast<const bf16x8_t*>(krow + step * 16);
+        } else if constexpr (G::kPeChunks == 8) {
+          kop = *reinterpret_cast<const bf16x8_t*>(prow + ((2 * (step - kLatSteps)) ^ xswz) * 8);
         } else {
-          const T* src = step < kLatSteps ? krow + step * 2 : prow + (step - kLatSteps) * 2 + g;
-          s = __builtin_amdgcn_mfma_f32_32x32x2f32(*src, q[kk], s, 0, 0, 0);
+          kop = *reinterpret_cast<const bf16x8_t*>(prow + (step - kLatSteps) * 16 + g * 8);
         }
-      }
-      if constexpr (kSplit > 1) {
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4)
-          sm.xs[wave][i4][lane_it] =
-              make_float4(s[4 * i4], s[4 * i4 + 1], s[4 * i4 + 2], s[4 * i4 + 3]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, q[kk], s, 0, 0, 0);
+      } else {
+        const T* src = step < kLatSteps ? krow + step * 2 : prow + (step - kLatSteps) * 2 + g;
+        s = __builtin_amdgcn_mfma_f32_32x32x2f32(*src, q[kk], s, 0, 0, 0);
       }
     }
-    if constexpr (kSplit > 1) lds_barrier();
-    if (wave_live) {
-      if constexpr (kSplit > 1) {
-        // Full scores: own share plus the partner's (addition commutes, so both
-        // waves of the pair hold bit-identical sums).
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const float4 o4 = sm.xs[wave ^ 1][i4][lane_it];
-          s[4 * i4] += o4.x;
-          s[4 * i4 + 1] += o4.y;
-          s[4 * i4 + 2] += o4.z;
-          s[4 * i4 + 3] += o4.w;
-        }
-      }
-      // Lane owns row n and keys 8*(i/4) + 4*g + (i%4), i = 0..15.  Invisible
-      // keys get -inf; the scale (> 0) is applied inside the exponent.
-      const int key0 = kb * kTileKeys;
-      const uint32_t valid = (uint32_t)uni((int)sm.valid[kb % kRing]);
-      const bool tree_tile = key0 + kTileKeys > u.ri.L;
+  };
+
+  // Softmax of tile kb over this wave's 16 keys; leaves the value-product
+  // operands of all 32 keys in p0/p1 (r0/r1, heavy0/heavy1) or p + xp.
+  auto do_softmax = [&](int kb, int lane_it) __attribute__((always_inline)) {
+    const int n = lane_it & 31;
+    const int g = lane_it >> 5;
+    // Lane owns row n and keys 8*(i/4) + 4*g + (i%4) of register i; registers
+    // kOwn..kOwn+7 are this wave's keys.  Hand over the partner's, take ours.
+    sm.xs[wave][0][lane_it] = make_float4(s[kMate], s[kMate + 1], s[kMate + 2], s[kMate + 3]);
+    sm.xs[wave][1][lane_it] = make_float4(s[kMate + 4], s[kMate + 5], s[kMate + 6], s[kMate + 7]);
+    pair_post(&sm.xflag[wave], ++seq);
+    pair_wait(&sm.xflag[mate], seq);
+    float sv[8];
+    {
+      const float4 h0 = sm.xs[mate][0][lane_it];
+      const float4 h1 = sm.xs[mate][1][lane_it];
+      sv[0] = s[kOwn] + h0.x;
+      sv[1] = s[kOwn + 1] + h0.y;
+      sv[2] = s[kOwn + 2] + h0.z;
+      sv[3] = s[kOwn + 3] + h0.w;
+      sv[4] = s[kOwn + 4] + h1.x;
+      sv[5] = s[kOwn + 5] + h1.y;
+      sv[6] = s[kOwn + 6] + h1.z;
+      sv[7] = s[kOwn + 7] + h1.w;
+    }
+    // Invisible keys get -inf; the scale (> 0) is applied inside the exponent.
+    // Register j of sv is key 16*HALF + 8*(j/4) + 4*g + (j%4).
+    const int key0 = kb * kTileKeys;
+    const uint32_t valid = (uint32_t)uni((int)sm.valid[kb % kRing]);
+    const bool tree_tile = key0 + kTileKeys > u.ri.L;
+    if (tree_tile || valid != 0xFFFFFFFFu) {
       uint32_t okm = valid;
       if (tree_tile) {
         const uint64_t* vr = sm.visrow[rb * 32 + n];
         okm &= tree_window(vr[0], vr[1], key0 - u.ri.L);
       }
-      okm >>= 4 * g;  // now bit 8*(i/4) + (i%4) is key m of register i
-      float mx = -INFINITY;
+      okm >>= 16 * HALF + 4 * g;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        s[i] = ((okm >> (8 * (i >> 2) + (i & 3))) & 1u) ? s[i] : -INFINITY;
-        mx = fmaxf(mx, s[i]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.sl2;  // row max of this tile, log2 units
-      // Lazy rescaling: the reference max m_run moves only on the first
-      // visible key (accumulators still zero) or when the tile's max exceeds
-      // it by more than kRescaleLog2, so probabilities stay below
-      // 2^kRescaleLog2 and the accumulators are rescaled only on such jumps.
-      if (m_run == -INFINITY) m_run = mx;
-      const bool jump = mx > m_run + kRescaleLog2;
-      if (__ballot(jump) != 0) {
-        const float alpha = jump ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f;
-        if (jump) {
-          l_run *= alpha;
-          m_run = mx;
-        }
+      for (int j = 0; j < 8; ++j)
+        sv[j] = ((okm >> (8 * (j >> 2) + (j & 3))) & 1u) ? sv[j] : -INFINITY;
+    }
+    float mo = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                     fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+    mo = xor32_max(mo);  // row max over this wave's 16 keys (unscaled)
+
+    // Probabilities of this wave's keys against reference `mref`, posted
+    // (with their bf16 residuals when some key of a row is heavy) for the
+    // partner.
+    float psum = 0.0f;
+    bf16x8_t pk = bf16x8_t{}, rk = bf16x8_t{};
+    bool heavy = false;
+    auto post_p = [&](float mref) __attribute__((always_inline)) {
+      psum = 0.0f;
 #pragma unroll
-        for (int cb = 0; cb < G::kNCBh; ++cb) o[cb] *= alpha;
+      for (int j = 0; j < 8; ++j) {
+        p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[j], a.sl2, -mref));
+        psum += p[j];
       }
-      const float mref = m_run == -INFINITY ? 0.0f : m_run;
-      float psum = 0.0f;
-      float p[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], a.sl2, -mref));
-        psum += p[i];
-      }
-      l_run += psum;
-      // O^T += V^T P^T over this wave's output columns.
       if constexpr (G::kBF16) {
-        const bf16x8_t p0 = pack_p<false>(p);
-        const bf16x8_t p1 = pack_p<false>(p + 8);
-        // Residual pass when some row of this wave has a heavy key here (the
-        // largest probability of the row in this tile is exp2(mx - mref)).
-        const float pmax = __builtin_amdgcn_exp2f(mx - mref);
-        const float lrow = l_run + __shfl_xor(l_run, 32);
-        const bool heavy = __ballot(pmax > kHeavyShare * lrow) != 0;
-        // Pack the residual operands now so the fp32 probabilities die here.
-        bf16x8_t r0 = bf16x8_t{}, r1 = bf16x8_t{};
+        pk = pack_p<false>(p);
+        sm.xp[wave][0][lane_it] = __builtin_bit_cast(float4, pk);
+        // Residual pass when some row's largest probability here is a sizeable
+        // share of the row's running sum over this wave's keys (a lower bound
+        // of the full sum, so the test errs towards the residual).
+        const float pmax = __builtin_amdgcn_exp2f(__builtin_fmaf(mo, a.sl2, -mref));
+        const float lrow = xor32_sum(l_run + psum);
+        heavy = __ballot(pmax > kHeavyShare * lrow) != 0;
         if (heavy) {
-          r0 = pack_p<true>(p);
-          r1 = pack_p<true>(p + 8);
+          rk = pack_p<true>(p);
+          sm.xr[wave][lane_it] = __builtin_bit_cast(uint4, rk);
         }
-        const uint16_t* vbase = reinterpret_cast<const uint16_t*>(kt);
-        const int colh = 16 * ((lane_it >> 4) & 1);
-#pragma unroll
-        for (int cb = 0; cb < G::kNCBh; ++cb) {
-          const int c0 = (kCb0 + cb) * 32 + colh;
-          const bf16x8_t a0 = read_vt(vbase, G::kLatPitch, 4 * g, c0, lane_it);
-          const bf16x8_t a1 = read_vt(vbase, G::kLatPitch, 16 + 4 * g, c0, lane_it);
-          o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, p0, o[cb], 0, 0, 0);
-          o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, p1, o[cb], 0, 0, 0);
-        }
-        if (heavy) {
-#pragma unroll
-          for (int cb = 0; cb < G::kNCBh; ++cb) {
-            const int c0 = (kCb0 + cb) * 32 + colh;
-            const bf16x8_t a0 = read_vt(vbase, G::kLatPitch, 4 * g, c0, lane_it);
-            const bf16x8_t a1 = read_vt(vbase, G::kLatPitch, 16 + 4 * g, c0, lane_it);
-            o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, r0, o[cb], 0, 0, 0);
-            o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, r1, o[cb], 0, 0, 0);
-          }
-        }
+        sm.xheavy[wave] = heavy ? 1u : 0u;
       } else {
+        sm.xp[wave][0][lane_it] = make_float4(p[0], p[1], p[2], p[3]);
+        sm.xp[wave][1][lane_it] = make_float4(p[4], p[5], p[6], p[7]);
+      }
+    };
+    post_p(m_run == -INFINITY ? 0.0f : m_run);
+    sm.xm[wave][lane_it] = mo;
+    pair_post(&sm.xflag[wave], ++seq);
+    pair_wait(&sm.xflag[mate], seq);
+    // Lazy rescaling: the reference moves on a row's first visible key or
+    // when the pair's tile max exceeds it by more than kRescaleLog2, so
+    // probabilities stay below 2^kRescaleLog2.  Both waves see the same
+    // maxima, so they agree on whether to move.
+    const float mt = fmaxf(mo, sm.xm[mate][lane_it]) * a.sl2;
+    float m_new = m_run;
+    if (m_run == -INFINITY || mt > m_run + kRescaleLog2) m_new = mt;
+    if (__ballot(m_new != m_run) != 0) {
+      const float alpha =
+          (m_run == -INFINITY || m_new == m_run) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+      m_run = m_new;
 #pragma unroll
-        for (int cb = 0; cb < G::kNCBh; ++cb) {
-          const int c0 = (kCb0 + cb) * 32;
+      for (int cb = 0; cb < G::kNCBh; ++cb) o[cb] *= alpha;
+      post_p(m_run == -INFINITY ? 0.0f : m_run);
+      pair_post(&sm.xflag[wave], ++seq);
+      pair_wait(&sm.xflag[mate], seq);
+    }
+    l_run += psum;
+    if constexpr (G::kBF16) {
+      const bf16x8_t pm = __builtin_bit_cast(bf16x8_t, sm.xp[mate][0][lane_it]);
+      const bool heavy_m = uni((int)sm.xheavy[mate]) != 0;
+      p0 = HALF == 0 ? pk : pm;
+      p1 = HALF == 0 ? pm : pk;
+      heavy0 = HALF == 0 ? heavy : heavy_m;
+      heavy1 = HALF == 0 ? heavy_m : heavy;
+      if (heavy_m) {
+        const bf16x8_t rm = __builtin_bit_cast(bf16x8_t, sm.xr[mate][lane_it]);
+        r0 = HALF == 0 ? rk : rm;
+        r1 = HALF == 0 ? rm : rk;
+      } else {
+        r0 = rk;
+        r1 = rk;
+      }
+    }
+  };
+
+  // O^T += V^T P^T of tile kb over this wave's output columns, keys 0..15
+  // (operand of HALF 0) and 16..31 (operand of HALF 1).
+  auto do_pv = [&](int kb, int lane_it) __attribute__((always_inline)) {
+    const int n = lane_it & 31;
+    const int g = lane_it >> 5;
+    const T* kt = reinterpret_cast<const T*>(sm.stage[kb % kStages]);
+    if constexpr (G::kBF16) {
+      const uint16_t* vbase = reinterpret_cast<const uint16_t*>(kt);
+      const int colh = 16 * ((lane_it >> 4) & 1);
+      // V^T operands: keys k..k+3 (first read) and k+8..k+11 (second) with
+      // k = 4g (A0) or 16 + 4g (A1), columns 32*cb + colh + 0..15.
+      const VtAddr va(lds_addr(kt), lane_it);
+      auto vt = [&](int cb, int k1) -> bf16x8_t {
+        if constexpr (G::kSwz) return va.read(kCb0 + cb, k1);
+        else return read_vt(vbase, G::kLatPitch, 16 * k1 + 4 * g, (kCb0 + cb) * 32 + colh, lane_it);
+      };
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int m = 8 * (i >> 2) + 4 * g + (i & 3);
-            o[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kt[m * G::kLatPitch + c0 + n], p[i],
-                                                          o[cb], 0, 0, 0);
-          }
+      for (int cb = 0; cb < G::kNCBh; ++cb) {
+        const bf16x8_t a0 = vt(cb, 0);
+        const bf16x8_t a1 = vt(cb, 1);
+        o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, p0, o[cb], 0, 0, 0);
+        o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, p1, o[cb], 0, 0, 0);
+      }
+      if (heavy0) {
+#pragma unroll
+        for (int cb = 0; cb < G::kNCBh; ++cb)
+          o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt(cb, 0), r0, o[cb], 0, 0, 0);
+      }
+      if (heavy1) {
+#pragma unroll
+        for (int cb = 0; cb < G::kNCBh; ++cb)
+          o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt(cb, 1), r1, o[cb], 0, 0, 0);
+      }
+    } else {
+      float pa[16];
+      {
+        const float4 m0 = sm.xp[mate][0][lane_it];
+        const float4 m1 = sm.xp[mate][1][lane_it];
+        const float mp[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          pa[kOwn + j] = p[j];
+          pa[kMate + j] = mp[j];
+        }
+      }
+#pragma unroll
+      for (int cb = 0; cb < G::kNCBh; ++cb) {
+        const int c0 = (kCb0 + cb) * 32;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int m = 8 * (i >> 2) + 4 * g + (i & 3);
+          o[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kt[m * G::kLatPitch + c0 + n], pa[i],
+                                                        o[cb], 0, 0, 0);
         }
       }
     }
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's tile loads have landed in LDS
+  };
+
+  for (int kb = u.kb0; kb < u.kb1; ++kb) {
+    // Lane-derived offsets are recomputed every tile from an opaque copy of the
+    // lane id: a handful of VALU ops instead of registers held across the loop.
+    int lane_it = lane;
+    __asm__ __volatile__("" : "+v"(lane_it));
+    int32_t ahead = -1;
     if (tid < kTileKeys && kb + 2 < u.kb1)
-      publish_slots(sm.slot[(kb + 2) % kRing], &sm.valid[(kb + 2) % kRing], ahead, tid);
+      ahead = fetch_slot(slots_b, (kb + 2) * kTileKeys + tid, u.nkeys);
+    // Tile kb+1 goes to the stage tile kb-2 used (every wave finished it
+    // before the previous iteration's closing barrier).
+    if (kb + 1 < u.kb1)
+      issue_tile<T, DL, DR>(sm.stage[(kb + 1) % kStages], sm.slot[(kb + 1) % kRing], c_kv, k_pe,
+                            wave, lane_it);
+    // First half.
+    if (wave_live) {
+      if constexpr (GRP == 0) {
+        if (kb > u.kb0) do_pv(kb - 1, lane_it);
+        do_qk(kb, lane_it);
+      } else {
+        if (kb > u.kb0) do_softmax(kb - 1, lane_it);
+      }
+    }
+    lds_barrier();
+    // Second half.
+    if (wave_live) {
+      if constexpr (GRP == 0) {
+        do_softmax(kb, lane_it);
+      } else {
+        if (kb > u.kb0) do_pv(kb - 1, lane_it);
+        do_qk(kb, lane_it);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile kb+1 have landed in LDS
+    if (tid < kTileKeys && kb + 2 < u.kb1)
+      publish_slots(sm.slot[(kb + 2) % kRing], &sm.valid[(kb + 2) % kRing], ahead, a.num_slots,
+                    tid);
     __syncthreads();
   }
+  // Drain: the last tile's remaining phases.
+  if (wave_live) {
+    int lane_it = lane;
+    __asm__ __volatile__("" : "+v"(lane_it));
+    if constexpr (GRP == 1) do_softmax(u.kb1 - 1, lane_it);
+    do_pv(u.kb1 - 1, lane_it);
+  }
 
+  // Row sum: this lane's keys, its twin lane's (l ^ 32) and the partner's.
+  const float l_own = xor32_sum(l_run);
+  sm.xl[wave][lane] = l_own;
+  __syncthreads();
+  const float l = l_own + sm.xl[mate][lane];
   // Normalise and write: this lane holds row n, columns
   // (kCb0 + cb)*32 + 8*t + 4*g + {0..3} in o[cb][4t..4t+3].
-  const float l = l_run + __shfl_xor(l_run, 32);
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
   const float lse_v = l > 0.0f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
   float* dst = nullptr;
@@ -671,8 +900,11 @@ __global__ __launch_bounds__(kThreads) void verify_attn_kernel(
   __shared__ Smem<T, DL, DR> sm;
   const Args args{q_lat, q_pe, c_kv, k_pe, num_slots, req_to_slot, max_kv, vis, Q, H,
                   sm_scale * kLog2e, out, lse, ws_o, ws_lse};
-  const int half = uni((int)(threadIdx.x >> 6) % kSplit);
+  // Role of this wave: HALF = wave % 2 (share of a pair), GRP = wave / 4.
+  const int role = uni((int)((threadIdx.x >> 6) & 1) + 2 * (int)(threadIdx.x >> 8));
 
+  if ((threadIdx.x & 63) == 0) sm.xflag[threadIdx.x >> 6] = 0;
+  int seq = 0;  // this wave's pair-sync sequence (see pair_post)
   work_prefix<kThreads>(sm.pref, sm.wsum, prefix_len, n_nodes, B, Q, H, max_kv, RT);
   const long long Wtot = uni(sm.pref[B]);
   const long long Gn = gridDim.x;
@@ -692,10 +924,19 @@ __global__ __launch_bounds__(kThreads) void verify_attn_kernel(
     b = uni(lo);
   }
 
+  // Units of [start, end): the head (holding `start`) may begin mid-row-tile,
+  // every later unit begins at key tile 0.  Later units run first and the head
+  // last, so that at any moment the workgroups of one XCD (consecutive ranges,
+  // mostly the same request) stream nearly the same key tiles and share them
+  // in L2 instead of trailing each other by a range's offset.
+  const int b_head = b;
+  for (int pass = 0; pass < 2; ++pass) {
   long long pos = start;
+  b = b_head;
   while (pos < end) {
     while (uni(sm.pref[b + 1]) <= pos) ++b;
     b = uni(b);
+    const bool head = pos == start;
     Unit u;
     u.b = b;
     u.ri = req_info(prefix_len, n_nodes, b, Q, H, max_kv, RT);
@@ -705,103 +946,175 @@ __global__ __launch_bounds__(kThreads) void verify_attn_kernel(
     const long long left = end - pos;
     u.kb1 = (long long)(u.ri.nkb - u.kb0) < left ? u.ri.nkb : u.kb0 + (int)left;
     u.complete = u.kb0 == 0 && u.kb1 == u.ri.nkb;
-    u.slot = 2 * gid + (pos == start ? 0 : 1);
+    u.slot = 2 * gid + (head ? 0 : 1);
     u.nkeys = u.ri.L + u.ri.nb;
     pos += u.kb1 - u.kb0;
-    if (kSplit == 1 || half == 0) run_unit<T, DL, DR, 0>(sm, args, u);
-    else run_unit<T, DL, DR, (kSplit > 1 ? 1 : 0)>(sm, args, u);
+    if (head != (pass == 1)) continue;
+    switch (role) {
+      case 0: run_unit<T, DL, DR, 0, 0>(sm, args, u, seq); break;
+      case 1: run_unit<T, DL, DR, 1, 0>(sm, args, u, seq); break;
+      case 2: run_unit<T, DL, DR, 0, 1>(sm, args, u, seq); break;
+      default: run_unit<T, DL, DR, 1, 1>(sm, args, u, seq); break;
+    }
+    if (pass == 1) break;
+  }
   }
 }
 
 // Combines the partial results of row tiles whose key range was cut, and writes
-// the padding output of row tiles with no live row.  One workgroup per 16 rows
-// of a row tile: the contributing partial slots are listed once in LDS, each
-// row's total log-sum-exp is computed once, then every thread accumulates
-// weighted float4 chunks of the partial outputs.
+// the padding output of row tiles with no live row.  One workgroup per
+// MergeGeo::kRows rows of a row tile.  The contributing partial slots are
+// compacted once into LDS; each row's total log-sum-exp is reduced by a group
+// of lanes; then, for batches of kMergeBatch contributors, the per-(contributor,
+// row) weights go to LDS and every thread accumulates its float4 chunks with
+// all of a batch's loads independent of one another.
+template <int DL>
+struct MergeGeo {
+  static constexpr int kChunks = DL / 4;                          // float4 per row
+  static constexpr int kItems = DL >= 256 ? 4 : 1;                // chunks per thread
+  static constexpr int kRows = kMergeThreads * kItems / kChunks;  // rows per workgroup
+  static constexpr int kLanesPerRow = kMergeThreads / kRows;      // lanes of a row's LSE
+  static_assert(kRows * kChunks == kMergeThreads * kItems, "merge tiling");
+  static_assert(kRowsPerWG % kRows == 0 && kLanesPerRow <= kWave, "merge tiling");
+};
+constexpr int kMergeBatch = 32;  // contributors whose weights are staged at once
+
 template <int DL>
 __global__ __launch_bounds__(kMergeThreads) void verify_merge_kernel(
     const int32_t* __restrict__ prefix_len, const int32_t* __restrict__ n_nodes, int B, int Q,
     int H, int RT, int max_kv, int grid_attn, float* __restrict__ out, float* __restrict__ lse,
     const float* __restrict__ ws_o, const float* __restrict__ ws_lse) {
+  using MG = MergeGeo<DL>;
   __shared__ long long s_pref[kMaxBatch + 1];
   __shared__ long long s_wsum[kMergeThreads / kWave];
   __shared__ int s_src[kMaxGrid];
-  __shared__ float s_lse[kMergeRows];
+  __shared__ int s_cnt;
+  __shared__ float s_lse[MG::kRows];
+  __shared__ float s_w[kMergeBatch][MG::kRows];
   work_prefix<kMergeThreads>(s_pref, s_wsum, prefix_len, n_nodes, B, Q, H, max_kv, RT);
   const int tid = threadIdx.x;
   const int u = blockIdx.x;
   const int b = u / RT, rt = u % RT;
   const ReqInfo ri = req_info(prefix_len, n_nodes, b, Q, H, max_kv, RT);
   const long long QH = (long long)Q * H;
-  const int r0 = blockIdx.y * kMergeRows;                  // first row within the tile
-  const long long r_begin = (long long)rt * kRowsPerWG + r0;
-  if (r_begin >= QH) return;
+  const int r0 = blockIdx.y * MG::kRows;                   // first row within the tile
+  if ((long long)rt * kRowsPerWG + r0 >= QH) return;
   const long long Wtot = s_pref[B];
   const long long Gn = grid_attn;
 
   const bool has_work = rt < ri.vt;
-  long long S_u = 0;
-  int cnt = 0;
   if (has_work) {
-    S_u = s_pref[b] + (long long)rt * ri.nkb;
+    const long long S_u = s_pref[b] + (long long)rt * ri.nkb;
     const long long g_first = range_owner(S_u, Wtot, Gn);
     const long long g_last = range_owner(S_u + ri.nkb - 1, Wtot, Gn);
     if (g_first == g_last) return;  // written directly by the attention kernel
-    cnt = (int)(g_last - g_first + 1);
     // Each contributing workgroup (non-empty range) wrote its partial for this
     // tile into slot 2g when the tile holds the start of its range, else 2g+1.
-    for (int k = tid; k < cnt; k += kMergeThreads) {
-      const long long gg = g_first + k;
-      const long long s0 = range_start(gg, Wtot, Gn);
-      const long long s1 = range_start(gg + 1, Wtot, Gn);
-      s_src[k] = s0 == s1 ? -1 : (int)(2 * gg + (s0 >= S_u ? 0 : 1));
+    if (tid < kWave) {
+      const int cnt = (int)(g_last - g_first + 1);
+      int base = 0;
+      for (int k0 = 0; k0 < cnt; k0 += kWave) {
+        const long long gg = g_first + k0 + tid;
+        int src = -1;
+        if (k0 + tid < cnt) {
+          const long long s0 = range_start(gg, Wtot, Gn);
+          const long long s1 = range_start(gg + 1, Wtot, Gn);
+          if (s0 != s1) src = (int)(2 * gg + (s0 >= S_u ? 0 : 1));
+        }
+        const uint64_t m = __ballot(src >= 0);
+        const int at = base + (int)__builtin_amdgcn_mbcnt_hi(
+                                  (unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+        if (src >= 0) s_src[at] = src;
+        base += __popcll(m);
+      }
+      if (tid == 0) s_cnt = base;
     }
+  } else if (tid == 0) {
+    s_cnt = 0;
   }
   __syncthreads();
-  if (tid < kMergeRows) {
-    const int rr = r0 + tid;
+  const int cnt = s_cnt;
+
+  // Row log-sum-exp: kLanesPerRow lanes per row, each over every
+  // kLanesPerRow-th contributor, then a butterfly over the group.
+  {
+    const int rl = tid / MG::kLanesPerRow, j = tid % MG::kLanesPerRow;
+    const int rr = r0 + rl;
     const long long r_loc = (long long)rt * kRowsPerWG + rr;
+    const bool live = r_loc < QH && (int)(r_loc / H) < ri.nb;
     float m = -INFINITY, z = 0.0f;
-    if (has_work && r_loc < QH && (int)(r_loc / H) < ri.nb) {
-      for (int k = 0; k < cnt; ++k) {
-        const int src = s_src[k];
-        if (src < 0) continue;
-        const float v = ws_lse[(long long)src * kRowsPerWG + rr];
+    if (live) {
+      for (int k = j; k < cnt; k += MG::kLanesPerRow) {
+        const float v = ws_lse[(long long)s_src[k] * kRowsPerWG + rr];
         if (v == -INFINITY) continue;
         if (v > m) {
-          z = z * expf(m - v) + 1.0f;
+          z = z * __expf(m - v) + 1.0f;
           m = v;
         } else {
-          z += expf(v - m);
+          z += __expf(v - m);
         }
       }
     }
-    s_lse[tid] = z > 0.0f ? m + logf(z) : -INFINITY;
-  }
-  __syncthreads();
-  constexpr int kChunks = DL / 4;
-  for (int idx = tid; idx < kMergeRows * kChunks; idx += kMergeThreads) {
-    const int rl = idx / kChunks, chunk = idx % kChunks;
-    const int rr = r0 + rl;
-    const long long r_loc = (long long)rt * kRowsPerWG + rr;
-    if (r_loc >= QH) continue;
-    const long long grow = (long long)b * QH + r_loc;
-    const float lt = s_lse[rl];
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (lt != -INFINITY) {
-      for (int k = 0; k < cnt; ++k) {
-        const int src = s_src[k];
-        if (src < 0) continue;
-        const long long sr = (long long)src * kRowsPerWG + rr;
-        const float w = expf(ws_lse[sr] - lt);
-        const float4 v = *reinterpret_cast<const float4*>(ws_o + sr * DL + chunk * 4);
-        acc.x += w * v.x;
-        acc.y += w * v.y;
-        acc.z += w * v.z;
-        acc.w += w * v.w;
+#pragma unroll
+    for (int off = 1; off < MG::kLanesPerRow; off <<= 1) {
+      const float m2 = __shfl_xor(m, off), z2 = __shfl_xor(z, off);
+      const float mn = fmaxf(m, m2);
+      if (mn != -INFINITY) {
+        z = (m == -INFINITY ? 0.0f : z * __expf(m - mn)) +
+            (m2 == -INFINITY ? 0.0f : z2 * __expf(m2 - mn));
+        m = mn;
       }
     }
-    *reinterpret_cast<float4*>(out + grow * DL + chunk * 4) = acc;
+    if (j == 0) s_lse[rl] = z > 0.0f ? m + __logf(z) : -INFINITY;
+  }
+  __syncthreads();
+
+  float4 acc[MG::kItems];
+  int rl_of[MG::kItems];
+#pragma unroll
+  for (int it = 0; it < MG::kItems; ++it) {
+    acc[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+    rl_of[it] = (tid + it * kMergeThreads) / MG::kChunks;
+  }
+  const int chunk = tid % MG::kChunks;
+  for (int k0 = 0; k0 < cnt; k0 += kMergeBatch) {
+    const int nk = cnt - k0 < kMergeBatch ? cnt - k0 : kMergeBatch;
+    for (int e = tid; e < kMergeBatch * MG::kRows; e += kMergeThreads) {
+      const int k = e / MG::kRows, rl = e % MG::kRows;
+      const float lt = s_lse[rl];
+      float w = 0.0f;
+      if (k < nk && lt != -INFINITY) {
+        const float v = ws_lse[(long long)s_src[k0 + k] * kRowsPerWG + r0 + rl];
+        if (v != -INFINITY) w = __expf(v - lt);
+      }
+      s_w[k][rl] = w;
+    }
+    __syncthreads();
+    // Rows that no contributor wrote (not live) read stale workspace here; their
+    // sums are discarded below, and every address stays inside the workspace.
+#pragma unroll 4
+    for (int k = 0; k < nk; ++k) {
+      const float* src = ws_o + ((long long)s_src[k0 + k] * kRowsPerWG + r0) * DL + chunk * 4;
+#pragma unroll
+      for (int it = 0; it < MG::kItems; ++it) {
+        const float w = s_w[k][rl_of[it]];
+        const float4 v = *reinterpret_cast<const float4*>(src + (long long)rl_of[it] * DL);
+        acc[it].x = __builtin_fmaf(w, v.x, acc[it].x);
+        acc[it].y = __builtin_fmaf(w, v.y, acc[it].y);
+        acc[it].z = __builtin_fmaf(w, v.z, acc[it].z);
+        acc[it].w = __builtin_fmaf(w, v.w, acc[it].w);
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int it = 0; it < MG::kItems; ++it) {
+    const long long r_loc = (long long)rt * kRowsPerWG + r0 + rl_of[it];
+    if (r_loc >= QH) continue;
+    const long long grow = (long long)b * QH + r_loc;
+    const float lt = s_lse[rl_of[it]];
+    *reinterpret_cast<float4*>(out + grow * DL + chunk * 4) =
+        lt != -INFINITY ? acc[it] : make_float4(0.f, 0.f, 0.f, 0.f);
     if (lse && chunk == 0) lse[grow] = lt;
   }
 }
@@ -821,7 +1134,7 @@ hipError_t launch_impl(const void* q_lat, const void* q_pe, const void* c_kv, co
                      sm_scale, out, lse, ws_o, ws_lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((verify_merge_kernel<DL>), dim3(B * plan.row_tiles, kRowsPerWG / kMergeRows),
+  hipLaunchKernelGGL((verify_merge_kernel<DL>), dim3(B * plan.row_tiles, kRowsPerWG / MergeGeo<DL>::kRows),
                      dim3(kMergeThreads), 0,
                      stream, prefix_len, n_nodes, B, Q, H, plan.row_tiles, max_kv, plan.grid,
                      out, lse, ws_o, ws_lse);
