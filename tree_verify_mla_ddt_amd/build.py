@@ -18,7 +18,7 @@ ARCH = os.environ.get("DDT_OFFLOAD_ARCH", "gfx950")
 def hipcc_command(out_path: str, resource_report: bool = False) -> list[str]:
     cmd = ["hipcc", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-fno-gpu-flush-denormals-to-zero",
-           # packed fp32 VALU forms are left to nobody: see the design notes
+           # no packed fp32 VALU instructions (v_pk_*_f32) anywhere in the library
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-Wall", "-I", os.path.join(HERE, "..", "include")]
     if resource_report:

@@ -226,7 +226,7 @@ template <typename T, int DL, int DR>
 struct Smem {
   using G = Geo<T, DL, DR>;
   alignas(1024) unsigned char stage[kStages][G::kStageBytes];
-  int32_t slot[kRing][kTileKeys];   // pool slot of each key of a tile (0 when invalid)
+  alignas(16) int32_t slot[kRing][kTileKeys];  // pool slot of each key of a tile (0 when invalid)
   uint32_t valid[kRing];            // bit m: key m of the tile is in range with a valid slot
   float4 xs[kWaves][2][kWave];      // partial scores of the partner's keys
   float4 xp[kWaves][G::kBF16 ? 1 : 2][kWave];  // probabilities of own keys (bf16: packed)
@@ -297,20 +297,26 @@ __device__ __forceinline__ void issue_tile(unsigned char* stage, const int32_t* 
   using G = Geo<T, DL, DR>;
   if constexpr (G::kLatChunks == kWave && G::kPeChunks == 8 && G::kLatInstr % kWaves == 0) {
     constexpr int kPerWave = G::kLatInstr / kWaves;
+    static_assert(kPerWave == 4, "one 16-byte read of slot ids per wave");
+    // This wave's four latent keys in one LDS read, and (waves < kPeInstr) the
+    // rope key of this lane, before waiting on either.
+    const int4 sl = *reinterpret_cast<const int4*>(ring_slots + wave * kPerWave);
+    const int pe_key = wave * 8 + (lane >> 3);
+    const int pe_row = wave < G::kPeInstr ? ring_slots[pe_key] : 0;
+    const int rows[4] = {sl.x, sl.y, sl.z, sl.w};
 #pragma unroll
     for (int it = 0; it < kPerWave; ++it) {
       const int key = wave * kPerWave + it;
-      const long long row = uni(ring_slots[key]);
+      const long long row = uni(rows[it]);
       // Lane l fills physical chunk l, i.e. logical chunk l ^ swz(key).
-      dma16(static_cast<const void*>(c_kv + row * DL + (lane ^ swz(key)) * G::kPerChunk), lds_addr((stage + key * G::kLatPitchB)));
+      dma16(static_cast<const void*>(c_kv + row * DL + (lane ^ swz(key)) * G::kPerChunk),
+            lds_addr(stage + key * G::kLatPitchB));
     }
     if (wave < G::kPeInstr) {
       // 8 keys x 8 chunks; key & 7 == lane / 8, so the swizzled chunk depends
       // on the lane only.
-      const int key = wave * 8 + (lane >> 3);
-      const long long row = ring_slots[key];
-      const T* src = k_pe + row * DR + (((lane & 7) ^ (lane >> 3)) * G::kPerChunk);
-      dma16(static_cast<const void*>(src), lds_addr((stage + G::kLatBytes + wave * kWave * 16)));
+      const T* src = k_pe + (long long)pe_row * DR + (((lane & 7) ^ (lane >> 3)) * G::kPerChunk);
+      dma16(static_cast<const void*>(src), lds_addr(stage + G::kLatBytes + wave * kWave * 16));
     }
   } else {
 #pragma unroll
@@ -479,9 +485,8 @@ __device__ __forceinline__ void pair_wait(int* flag, int seq) {
   __asm__ __volatile__("" ::: "memory");
 }
 
-// One row tile over key tiles [kb0, kb1) by the waves of share HALF of group
-// GRP (both compile time, so every LDS operand address is one base register
-// plus an immediate and every phase decision is static).
+// One row tile over key tiles [kb0, kb1) by the waves of share HALF (compile
+// time, so every LDS operand address is one base register plus an immediate).
 // The two waves of a pair split the work of each tile three ways:
 //   QK^T  over their half of the 576 contraction dimensions (partial scores of
 //         all 32 keys), then exchange the partial scores of the partner's keys;
@@ -492,14 +497,10 @@ __device__ __forceinline__ void pair_wait(int* flag, int seq) {
 // the pair's combined tile max.  Probabilities are computed against the
 // current reference before the maxima are exchanged; in the rare tiles where
 // the reference moves, both waves recompute and exchange them again.
-// Ping-pong: group 0 (pairs 0, 1: waves 0..3, one per SIMD) and group 1 (pairs
-// 2, 3: waves 4..7) run half a tile apart, so that on every SIMD one wave
-// issues matrix instructions while the other does the exchange and softmax:
-//   iteration t, first half:   group 0: PV(t-1), QK(t)   group 1: softmax(t-1)
-//   iteration t, second half:  group 0: softmax(t)       group 1: PV(t-1), QK(t)
-// Tiles t-1 and t are read during iteration t while tile t+1 loads, so the
-// key tiles rotate through three LDS stages (stage of tile t = t mod 3).
-template <typename T, int DL, int DR, int HALF, int GRP>
+// Iteration t issues the loads of tile t+1, then runs PV of tile t-1 and QK
+// and softmax of tile t, so tiles t-1 and t are read while t+1 loads: the key
+// tiles rotate through three LDS stages (stage of tile t = t mod 3).
+template <typename T, int DL, int DR, int HALF>
 __device__ __forceinline__ void run_unit(Smem<T, DL, DR>& sm, const Args& a, const Unit& u,
                                          int& seq) {
   using G = Geo<T, DL, DR>;
@@ -589,6 +590,9 @@ __device__ __forceinline__ void run_unit(Smem<T, DL, DR>& sm, const Args& a, con
   bf16x8_t p0 = bf16x8_t{}, p1 = bf16x8_t{};  // keys 0..15 / 16..31 (bf16 inputs)
   bf16x8_t r0 = bf16x8_t{}, r1 = bf16x8_t{};  // their rounding residuals
   bool heavy0 = false, heavy1 = false;
+  // The partner's share of the row sum as of its previous tile (a lower bound
+  // of its current share), for the residual test.
+  float l_mate = 0.0f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) p[j] = 0.0f;
 
@@ -692,10 +696,11 @@ __device__ __forceinline__ void run_unit(Smem<T, DL, DR>& sm, const Args& a, con
         pk = pack_p<false>(p);
         sm.xp[wave][0][lane_it] = __builtin_bit_cast(float4, pk);
         // Residual pass when some row's largest probability here is a sizeable
-        // share of the row's running sum over this wave's keys (a lower bound
-        // of the full sum, so the test errs towards the residual).
+        // share of the row's running sum (this wave's keys so far plus the
+        // partner's up to its previous tile: a lower bound of the full sum, so
+        // the test errs towards the residual).
         const float pmax = __builtin_amdgcn_exp2f(__builtin_fmaf(mo, a.sl2, -mref));
-        const float lrow = xor32_sum(l_run + psum);
+        const float lrow = xor32_sum(l_run + psum) + l_mate;
         heavy = __ballot(pmax > kHeavyShare * lrow) != 0;
         if (heavy) {
           rk = pack_p<true>(p);
@@ -709,8 +714,10 @@ __device__ __forceinline__ void run_unit(Smem<T, DL, DR>& sm, const Args& a, con
     };
     post_p(m_run == -INFINITY ? 0.0f : m_run);
     sm.xm[wave][lane_it] = mo;
+    if constexpr (G::kBF16) sm.xl[wave][lane_it] = xor32_sum(l_run);
     pair_post(&sm.xflag[wave], ++seq);
     pair_wait(&sm.xflag[mate], seq);
+    if constexpr (G::kBF16) l_mate = sm.xl[mate][lane_it];
     // Lazy rescaling: the reference moves on a row's first visible key or
     // when the pair's tile max exceeds it by more than kRescaleLog2, so
     // probabilities stay below 2^kRescaleLog2.  Both waves see the same
@@ -722,6 +729,7 @@ __device__ __forceinline__ void run_unit(Smem<T, DL, DR>& sm, const Args& a, con
       const float alpha =
           (m_run == -INFINITY || m_new == m_run) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
+      l_mate *= alpha;
       m_run = m_new;
 #pragma unroll
       for (int cb = 0; cb < G::kNCBh; ++cb) o[cb] *= alpha;
@@ -819,24 +827,10 @@ __device__ __forceinline__ void run_unit(Smem<T, DL, DR>& sm, const Args& a, con
     if (kb + 1 < u.kb1)
       issue_tile<T, DL, DR>(sm.stage[(kb + 1) % kStages], sm.slot[(kb + 1) % kRing], c_kv, k_pe,
                             wave, lane_it);
-    // First half.
     if (wave_live) {
-      if constexpr (GRP == 0) {
-        if (kb > u.kb0) do_pv(kb - 1, lane_it);
-        do_qk(kb, lane_it);
-      } else {
-        if (kb > u.kb0) do_softmax(kb - 1, lane_it);
-      }
-    }
-    lds_barrier();
-    // Second half.
-    if (wave_live) {
-      if constexpr (GRP == 0) {
-        do_softmax(kb, lane_it);
-      } else {
-        if (kb > u.kb0) do_pv(kb - 1, lane_it);
-        do_qk(kb, lane_it);
-      }
+      if (kb > u.kb0) do_pv(kb - 1, lane_it);
+      do_qk(kb, lane_it);
+      do_softmax(kb, lane_it);
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile kb+1 have landed in LDS
     if (tid < kTileKeys && kb + 2 < u.kb1)
@@ -844,11 +838,10 @@ __device__ __forceinline__ void run_unit(Smem<T, DL, DR>& sm, const Args& a, con
                     tid);
     __syncthreads();
   }
-  // Drain: the last tile's remaining phases.
+  // Drain: the last tile's value product.
   if (wave_live) {
     int lane_it = lane;
     __asm__ __volatile__("" : "+v"(lane_it));
-    if constexpr (GRP == 1) do_softmax(u.kb1 - 1, lane_it);
     do_pv(u.kb1 - 1, lane_it);
   }
 
@@ -900,8 +893,7 @@ __global__ __launch_bounds__(kThreads) void verify_attn_kernel(
   __shared__ Smem<T, DL, DR> sm;
   const Args args{q_lat, q_pe, c_kv, k_pe, num_slots, req_to_slot, max_kv, vis, Q, H,
                   sm_scale * kLog2e, out, lse, ws_o, ws_lse};
-  // Role of this wave: HALF = wave % 2 (share of a pair), GRP = wave / 4.
-  const int role = uni((int)((threadIdx.x >> 6) & 1) + 2 * (int)(threadIdx.x >> 8));
+  const int half = uni((int)((threadIdx.x >> 6) & 1));  // share of the pair: wave % 2
 
   if ((threadIdx.x & 63) == 0) sm.xflag[threadIdx.x >> 6] = 0;
   int seq = 0;  // this wave's pair-sync sequence (see pair_post)
@@ -950,12 +942,8 @@ __global__ __launch_bounds__(kThreads) void verify_attn_kernel(
     u.nkeys = u.ri.L + u.ri.nb;
     pos += u.kb1 - u.kb0;
     if (head != (pass == 1)) continue;
-    switch (role) {
-      case 0: run_unit<T, DL, DR, 0, 0>(sm, args, u, seq); break;
-      case 1: run_unit<T, DL, DR, 1, 0>(sm, args, u, seq); break;
-      case 2: run_unit<T, DL, DR, 0, 1>(sm, args, u, seq); break;
-      default: run_unit<T, DL, DR, 1, 1>(sm, args, u, seq); break;
-    }
+    if (half == 0) run_unit<T, DL, DR, 0>(sm, args, u, seq);
+    else run_unit<T, DL, DR, 1>(sm, args, u, seq);
     if (pass == 1) break;
   }
   }
