@@ -72,6 +72,65 @@ def source_digest():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+COPY_BYTES = 256 << 20  # the --copy-calibration copy
+ATTN_KERNELS = ("verify_attn_kernel", "verify_merge_kernel")
+
+
+def _counter_rows(directory):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no *counter_collection.csv under {directory}")
+    return rows
+
+
+def _per_launch_kib(rows, counter):
+    """(attention-call KiB per launch, copy KiB) for one counter: the verify_attn
+    call's kernels summed per launch (mean over launches), and the 256 MiB copy."""
+    per_kernel, copy = {}, []
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        name, v = r["Kernel_Name"], float(r["Counter_Value"])
+        for k in ATTN_KERNELS:
+            if k in name:
+                per_kernel.setdefault(k, []).append(v)
+        if "copyBuffer" in name and int(r["Grid_Size"]) * 2048 == COPY_BYTES:
+            copy.append(v)  # the calibration copy moves 2 KiB per work-item
+    if "verify_attn_kernel" not in per_kernel or not copy:
+        raise SystemExit(f"{counter}: attention kernel or calibration copy missing")
+    att = sum(sum(v) / len(v) for v in per_kernel.values())
+    return att, sum(copy) / len(copy)
+
+
+def write_traffic(workload, fetch_dir, write_dir):
+    """Record HBM bytes per verify_attn call from two rocprofv3 --pmc runs
+    (FETCH_SIZE, WRITE_SIZE), each counter scaled by what it reads for a plain
+    copy of COPY_BYTES (read once, written once)."""
+    f_att, f_copy = _per_launch_kib(_counter_rows(fetch_dir), "FETCH_SIZE")
+    w_att, w_copy = _per_launch_kib(_counter_rows(write_dir), "WRITE_SIZE")
+    f_scale, w_scale = COPY_BYTES / (f_copy * 1024.0), COPY_BYTES / (w_copy * 1024.0)
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        rec = {}
+    if rec.get("source_sha256_16") != source_digest():
+        rec = {"source_sha256_16": source_digest(), "workloads": {}}
+    rec["workloads"][workload] = {
+        "bytes_per_launch": round(f_att * 1024.0 * f_scale + w_att * 1024.0 * w_scale),
+        "fetch_kib_raw": round(f_att, 1), "write_kib_raw": round(w_att, 1),
+        "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(rec["workloads"][workload]))
+
+
 def measured_traffic(workload):
     """HBM bytes per attention launch from committed rocprofv3 counter runs, or
     None when absent or taken on a different kernel source."""
@@ -233,7 +292,13 @@ def main():
                     help="also run a plain 256 MiB device copy (reference for byte counters)")
     ap.add_argument("--workload", default=PRIMARY,
                     help="headline workload (default: the batch-1 configuration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="record the workload's HBM bytes per attention call from two "
+                         "rocprofv3 --pmc output directories (FETCH_SIZE, WRITE_SIZE) and exit")
     args = ap.parse_args()
+    if args.traffic_from:
+        write_traffic(args.workload, *args.traffic_from)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not "
               f"supported (the step is single-GPU: no sharding or collectives).", file=sys.stderr)

@@ -824,11 +824,19 @@ __device__ __forceinline__ void run_unit(Smem<T, DL, DR>& sm, const Args& a, con
       ahead = fetch_slot(slots_b, (kb + 2) * kTileKeys + tid, u.nkeys);
     // Tile kb+1 goes to the stage tile kb-2 used (every wave finished it
     // before the previous iteration's closing barrier).
-    if (kb + 1 < u.kb1)
+    // The two waves of a pair issue their loads at different points of the
+    // iteration, so the CU's load path is not hit by every wave at once.
+    const bool dma_next = kb + 1 < u.kb1;
+    if (dma_next && (HALF == 0 || !wave_live || kb == u.kb0))
       issue_tile<T, DL, DR>(sm.stage[(kb + 1) % kStages], sm.slot[(kb + 1) % kRing], c_kv, k_pe,
                             wave, lane_it);
     if (wave_live) {
-      if (kb > u.kb0) do_pv(kb - 1, lane_it);
+      if (kb > u.kb0) {
+        do_pv(kb - 1, lane_it);
+        if (HALF == 1 && dma_next)
+          issue_tile<T, DL, DR>(sm.stage[(kb + 1) % kStages], sm.slot[(kb + 1) % kRing], c_kv,
+                                k_pe, wave, lane_it);
+      }
       do_qk(kb, lane_it);
       do_softmax(kb, lane_it);
     }
