@@ -34,8 +34,9 @@ hipError_t launch_tree_accept(const int32_t* node_token, const int32_t* parent,
 // workgroups (see verify_attn.hip); partial results go to the workspace and a
 // merge kernel combines them.
 struct AttnPlan {
-  int grid;          // attention workgroups (multiple of 8)
+  int grid;          // attention workgroups (at most one per CU)
   int row_tiles;     // ceil(Q*H / 128)
+  int num_cu;        // compute units the plan was made for
   size_t ws_bytes;   // workspace bytes needed
 };
 AttnPlan plan_verify_attn(int B, int Q, int H, int max_kv, int d_lat, int num_cu);

@@ -71,7 +71,10 @@ constexpr int kRing = 3;                 // slot-id ring (tiles kb .. kb+2)
 constexpr int kStages = 3;               // key-tile stages in LDS (tiles kb-1 .. kb+1)
 constexpr int kMergeThreads = 256;
 constexpr int kMaxGrid = 1024;           // upper bound of the attention grid
-constexpr int kMinTilesPerWG = 8;        // key tiles per workgroup before splitting further
+#ifndef DDT_MIN_TILES
+#define DDT_MIN_TILES 6
+#endif
+constexpr int kMinTilesPerWG = DDT_MIN_TILES;  // key tiles per workgroup before splitting further
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // A tile takes the residual pass when some key's probability exceeds this share
@@ -897,7 +900,7 @@ __global__ __launch_bounds__(kThreads) void verify_attn_kernel(
     int max_kv, const int32_t* __restrict__ prefix_len, const int32_t* __restrict__ n_nodes,
     const uint64_t* __restrict__ vis, int B, int Q, int H, int RT, float sm_scale,
     float* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o,
-    float* __restrict__ ws_lse) {
+    float* __restrict__ ws_lse, long long* __restrict__ ws_pref) {
   __shared__ Smem<T, DL, DR> sm;
   const Args args{q_lat, q_pe, c_kv, k_pe, num_slots, req_to_slot, max_kv, vis, Q, H,
                   sm_scale * kLog2e, out, lse, ws_o, ws_lse};
@@ -907,8 +910,14 @@ __global__ __launch_bounds__(kThreads) void verify_attn_kernel(
   int seq = 0;  // this wave's pair-sync sequence (see pair_post)
   work_prefix<kThreads>(sm.pref, sm.wsum, prefix_len, n_nodes, B, Q, H, max_kv, RT);
   const long long Wtot = uni(sm.pref[B]);
+  if (blockIdx.x == 0)  // for the merge kernel
+    for (int i = threadIdx.x; i <= B; i += kThreads) ws_pref[i] = sm.pref[i];
   const long long Gn = gridDim.x;
-  const long long gid = (long long)(blockIdx.x % kXcds) * (Gn / kXcds) + blockIdx.x / kXcds;
+  // Logical id: workgroups are dealt to the XCDs round-robin (blockIdx % 8), so
+  // XCD x gets the consecutive logical ids [start_x, start_x + count_x).
+  const long long xcd = blockIdx.x % kXcds;
+  const long long gid = xcd * (Gn / kXcds) + (xcd < Gn % kXcds ? xcd : Gn % kXcds) +
+                        blockIdx.x / kXcds;
   const long long start = range_start(gid, Wtot, Gn);
   const long long end = range_start(gid + 1, Wtot, Gn);
   if (start >= end) return;
@@ -958,14 +967,188 @@ __global__ __launch_bounds__(kThreads) void verify_attn_kernel(
 }
 
 // Combines the partial results of row tiles whose key range was cut, and writes
-// the padding output of row tiles with no live row.  One workgroup per
-// MergeGeo::kRows rows of a row tile.  The contributing partial slots are
-// compacted once into LDS; each row's total log-sum-exp is reduced by a group
-// of lanes; then, for batches of kMergeBatch contributors, the per-(contributor,
-// row) weights go to LDS and every thread accumulates its float4 chunks with
-// all of a batch's loads independent of one another.
-template <int DL>
+// the padding output of row tiles with no live row.  Two variants share the
+// contributor rule (slot 2g holds a workgroup's head unit, 2g+1 its tail):
+//  * verify_merge_kernel (few row tiles, as at batch 1): thin workgroups of
+//    MergeGeo::kRows rows, so that many CUs share the work; the work prefix
+//    comes from the workspace (the attention kernel's first workgroup stores
+//    it); the contributing partial slots are compacted once into LDS; each
+//    row's total log-sum-exp is reduced by a group of lanes; then, for batches
+//    of MergeGeo::kBatch contributors, the per-(contributor, row) weights go to
+//    LDS and every thread accumulates its float4 chunks with all of a batch's
+//    loads independent of one another.
+//  * verify_merge_wide_kernel (otherwise): see below.
+template <int DL, int ROWS>
 struct MergeGeo {
+  static constexpr int kChunks = DL / 4;                   // float4 per row
+  static constexpr int kRows = ROWS;                       // rows per workgroup
+  static constexpr int kItems = kRows * kChunks / kMergeThreads;  // chunks per thread
+  // Contributors whose loads are in flight at once: about 32 float4 per thread.
+  static constexpr int kBatch = kItems >= 8 ? 4 : 32 / kItems > 16 ? 16 : 32 / kItems;
+  static constexpr int kLanesPerRow =                      // lanes of a row's LSE
+      kMergeThreads / kRows < kWave ? kMergeThreads / kRows : kWave;
+  static_assert(kRows * kChunks == kMergeThreads * kItems, "merge tiling");
+  static_assert(kRowsPerWG % kRows == 0 && kRows * kLanesPerRow <= kMergeThreads, "merge tiling");
+};
+
+template <int DL, int ROWS>
+__global__ __launch_bounds__(kMergeThreads) void verify_merge_kernel(
+    const int32_t* __restrict__ prefix_len, const int32_t* __restrict__ n_nodes, int B, int Q,
+    int H, int RT, int max_kv, int grid_attn, float* __restrict__ out, float* __restrict__ lse,
+    const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
+    const long long* __restrict__ ws_pref) {
+  using MG = MergeGeo<DL, ROWS>;
+  __shared__ int s_src[kMaxGrid];
+  __shared__ int s_cnt;
+  __shared__ float s_lse[MG::kRows];
+  __shared__ float s_w[MG::kBatch][MG::kRows];
+  const int tid = threadIdx.x;
+  const int u = blockIdx.x;
+  const int b = u / RT, rt = u % RT;
+  const ReqInfo ri = req_info(prefix_len, n_nodes, b, Q, H, max_kv, RT);
+  const long long QH = (long long)Q * H;
+  const int r0 = blockIdx.y * MG::kRows;                   // first row within the tile
+  if ((long long)rt * kRowsPerWG + r0 >= QH) return;
+  // Work prefix over requests, as the attention kernel computed it.
+  const long long Wtot = ws_pref[B];
+  const long long Gn = grid_attn;
+
+  const bool has_work = rt < ri.vt;
+  if (has_work) {
+    const long long S_u = ws_pref[b] + (long long)rt * ri.nkb;
+    const long long g_first = range_owner(S_u, Wtot, Gn);
+    const long long g_last = range_owner(S_u + ri.nkb - 1, Wtot, Gn);
+    if (g_first == g_last) return;  // written directly by the attention kernel
+    // Each contributing workgroup (non-empty range) wrote its partial for this
+    // tile into slot 2g when the tile holds the start of its range, else 2g+1.
+    if (tid < kWave) {
+      const int cnt = (int)(g_last - g_first + 1);
+      int base = 0;
+      for (int k0 = 0; k0 < cnt; k0 += kWave) {
+        const long long gg = g_first + k0 + tid;
+        int src = -1;
+        if (k0 + tid < cnt) {
+          const long long s0 = range_start(gg, Wtot, Gn);
+          const long long s1 = range_start(gg + 1, Wtot, Gn);
+          if (s0 != s1) src = (int)(2 * gg + (s0 >= S_u ? 0 : 1));
+        }
+        const uint64_t m = __ballot(src >= 0);
+        const int at = base + (int)__builtin_amdgcn_mbcnt_hi(
+                                  (unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+        if (src >= 0) s_src[at] = src;
+        base += __popcll(m);
+      }
+      if (tid == 0) s_cnt = base;
+    }
+  } else if (tid == 0) {
+    s_cnt = 0;
+  }
+  __syncthreads();
+  const int cnt = s_cnt;
+
+  // Row log-sum-exp: kLanesPerRow lanes per row, each over every
+  // kLanesPerRow-th contributor, then a butterfly over the group.
+  if (tid < MG::kRows * MG::kLanesPerRow) {
+    const int rl = tid / MG::kLanesPerRow, j = tid % MG::kLanesPerRow;
+    const int rr = r0 + rl;
+    const long long r_loc = (long long)rt * kRowsPerWG + rr;
+    const bool live = r_loc < QH && (int)(r_loc / H) < ri.nb;
+    float m = -INFINITY, z = 0.0f;
+    if (live) {
+      for (int k = j; k < cnt; k += MG::kLanesPerRow) {
+        const float v = ws_lse[(long long)s_src[k] * kRowsPerWG + rr];
+        if (v == -INFINITY) continue;
+        if (v > m) {
+          z = z * __expf(m - v) + 1.0f;
+          m = v;
+        } else {
+          z += __expf(v - m);
+        }
+      }
+    }
+#pragma unroll
+    for (int off = 1; off < MG::kLanesPerRow; off <<= 1) {
+      const float m2 = __shfl_xor(m, off), z2 = __shfl_xor(z, off);
+      const float mn = fmaxf(m, m2);
+      if (mn != -INFINITY) {
+        z = (m == -INFINITY ? 0.0f : z * __expf(m - mn)) +
+            (m2 == -INFINITY ? 0.0f : z2 * __expf(m2 - mn));
+        m = mn;
+      }
+    }
+    if (j == 0) s_lse[rl] = z > 0.0f ? m + __logf(z) : -INFINITY;
+  }
+  __syncthreads();
+
+  float4 acc[MG::kItems];
+  int rl_of[MG::kItems];
+#pragma unroll
+  for (int it = 0; it < MG::kItems; ++it) {
+    acc[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+    rl_of[it] = (tid + it * kMergeThreads) / MG::kChunks;
+  }
+  const int chunk = tid % MG::kChunks;
+  for (int k0 = 0; k0 < cnt; k0 += MG::kBatch) {
+    const int nk = cnt - k0 < MG::kBatch ? cnt - k0 : MG::kBatch;
+    for (int e = tid; e < MG::kBatch * MG::kRows; e += kMergeThreads) {
+      const int k = e / MG::kRows, rl = e % MG::kRows;
+      const float lt = s_lse[rl];
+      float w = 0.0f;
+      if (k < nk && lt != -INFINITY) {
+        const float v = ws_lse[(long long)s_src[k0 + k] * kRowsPerWG + r0 + rl];
+        if (v != -INFINITY) w = __expf(v - lt);
+      }
+      s_w[k][rl] = w;
+    }
+    __syncthreads();
+    // Rows that no contributor wrote (not live) read stale workspace here; their
+    // sums are discarded below, and every address stays inside the workspace.
+    // All loads of a batch (every item, every contributor) are issued before
+    // the first is used.
+    float4 v[MG::kItems][MG::kBatch];
+#pragma unroll
+    for (int it = 0; it < MG::kItems; ++it) {
+#pragma unroll
+      for (int k = 0; k < MG::kBatch; ++k) {
+        if (k < nk) {
+          const float* src =
+              ws_o + ((long long)s_src[k0 + k] * kRowsPerWG + r0 + rl_of[it]) * DL + chunk * 4;
+          v[it][k] = *reinterpret_cast<const float4*>(src);
+        }
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < MG::kItems; ++it) {
+#pragma unroll
+      for (int k = 0; k < MG::kBatch; ++k) {
+        if (k < nk) {
+          const float w = s_w[k][rl_of[it]];
+          acc[it].x = __builtin_fmaf(w, v[it][k].x, acc[it].x);
+          acc[it].y = __builtin_fmaf(w, v[it][k].y, acc[it].y);
+          acc[it].z = __builtin_fmaf(w, v[it][k].z, acc[it].z);
+          acc[it].w = __builtin_fmaf(w, v[it][k].w, acc[it].w);
+        }
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int it = 0; it < MG::kItems; ++it) {
+    const long long r_loc = (long long)rt * kRowsPerWG + r0 + rl_of[it];
+    if (r_loc >= QH) continue;
+    const long long grow = (long long)b * QH + r_loc;
+    const float lt = s_lse[rl_of[it]];
+    *reinterpret_cast<float4*>(out + grow * DL + chunk * 4) =
+        lt != -INFINITY ? acc[it] : make_float4(0.f, 0.f, 0.f, 0.f);
+    if (lse && chunk == 0) lse[grow] = lt;
+  }
+}
+
+// The merge for many row tiles: 8 rows of 512 (16 of 64) per workgroup, the
+// work prefix recomputed per workgroup, contributors' chunks accumulated four
+// at a time.
+template <int DL>
+struct MergeGeoW {
   static constexpr int kChunks = DL / 4;                          // float4 per row
   static constexpr int kItems = DL >= 256 ? 4 : 1;                // chunks per thread
   static constexpr int kRows = kMergeThreads * kItems / kChunks;  // rows per workgroup
@@ -973,20 +1156,20 @@ struct MergeGeo {
   static_assert(kRows * kChunks == kMergeThreads * kItems, "merge tiling");
   static_assert(kRowsPerWG % kRows == 0 && kLanesPerRow <= kWave, "merge tiling");
 };
-constexpr int kMergeBatch = 32;  // contributors whose weights are staged at once
+constexpr int kMergeBatchW = 32;  // contributors whose weights are staged at once
 
 template <int DL>
-__global__ __launch_bounds__(kMergeThreads) void verify_merge_kernel(
+__global__ __launch_bounds__(kMergeThreads) void verify_merge_wide_kernel(
     const int32_t* __restrict__ prefix_len, const int32_t* __restrict__ n_nodes, int B, int Q,
     int H, int RT, int max_kv, int grid_attn, float* __restrict__ out, float* __restrict__ lse,
     const float* __restrict__ ws_o, const float* __restrict__ ws_lse) {
-  using MG = MergeGeo<DL>;
+  using MG = MergeGeoW<DL>;
   __shared__ long long s_pref[kMaxBatch + 1];
   __shared__ long long s_wsum[kMergeThreads / kWave];
   __shared__ int s_src[kMaxGrid];
   __shared__ int s_cnt;
   __shared__ float s_lse[MG::kRows];
-  __shared__ float s_w[kMergeBatch][MG::kRows];
+  __shared__ float s_w[kMergeBatchW][MG::kRows];
   work_prefix<kMergeThreads>(s_pref, s_wsum, prefix_len, n_nodes, B, Q, H, max_kv, RT);
   const int tid = threadIdx.x;
   const int u = blockIdx.x;
@@ -1073,9 +1256,9 @@ __global__ __launch_bounds__(kMergeThreads) void verify_merge_kernel(
     rl_of[it] = (tid + it * kMergeThreads) / MG::kChunks;
   }
   const int chunk = tid % MG::kChunks;
-  for (int k0 = 0; k0 < cnt; k0 += kMergeBatch) {
-    const int nk = cnt - k0 < kMergeBatch ? cnt - k0 : kMergeBatch;
-    for (int e = tid; e < kMergeBatch * MG::kRows; e += kMergeThreads) {
+  for (int k0 = 0; k0 < cnt; k0 += kMergeBatchW) {
+    const int nk = cnt - k0 < kMergeBatchW ? cnt - k0 : kMergeBatchW;
+    for (int e = tid; e < kMergeBatchW * MG::kRows; e += kMergeThreads) {
       const int k = e / MG::kRows, rl = e % MG::kRows;
       const float lt = s_lse[rl];
       float w = 0.0f;
@@ -1123,17 +1306,27 @@ hipError_t launch_impl(const void* q_lat, const void* q_pe, const void* c_kv, co
                        void* workspace, const AttnPlan& plan, hipStream_t stream) {
   float* ws_o = static_cast<float*>(workspace);
   float* ws_lse = ws_o + (size_t)2 * plan.grid * kRowsPerWG * DL;
+  long long* ws_pref = reinterpret_cast<long long*>(ws_lse + (size_t)2 * plan.grid * kRowsPerWG);
   hipLaunchKernelGGL((verify_attn_kernel<T, DL, DR>), dim3(plan.grid), dim3(kThreads), 0,
                      stream, static_cast<const T*>(q_lat), static_cast<const T*>(q_pe),
                      static_cast<const T*>(c_kv), static_cast<const T*>(k_pe), num_slots,
                      req_to_slot, max_kv, prefix_len, n_nodes, vis, B, Q, H, plan.row_tiles,
-                     sm_scale, out, lse, ws_o, ws_lse);
+                     sm_scale, out, lse, ws_o, ws_lse, ws_pref);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((verify_merge_kernel<DL>), dim3(B * plan.row_tiles, kRowsPerWG / MergeGeo<DL>::kRows),
-                     dim3(kMergeThreads), 0,
-                     stream, prefix_len, n_nodes, B, Q, H, plan.row_tiles, max_kv, plan.grid,
-                     out, lse, ws_o, ws_lse);
+  // Thin merge workgroups (2 rows of 512) when there are so few row tiles that
+  // the wide merge would leave most CUs idle.
+  const int units = B * plan.row_tiles;
+  constexpr int kRn = MergeGeoW<DL>::kRows, kRs = DL >= 256 ? 2 : 16;
+  if (units * (kRowsPerWG / kRn) < plan.num_cu)
+    hipLaunchKernelGGL((verify_merge_kernel<DL, kRs>), dim3(units, kRowsPerWG / kRs),
+                       dim3(kMergeThreads), 0, stream, prefix_len, n_nodes, B, Q, H,
+                       plan.row_tiles, max_kv, plan.grid, out, lse, ws_o, ws_lse, ws_pref);
+  else
+    hipLaunchKernelGGL((verify_merge_wide_kernel<DL>),
+                       dim3(units, kRowsPerWG / MergeGeoW<DL>::kRows), dim3(kMergeThreads), 0,
+                       stream, prefix_len, n_nodes, B, Q, H, plan.row_tiles, max_kv, plan.grid,
+                       out, lse, ws_o, ws_lse);
   return hipGetLastError();
 }
 
@@ -1151,11 +1344,18 @@ AttnPlan plan_verify_attn(int B, int Q, int H, int max_kv, int d_lat, int num_cu
   if (g > kMaxGrid) g = kMaxGrid;
   const long long by_work = (work + kMinTilesPerWG - 1) / kMinTilesPerWG;
   if (by_work < g) g = by_work;
-  g = ((g + kXcds - 1) / kXcds) * kXcds;
-  if (g < kXcds) g = kXcds;
-  if (g > kMaxGrid) g = kMaxGrid;
+  if (g < 1) g = 1;
+  // When a multiple of the row-tile count comes within 10% of that, take it:
+  // with requests of equal length every workgroup's range then lies inside one
+  // row tile (one query load, one partial output, one merge contributor each).
+  const long long units = (long long)B * p.row_tiles;
+  if (units <= g && units * (g / units) * 10 >= g * 9) g = units * (g / units);
   p.grid = (int)g;
-  p.ws_bytes = (size_t)2 * p.grid * kRowsPerWG * ((size_t)d_lat + 1) * sizeof(float);
+  p.num_cu = num_cu > 0 ? num_cu : 256;
+  // Partial outputs and log-sum-exps (two slots per workgroup), then the work
+  // prefix over requests that the merge kernel reads.
+  p.ws_bytes = (size_t)2 * p.grid * kRowsPerWG * ((size_t)d_lat + 1) * sizeof(float) +
+               ((size_t)B + 1) * sizeof(long long);
   return p;
 }
 
