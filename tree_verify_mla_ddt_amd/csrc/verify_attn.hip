@@ -72,7 +72,7 @@ constexpr int kStages = 3;               // key-tile stages in LDS (tiles kb-1 .
 constexpr int kMergeThreads = 256;
 constexpr int kMaxGrid = 1024;           // upper bound of the attention grid
 #ifndef DDT_MIN_TILES
-#define DDT_MIN_TILES 6
+#define DDT_MIN_TILES 4
 #endif
 constexpr int kMinTilesPerWG = DDT_MIN_TILES;  // key tiles per workgroup before splitting further
 constexpr float kLog2e = 1.4426950408889634f;
