@@ -79,7 +79,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // A tile takes the residual pass when some key's probability exceeds this share
 // of its row's running sum (an upper bound on the key's final weight).
-constexpr float kHeavyShare = 1.0f / 64.0f;
+constexpr float kHeavyShare = 1.0f / 32.0f;
 // Reference-max slack of the online softmax, in log2 units.
 constexpr float kRescaleLog2 = 8.0f;
 
