@@ -160,12 +160,11 @@ struct ReqInfo {
   int vt;     // row tiles holding at least one live row
 };
 
-__device__ __forceinline__ ReqInfo req_info(const int32_t* prefix_len, const int32_t* n_nodes,
-                                            int b, int Q, int H, int max_kv, int RT) {
+// From the clamped prefix length and tree size.
+__device__ __forceinline__ ReqInfo req_info_ln(int L, int nb, int H, int RT) {
   ReqInfo r;
-  r.L = clampi(prefix_len[b], 0, max_kv);
-  const int cap = Q < max_kv - r.L ? Q : max_kv - r.L;
-  r.nb = clampi(n_nodes[b], 0, cap);
+  r.L = L;
+  r.nb = nb;
   r.nkb = (r.L + r.nb + kTileKeys - 1) / kTileKeys;
   const long long live_rows = (long long)r.nb * H;
   long long vt = (live_rows + kRowsPerWG - 1) / kRowsPerWG;
@@ -173,11 +172,20 @@ __device__ __forceinline__ ReqInfo req_info(const int32_t* prefix_len, const int
   return r;
 }
 
-// Exclusive prefix of work (key tiles) over requests into s_pref[0..B]; called
-// by all kBlock threads of a workgroup.
+__device__ __forceinline__ ReqInfo req_info(const int32_t* prefix_len, const int32_t* n_nodes,
+                                            int b, int Q, int H, int max_kv, int RT) {
+  const int L = clampi(prefix_len[b], 0, max_kv);
+  const int cap = Q < max_kv - L ? Q : max_kv - L;
+  return req_info_ln(L, clampi(n_nodes[b], 0, cap), H, RT);
+}
+
+// Exclusive prefix of work (key tiles) over requests into s_pref[0..B], and
+// (when s_req is given) each request's clamped prefix length and tree size
+// into s_req[0..B); called by all kBlock threads of a workgroup.
 template <int kBlock>
-__device__ void work_prefix(long long* s_pref, long long* s_wsum, const int32_t* prefix_len,
-                            const int32_t* n_nodes, int B, int Q, int H, int max_kv, int RT) {
+__device__ void work_prefix(long long* s_pref, long long* s_wsum, int2* s_req,
+                            const int32_t* prefix_len, const int32_t* n_nodes, int B, int Q, int H,
+                            int max_kv, int RT) {
   constexpr int kPer = (kMaxBatch + kBlock - 1) / kBlock;  // requests per thread
   const int t = threadIdx.x;
   long long w[kPer];
@@ -189,6 +197,7 @@ __device__ void work_prefix(long long* s_pref, long long* s_wsum, const int32_t*
     if (b < B) {
       const ReqInfo r = req_info(prefix_len, n_nodes, b, Q, H, max_kv, RT);
       w[k] = (long long)r.vt * r.nkb;
+      if (s_req) s_req[b] = make_int2(r.L, r.nb);
     }
     mine += w[k];
   }
@@ -240,12 +249,20 @@ struct Smem {
   uint32_t xheavy[kWaves];          // residuals posted with the latest probabilities
   uint64_t visrow[kRowsPerWG][2];   // visibility bitset of each row's tree node
   long long pref[kMaxBatch + 1];
+  int2 req[kMaxBatch];  // per request: clamped prefix length, tree size
   long long wsum[kWaves];
 };
 
 // Raw pool slot id of key `j` of the request (-1 past the request); its range
 // is checked when it is published, so the load's latency is not waited for
 // where it is issued.
+// 16-byte store that does not stay in the cache hierarchy on its way out.
+__device__ __forceinline__ void store_nt(float* d, float4 v) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  const f4 x = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(x, reinterpret_cast<f4*>(d));
+}
+
 __device__ __forceinline__ int32_t fetch_slot(const int32_t* __restrict__ slots_b, int j,
                                               int nkeys) {
   return j < nkeys ? slots_b[j] : -1;
@@ -515,7 +532,11 @@ __device__ __forceinline__ void run_unit(Smem<T, DL, DR>& sm, const Args& a, con
   const int tid = threadIdx.x;
   const int wave = uni(tid >> 6);  // wave-uniform: keep it (and what derives from it) scalar
   const int mate = wave ^ 1;
-  const int lane = tid & 63;
+  // An opaque copy of the lane id: nothing lane-derived is hoisted out of the
+  // unit loop (values held across it would not fit the register budget).
+  int lane = tid;
+  __asm__ __volatile__("" : "+v"(lane));
+  lane &= 63;
   const int rb = wave / kSplit;
   const int n = lane & 31;
   const int g = lane >> 5;
@@ -527,43 +548,35 @@ __device__ __forceinline__ void run_unit(Smem<T, DL, DR>& sm, const Args& a, con
   const T* k_pe = static_cast<const T*>(a.k_pe);
   const int32_t* slots_b = a.req_to_slot + (long long)u.b * a.max_kv;
 
+  // Slot ids of the first two tiles are requested before anything else: the
+  // first tile's loads depend on them, the query and visibility rows do not.
+  int32_t raw0 = -1, raw1 = -1;
+  if (tid < kTileKeys) {
+    raw0 = fetch_slot(slots_b, u.kb0 * kTileKeys + tid, u.nkeys);
+    if (u.kb0 + 1 < u.kb1) raw1 = fetch_slot(slots_b, (u.kb0 + 1) * kTileKeys + tid, u.nkeys);
+  }
+
   // This lane's row.
   const long long r_loc = (long long)u.rt * kRowsPerWG + rb * 32 + n;  // row in request
-  const int node = (int)(r_loc / a.H);
+  int heads = a.H;  // opaque: the division's reciprocal is formed per unit, not held
+  __asm__ __volatile__("" : "+s"(heads));
+  const int node = (int)(r_loc / heads);
   const bool row_exists = r_loc < QH;
   const bool row_live = row_exists && node < u.ri.nb;
   const bool wave_live = __ballot(row_live) != 0;  // the same in both waves of the pair
   const long long grow = (long long)u.b * QH + r_loc;
 
+  // Visibility row of this lane's node.
+  uint64_t vis0 = 0, vis1 = 0;
+  if (HALF == 0 && g == 0 && row_live) {
+    const uint64_t* vr = a.vis + ((long long)u.b * a.Q + node) * W;
+    vis0 = vr[0];
+    if (W > 1) vis1 = vr[1];
+  }
+
   // Query operand: B slots of this lane's row for contraction steps of HALF.
   using QV = typename std::conditional<G::kBF16, bf16x8_t, float>::type;
   QV q[kStep1 - kStep0];
-#pragma unroll
-  for (int kk = 0; kk < kStep1 - kStep0; ++kk) {
-    const int d = (kStep0 + kk) * G::kKStep + g * (G::kBF16 ? 8 : 1);
-    if constexpr (G::kBF16) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (row_live)
-        v = d < DL ? *reinterpret_cast<const uint4*>(q_lat + grow * DL + d)
-                   : *reinterpret_cast<const uint4*>(q_pe + grow * DR + (d - DL));
-      q[kk] = __builtin_bit_cast(bf16x8_t, v);
-    } else {
-      float v = 0.0f;
-      if (row_live) v = d < DL ? q_lat[grow * DL + d] : q_pe[grow * DR + (d - DL)];
-      q[kk] = v;
-    }
-  }
-  if (HALF == 0 && g == 0) {
-    uint64_t v0 = 0, v1 = 0;
-    if (row_live) {
-      const uint64_t* vr = a.vis + ((long long)u.b * a.Q + node) * W;
-      v0 = vr[0];
-      if (W > 1) v1 = vr[1];
-    }
-    sm.visrow[rb * 32 + n][0] = v0;
-    sm.visrow[rb * 32 + n][1] = v1;
-  }
-
   f32x16_t o[G::kNCBh];
 #pragma unroll
   for (int cb = 0; cb < G::kNCBh; ++cb) o[cb] = f32x16_t{};
@@ -571,20 +584,86 @@ __device__ __forceinline__ void run_unit(Smem<T, DL, DR>& sm, const Args& a, con
   // pair; l_run: this lane's share of the row sum (own keys, its 8 of them).
   float m_run = -INFINITY, l_run = 0.0f;
 
-  // Prologue: slot ids of the first two tiles, then the first tile.
+  // Prologue: publish the slot ids and visibility rows, then issue the first
+  // tile's loads and after them the query loads (both land together).
   if (tid < kTileKeys) {
-    publish_slots(sm.slot[u.kb0 % kRing], &sm.valid[u.kb0 % kRing],
-                  fetch_slot(slots_b, u.kb0 * kTileKeys + tid, u.nkeys), a.num_slots, tid);
+    publish_slots(sm.slot[u.kb0 % kRing], &sm.valid[u.kb0 % kRing], raw0, a.num_slots, tid);
     if (u.kb0 + 1 < u.kb1)
-      publish_slots(sm.slot[(u.kb0 + 1) % kRing], &sm.valid[(u.kb0 + 1) % kRing],
-                    fetch_slot(slots_b, (u.kb0 + 1) * kTileKeys + tid, u.nkeys), a.num_slots,
-                    tid);
+      publish_slots(sm.slot[(u.kb0 + 1) % kRing], &sm.valid[(u.kb0 + 1) % kRing], raw1,
+                    a.num_slots, tid);
+  }
+  if (HALF == 0 && g == 0) {
+    sm.visrow[rb * 32 + n][0] = vis0;
+    sm.visrow[rb * 32 + n][1] = vis1;
   }
   __syncthreads();
   issue_tile<T, DL, DR>(sm.stage[u.kb0 % kStages], sm.slot[u.kb0 % kRing], c_kv, k_pe, wave,
                         lane);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+#ifndef DDT_QSTAGE
+#define DDT_QSTAGE 1
+#endif
+  if constexpr (DDT_QSTAGE && G::kBF16 && DL == 512 && DR == 64) {
+    // The query tile goes through LDS in two passes of 128 rows x 288 dims (the
+    // share of one wave of each pair), parked in the two stages the first key
+    // tile does not use: every load instruction then reads 1 KiB of
+    // consecutive bytes instead of 32-byte pieces of 32 rows.
+    constexpr int kQC = 36;                                     // 16-byte chunks per row and pass
+    constexpr int kQPerWave = kRowsPerWG * kQC / kWave / kWaves;  // instructions per wave
+    constexpr int kQStageChunks = kRowsPerWG / 2 * kQC;          // 64 rows per stage
+    static_assert(kQStageChunks * 16 <= G::kStageBytes && kQStageChunks % kWave == 0 &&
+                      kQPerWave * kWave * kWaves == kRowsPerWG * kQC && kStep1 - kStep0 == kQC / 2,
+                  "query staging");
+    unsigned char* qst[2] = {sm.stage[(u.kb0 + 1) % kStages], sm.stage[(u.kb0 + 2) % kStages]};
+    const long long row0 = (long long)u.b * QH + (long long)u.rt * kRowsPerWG;
+    const long long rlast = (long long)u.b * QH + QH - 1;  // rows past it are clamped, unused
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+      for (int i = 0; i < kQPerWave; ++i) {
+        const int c0 = (wave * kQPerWave + i) * kWave;  // first chunk of this instruction
+        const int c = c0 + lane;
+        const int r = c / kQC, j = c - r * kQC;
+        long long gr = row0 + r;
+        gr = gr < rlast ? gr : rlast;
+        // Chunk j of pass p holds dims 288 p + 8 j .. +8 (latent, then rope).
+        const T* src = pass == 0 ? q_lat + gr * DL + 8 * j
+                       : j < 28  ? q_lat + gr * DL + 288 + 8 * j
+                                 : q_pe + gr * DR + 8 * (j - 28);
+        const int h = c0 >= kQStageChunks ? 1 : 0;
+        dma16(static_cast<const void*>(src), lds_addr(qst[h] + 16 * (c0 - h * kQStageChunks)));
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (HALF == pass) {
+        const int row = rb * 32 + n;  // (LDS address space kept explicit: no flat loads)
+        const uint32_t qrow = lds_addr(qst[row >> 6]) + (row & 63) * (kQC * 16);
+#pragma unroll
+        for (int kk = 0; kk < kStep1 - kStep0; ++kk) {
+          q[kk] = bf16x8_t{};
+          if (row_live) q[kk] = *(const DDT_LDS bf16x8_t*)(uintptr_t)(qrow + 16 * (2 * kk + g));
+        }
+      }
+      __syncthreads();  // the stages are reused by the next pass and the loop
+    }
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < kStep1 - kStep0; ++kk) {
+      const int d = (kStep0 + kk) * G::kKStep + g * (G::kBF16 ? 8 : 1);
+      if constexpr (G::kBF16) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (row_live)
+          v = d < DL ? *reinterpret_cast<const uint4*>(q_lat + grow * DL + d)
+                     : *reinterpret_cast<const uint4*>(q_pe + grow * DR + (d - DL));
+        q[kk] = __builtin_bit_cast(bf16x8_t, v);
+      } else {
+        float v = 0.0f;
+        if (row_live) v = d < DL ? q_lat[grow * DL + d] : q_pe[grow * DR + (d - DL)];
+        q[kk] = v;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
 
   // State carried between the phases of one tile: the partial scores (QK ->
   // softmax) and the value-product operands (softmax -> PV).
@@ -877,7 +956,52 @@ __device__ __forceinline__ void run_unit(Smem<T, DL, DR>& sm, const Args& a, con
     dst = a.ws_o + rr * DL;
     dst_lse = a.ws_lse + rr;
   }
-  if (dst) {
+#ifndef DDT_EPI
+#define DDT_EPI 2
+#endif
+  if constexpr (DDT_EPI >= 2 && G::kNCBh % 2 == 0) {
+    // Rows go out through LDS (the key stages are free now): each pass parks 64
+    // of this wave's columns of its 32 rows, then every store instruction
+    // writes four 256-byte row segments instead of 32-byte pieces of 32 rows.
+    constexpr int kPCb = 2, kPCols = 32 * kPCb, kPitch = kPCols + 4;  // floats
+    static_assert(kWaves * 32 * kPitch * 4 <= kStages * G::kStageBytes, "epilogue staging");
+    float* buf = reinterpret_cast<float*>(sm.stage[0]) + wave * (32 * kPitch);
+    const uint32_t live_m = (uint32_t)__ballot(row_live);  // bit r: row r of this wave
+    const uint32_t exist_m = (uint32_t)__ballot(row_exists);
+    const uint32_t write_m = u.complete ? exist_m : live_m;
+    float* base = u.complete
+                      ? a.out + ((long long)u.b * QH + (long long)u.rt * kRowsPerWG + rb * 32) * DL
+                      : a.ws_o + ((long long)u.slot * kRowsPerWG + rb * 32) * DL;
+    const int c4 = lane & 15;
+#pragma unroll
+    for (int pass = 0; pass < G::kNCBh / kPCb; ++pass) {
+#pragma unroll
+      for (int c = 0; c < kPCb; ++c) {
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) {
+          const int cb = pass * kPCb + c;
+          float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (row_live)
+            v = make_float4(o[cb][4 * t4] * inv, o[cb][4 * t4 + 1] * inv,
+                            o[cb][4 * t4 + 2] * inv, o[cb][4 * t4 + 3] * inv);
+          *reinterpret_cast<float4*>(buf + n * kPitch + c * 32 + 8 * t4 + 4 * g) = v;
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's parked rows are in LDS
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 4 * i + (lane >> 4);
+        const float4 v = *reinterpret_cast<const float4*>(buf + r * kPitch + 4 * c4);
+        float* d = base + (long long)r * DL + (kCb0 + pass * kPCb) * 32 + 4 * c4;
+        if ((write_m >> r) & 1u) {
+          if constexpr (DDT_EPI == 3) store_nt(d, v);
+          else *reinterpret_cast<float4*>(d) = v;
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next pass overwrites
+    }
+    if (dst_lse && g == 0 && HALF == 0) *dst_lse = row_live ? lse_v : -INFINITY;
+  } else if (dst) {
 #pragma unroll
     for (int cb = 0; cb < G::kNCBh; ++cb) {
 #pragma unroll
@@ -886,7 +1010,9 @@ __device__ __forceinline__ void run_unit(Smem<T, DL, DR>& sm, const Args& a, con
         if (row_live)
           v = make_float4(o[cb][4 * t4] * inv, o[cb][4 * t4 + 1] * inv,
                           o[cb][4 * t4 + 2] * inv, o[cb][4 * t4 + 3] * inv);
-        *reinterpret_cast<float4*>(dst + (kCb0 + cb) * 32 + 8 * t4 + 4 * g) = v;
+        float* d = dst + (kCb0 + cb) * 32 + 8 * t4 + 4 * g;
+        if constexpr (DDT_EPI == 1) store_nt(d, v);
+        else *reinterpret_cast<float4*>(d) = v;
       }
     }
     if (dst_lse && g == 0 && HALF == 0) *dst_lse = row_live ? lse_v : -INFINITY;
@@ -908,7 +1034,7 @@ __global__ __launch_bounds__(kThreads) void verify_attn_kernel(
 
   if ((threadIdx.x & 63) == 0) sm.xflag[threadIdx.x >> 6] = 0;
   int seq = 0;  // this wave's pair-sync sequence (see pair_post)
-  work_prefix<kThreads>(sm.pref, sm.wsum, prefix_len, n_nodes, B, Q, H, max_kv, RT);
+  work_prefix<kThreads>(sm.pref, sm.wsum, sm.req, prefix_len, n_nodes, B, Q, H, max_kv, RT);
   const long long Wtot = uni(sm.pref[B]);
   if (blockIdx.x == 0)  // for the merge kernel
     for (int i = threadIdx.x; i <= B; i += kThreads) ws_pref[i] = sm.pref[i];
@@ -948,7 +1074,10 @@ __global__ __launch_bounds__(kThreads) void verify_attn_kernel(
     const bool head = pos == start;
     Unit u;
     u.b = b;
-    u.ri = req_info(prefix_len, n_nodes, b, Q, H, max_kv, RT);
+    {
+      const int2 ln = sm.req[b];
+      u.ri = req_info_ln(uni(ln.x), uni(ln.y), H, RT);
+    }
     const long long off = pos - uni(sm.pref[b]);
     u.rt = (int)(off / u.ri.nkb);
     u.kb0 = (int)(off % u.ri.nkb);
@@ -1001,6 +1130,7 @@ __global__ __launch_bounds__(kMergeThreads) void verify_merge_kernel(
   __shared__ int s_src[kMaxGrid];
   __shared__ int s_cnt;
   __shared__ float s_lse[MG::kRows];
+  __shared__ float s_lv[MG::kBatch][MG::kRows];  // LSEs of the first batch's contributors
   __shared__ float s_w[MG::kBatch][MG::kRows];
   const int tid = threadIdx.x;
   const int u = blockIdx.x;
@@ -1046,6 +1176,36 @@ __global__ __launch_bounds__(kMergeThreads) void verify_merge_kernel(
   __syncthreads();
   const int cnt = s_cnt;
 
+  // The first batch's partial rows are requested before the log-sum-exps are
+  // combined: they do not depend on them.
+  float4 acc[MG::kItems];
+  int rl_of[MG::kItems];
+#pragma unroll
+  for (int it = 0; it < MG::kItems; ++it) {
+    acc[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+    rl_of[it] = (tid + it * kMergeThreads) / MG::kChunks;
+  }
+  const int chunk = tid % MG::kChunks;
+  // Rows that no contributor wrote (not live) read stale workspace here; their
+  // sums are discarded below, and every address stays inside the workspace.
+  // All loads of a batch (every item, every contributor) are issued before
+  // the first is used.
+  float4 v[MG::kItems][MG::kBatch];
+  auto load_batch = [&](int k0, int nk) __attribute__((always_inline)) {
+#pragma unroll
+    for (int it = 0; it < MG::kItems; ++it) {
+#pragma unroll
+      for (int k = 0; k < MG::kBatch; ++k) {
+        if (k < nk) {
+          const float* src =
+              ws_o + ((long long)s_src[k0 + k] * kRowsPerWG + r0 + rl_of[it]) * DL + chunk * 4;
+          v[it][k] = *reinterpret_cast<const float4*>(src);
+        }
+      }
+    }
+  };
+  load_batch(0, cnt < MG::kBatch ? cnt : MG::kBatch);
+
   // Row log-sum-exp: kLanesPerRow lanes per row, each over every
   // kLanesPerRow-th contributor, then a butterfly over the group.
   if (tid < MG::kRows * MG::kLanesPerRow) {
@@ -1056,13 +1216,14 @@ __global__ __launch_bounds__(kMergeThreads) void verify_merge_kernel(
     float m = -INFINITY, z = 0.0f;
     if (live) {
       for (int k = j; k < cnt; k += MG::kLanesPerRow) {
-        const float v = ws_lse[(long long)s_src[k] * kRowsPerWG + rr];
-        if (v == -INFINITY) continue;
-        if (v > m) {
-          z = z * __expf(m - v) + 1.0f;
-          m = v;
+        const float x = ws_lse[(long long)s_src[k] * kRowsPerWG + rr];
+        if (k < MG::kBatch) s_lv[k][rl] = x;
+        if (x == -INFINITY) continue;
+        if (x > m) {
+          z = z * __expf(m - x) + 1.0f;
+          m = x;
         } else {
-          z += __expf(v - m);
+          z += __expf(x - m);
         }
       }
     }
@@ -1080,43 +1241,21 @@ __global__ __launch_bounds__(kMergeThreads) void verify_merge_kernel(
   }
   __syncthreads();
 
-  float4 acc[MG::kItems];
-  int rl_of[MG::kItems];
-#pragma unroll
-  for (int it = 0; it < MG::kItems; ++it) {
-    acc[it] = make_float4(0.f, 0.f, 0.f, 0.f);
-    rl_of[it] = (tid + it * kMergeThreads) / MG::kChunks;
-  }
-  const int chunk = tid % MG::kChunks;
   for (int k0 = 0; k0 < cnt; k0 += MG::kBatch) {
     const int nk = cnt - k0 < MG::kBatch ? cnt - k0 : MG::kBatch;
+    if (k0 > 0) load_batch(k0, nk);
     for (int e = tid; e < MG::kBatch * MG::kRows; e += kMergeThreads) {
       const int k = e / MG::kRows, rl = e % MG::kRows;
       const float lt = s_lse[rl];
       float w = 0.0f;
       if (k < nk && lt != -INFINITY) {
-        const float v = ws_lse[(long long)s_src[k0 + k] * kRowsPerWG + r0 + rl];
-        if (v != -INFINITY) w = __expf(v - lt);
+        const float x = k0 == 0 ? s_lv[k][rl]
+                                : ws_lse[(long long)s_src[k0 + k] * kRowsPerWG + r0 + rl];
+        if (x != -INFINITY) w = __expf(x - lt);
       }
       s_w[k][rl] = w;
     }
     __syncthreads();
-    // Rows that no contributor wrote (not live) read stale workspace here; their
-    // sums are discarded below, and every address stays inside the workspace.
-    // All loads of a batch (every item, every contributor) are issued before
-    // the first is used.
-    float4 v[MG::kItems][MG::kBatch];
-#pragma unroll
-    for (int it = 0; it < MG::kItems; ++it) {
-#pragma unroll
-      for (int k = 0; k < MG::kBatch; ++k) {
-        if (k < nk) {
-          const float* src =
-              ws_o + ((long long)s_src[k0 + k] * kRowsPerWG + r0 + rl_of[it]) * DL + chunk * 4;
-          v[it][k] = *reinterpret_cast<const float4*>(src);
-        }
-      }
-    }
 #pragma unroll
     for (int it = 0; it < MG::kItems; ++it) {
 #pragma unroll
@@ -1170,7 +1309,7 @@ __global__ __launch_bounds__(kMergeThreads) void verify_merge_wide_kernel(
   __shared__ int s_cnt;
   __shared__ float s_lse[MG::kRows];
   __shared__ float s_w[kMergeBatchW][MG::kRows];
-  work_prefix<kMergeThreads>(s_pref, s_wsum, prefix_len, n_nodes, B, Q, H, max_kv, RT);
+  work_prefix<kMergeThreads>(s_pref, s_wsum, nullptr, prefix_len, n_nodes, B, Q, H, max_kv, RT);
   const int tid = threadIdx.x;
   const int u = blockIdx.x;
   const int b = u / RT, rt = u % RT;
