@@ -256,13 +256,6 @@ struct Smem {
 // Raw pool slot id of key `j` of the request (-1 past the request); its range
 // is checked when it is published, so the load's latency is not waited for
 // where it is issued.
-// 16-byte store that does not stay in the cache hierarchy on its way out.
-__device__ __forceinline__ void store_nt(float* d, float4 v) {
-  typedef float f4 __attribute__((ext_vector_type(4)));
-  const f4 x = {v.x, v.y, v.z, v.w};
-  __builtin_nontemporal_store(x, reinterpret_cast<f4*>(d));
-}
-
 __device__ __forceinline__ int32_t fetch_slot(const int32_t* __restrict__ slots_b, int j,
                                               int nkeys) {
   return j < nkeys ? slots_b[j] : -1;
@@ -440,13 +433,6 @@ __device__ __forceinline__ uint32_t tree_window(uint64_t v0, uint64_t v1, int jb
   return (uint32_t)(v1 >> (jb - 64));
 }
 
-// Workgroup barrier that orders LDS traffic only: it does not wait for the
-// direct global->LDS tile loads still in flight (a __syncthreads() fence would).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads/writes are done
-  __asm__ __volatile__("s_barrier" ::: "memory");
-}
-
 // Everything one workgroup needs to process one row tile over a key range.
 struct Unit {
   int b, rt, kb0, kb1, nkeys;
@@ -599,10 +585,7 @@ __device__ __forceinline__ void run_unit(Smem<T, DL, DR>& sm, const Args& a, con
   __syncthreads();
   issue_tile<T, DL, DR>(sm.stage[u.kb0 % kStages], sm.slot[u.kb0 % kRing], c_kv, k_pe, wave,
                         lane);
-#ifndef DDT_QSTAGE
-#define DDT_QSTAGE 1
-#endif
-  if constexpr (DDT_QSTAGE && G::kBF16 && DL == 512 && DR == 64) {
+  if constexpr (G::kBF16 && DL == 512 && DR == 64) {
     // The query tile goes through LDS in two passes of 128 rows x 288 dims (the
     // share of one wave of each pair), parked in the two stages the first key
     // tile does not use: every load instruction then reads 1 KiB of
@@ -956,10 +939,7 @@ __device__ __forceinline__ void run_unit(Smem<T, DL, DR>& sm, const Args& a, con
     dst = a.ws_o + rr * DL;
     dst_lse = a.ws_lse + rr;
   }
-#ifndef DDT_EPI
-#define DDT_EPI 2
-#endif
-  if constexpr (DDT_EPI >= 2 && G::kNCBh % 2 == 0) {
+  if constexpr (G::kNCBh % 2 == 0) {
     // Rows go out through LDS (the key stages are free now): each pass parks 64
     // of this wave's columns of its 32 rows, then every store instruction
     // writes four 256-byte row segments instead of 32-byte pieces of 32 rows.
@@ -993,10 +973,7 @@ __device__ __forceinline__ void run_unit(Smem<T, DL, DR>& sm, const Args& a, con
         const int r = 4 * i + (lane >> 4);
         const float4 v = *reinterpret_cast<const float4*>(buf + r * kPitch + 4 * c4);
         float* d = base + (long long)r * DL + (kCb0 + pass * kPCb) * 32 + 4 * c4;
-        if ((write_m >> r) & 1u) {
-          if constexpr (DDT_EPI == 3) store_nt(d, v);
-          else *reinterpret_cast<float4*>(d) = v;
-        }
+        if ((write_m >> r) & 1u) *reinterpret_cast<float4*>(d) = v;
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next pass overwrites
     }
@@ -1010,9 +987,7 @@ __device__ __forceinline__ void run_unit(Smem<T, DL, DR>& sm, const Args& a, con
         if (row_live)
           v = make_float4(o[cb][4 * t4] * inv, o[cb][4 * t4 + 1] * inv,
                           o[cb][4 * t4 + 2] * inv, o[cb][4 * t4 + 3] * inv);
-        float* d = dst + (kCb0 + cb) * 32 + 8 * t4 + 4 * g;
-        if constexpr (DDT_EPI == 1) store_nt(d, v);
-        else *reinterpret_cast<float4*>(d) = v;
+        *reinterpret_cast<float4*>(dst + (kCb0 + cb) * 32 + 8 * t4 + 4 * g) = v;
       }
     }
     if (dst_lse && g == 0 && HALF == 0) *dst_lse = row_live ? lse_v : -INFINITY;
