@@ -72,7 +72,7 @@ constexpr int kStages = 3;               // key-tile stages in LDS (tiles kb-1 .
 constexpr int kMergeThreads = 256;
 constexpr int kMaxGrid = 1024;           // upper bound of the attention grid
 #ifndef DDT_MIN_TILES
-#define DDT_MIN_TILES 4
+#define DDT_MIN_TILES 3
 #endif
 constexpr int kMinTilesPerWG = DDT_MIN_TILES;  // key tiles per workgroup before splitting further
 constexpr float kLog2e = 1.4426950408889634f;
@@ -1454,16 +1454,25 @@ AttnPlan plan_verify_attn(int B, int Q, int H, int max_kv, int d_lat, int num_cu
   const long long work = (long long)B * p.row_tiles * nkb;
   // One resident workgroup per CU (register-bound), but at least kMinTilesPerWG
   // key tiles each so that query loads and partial outputs stay a small share.
-  long long g = num_cu > 0 ? num_cu : 256;
-  if (g > kMaxGrid) g = kMaxGrid;
-  const long long by_work = (work + kMinTilesPerWG - 1) / kMinTilesPerWG;
-  if (by_work < g) g = by_work;
-  if (g < 1) g = 1;
-  // When a multiple of the row-tile count comes within 10% of that, take it:
-  // with requests of equal length every workgroup's range then lies inside one
-  // row tile (one query load, one partial output, one merge contributor each).
+  long long cap = num_cu > 0 ? num_cu : 256;
+  if (cap > kMaxGrid) cap = kMaxGrid;
   const long long units = (long long)B * p.row_tiles;
-  if (units <= g && units * (g / units) * 10 >= g * 9) g = units * (g / units);
+  const long long per_unit = (nkb + kMinTilesPerWG - 1) / kMinTilesPerWG;
+  long long g;
+  if (units * per_unit <= cap) {
+    // Few row tiles: cut each into ranges of at most kMinTilesPerWG tiles, so
+    // that every workgroup's range lies inside one row tile (one query load,
+    // one partial output) and none is longer than that.
+    g = units * per_unit;
+  } else {
+    g = cap;
+    const long long by_work = (work + kMinTilesPerWG - 1) / kMinTilesPerWG;
+    if (by_work < g) g = by_work;
+    // When a multiple of the row-tile count comes within 10% of that, take it
+    // (requests of equal length then give ranges inside one row tile).
+    if (units <= g && units * (g / units) * 10 >= g * 9) g = units * (g / units);
+  }
+  if (g < 1) g = 1;
   p.grid = (int)g;
   p.num_cu = num_cu > 0 ? num_cu : 256;
   // Partial outputs and log-sum-exps (two slots per workgroup), then the work
