@@ -256,7 +256,7 @@ def cpu_baseline(name, wl, host_tree, tgt_host, budget_s=12.0):
     q_lat, q_pe, c_kv, k_pe = f(wl.q_lat), f(wl.q_pe), f(wl.c_kv), f(wl.k_pe)
     reps, t_total = 0, 0.0
     t_build = t_attn = t_acc = 0.0
-    while t_total < budget_s and reps < 50:
+    while t_total < budget_s and reps < 1000:
         t0 = time.perf_counter()
         t = oracle.tree_build(wl.topk_logp, wl.topk_ids, wl.root_token, wl.prefix_len, wl.budget)
         t1 = time.perf_counter()
