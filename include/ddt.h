@@ -2,17 +2,20 @@
  * ddt.h -- C ABI of libddt.so, the MI355X (gfx950) DDTree tree-verify step.
  *
  * One verify step of DDTree speculative decoding runs as three device stages on
- * one HIP stream with no host round-trip between them:
+ * one HIP stream with no host round-trip between them, and a fourth commits
+ * the accepted path to the KV cache:
  *
  *   ddt_tree_build   drafter per-depth top-K log-probs -> draft tree
  *   ddt_verify_attn  every tree node of every request attends, in absorbed MLA
  *                    form, over its committed latent prefix and its ancestors
  *   ddt_tree_accept  greedy walk of the verified tree -> accepted tokens
+ *   ddt_kv_commit    accepted path -> committed prefix slots (slot table rewrite)
  *
  * The operations are the ones described on the pages
  *   [P1] "The Architecture of a Thousand-Parameter Decision: Designing a Native
  *        DDTree Inference Engine for Kimi K2.6", section "What to Build New"
- *        (item 2, tree-verify MLA attention; item 3, GPU tree builder);
+ *        (item 2, tree-verify MLA attention; item 3, GPU tree builder; item 5,
+ *        the paged latent KV cache and the append step);
  *   [P2] "The Architecture of Closure: How a Summary Message Encodes an Entire
  *        Engineering Session", section "The Table as a Decision Artifact"
  *        (tree_build, verify_attn, tree_accept and their chaining on device);
@@ -173,6 +176,38 @@ int ddt_tree_accept(const int32_t* node_token, const int32_t* parent,
                     const int32_t* n_nodes, const int32_t* target_argmax,
                     int B, int Q, int32_t* accept_len, int32_t* accept_nodes,
                     int32_t* out_tokens, int32_t* next_root, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * ddt_kv_commit -- append the accepted path to the committed prefix ([P1]
+ * "What to Build New", item 5: the paged MLA-latent KV cache and the "append"
+ * step closing draft -> build -> verify -> accept; [P3] "Architectural
+ * Abstraction": tree entries sit at positions L + depth).  With one token per
+ * page this is a rewrite of the request's slot table.
+ *
+ * In/out (device): req_to_slot [B][max_kv] i32 (as for ddt_verify_attn: entries
+ *   [L_b, L_b + n_b) are the tree nodes in node-index order), prefix_len [B] i32.
+ * Inputs (device): n_nodes [B] i32 (ddt_tree_build), accept_len [B] and
+ *   accept_nodes [B][Q] i32 (ddt_tree_accept: the root-first accepted path).
+ * Scalars: 1 <= B, 1 <= Q <= DDT_MAX_Q, max_kv >= 1.
+ * Outputs (device): freed_slots [B][Q] i32 -- the slot-table values of the tree
+ *   entries not committed, in increasing node index, -1 padded; n_freed [B] i32.
+ *
+ * Semantics, per request b, with L = prefix_len[b] clamped to [0, max_kv],
+ * n = n_nodes[b] clamped to [0, min(Q, max_kv - L)]: the path is
+ * accept_nodes[b][0 .. a) for a = accept_len[b] clamped to [0, n], cut before
+ * the first entry that is outside [0, n) or not larger than the one before it
+ * (node indices increase along any root path).  Entry L + j (j < a) becomes
+ * the slot of tree node path[j] (its value in req_to_slot before the call);
+ * entries L + a .. L + n - 1 become -1; prefix_len[b] = L + a; the other
+ * tree nodes' slots go to freed_slots.  Entries outside [L, L + n) are not
+ * touched.  Node path[j] has depth j, so its KV, written at position L + j
+ * during the verify step, is already where the committed prefix expects it.
+ * Bit-exact deterministic.  One 64-lane wavefront per request.
+ * ------------------------------------------------------------------------- */
+int ddt_kv_commit(int32_t* req_to_slot, int max_kv, int32_t* prefix_len,
+                  const int32_t* n_nodes, const int32_t* accept_len,
+                  const int32_t* accept_nodes, int B, int Q, int32_t* freed_slots,
+                  int32_t* n_freed, void* stream);
 
 #ifdef __cplusplus
 }

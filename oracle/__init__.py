@@ -46,9 +46,11 @@ def _load():
         lib.ddt_oracle_verify_attn_rows.argtypes = (
             [p, p, p, p, i64, p, i32, p, p, p, i32, i32, i32, i32, i32, f32, i64, p, p, p])
         lib.ddt_oracle_tree_accept.argtypes = [p, p, p, p, i32, i32, p, p, p, p]
+        lib.ddt_oracle_kv_commit.argtypes = [p, i32, p, p, p, p, i32, i32, p, p]
         lib.ddt_oracle_num_threads.argtypes = []
         for f in (lib.ddt_oracle_tree_build, lib.ddt_oracle_verify_attn_rows,
-                  lib.ddt_oracle_tree_accept, lib.ddt_oracle_num_threads):
+                  lib.ddt_oracle_tree_accept, lib.ddt_oracle_kv_commit,
+                  lib.ddt_oracle_num_threads):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -148,4 +150,26 @@ def tree_accept(node_token, parent, n_nodes, target_argmax) -> dict:
                                     ptr["out_tokens"], ptr["next_root"])
     if rc != 0:
         raise ValueError("oracle tree_accept rejected its arguments")
+    return out
+
+
+def kv_commit(req_to_slot, prefix_len, n_nodes, accept_len, accept_nodes) -> dict:
+    """Append the accepted path to the committed prefix.  Returns new copies of
+    req_to_slot and prefix_len and the released slots (inputs untouched)."""
+    lib = _load()
+    r2s = np.array(req_to_slot, dtype=np.int32, order="C", copy=True)
+    plen = np.array(prefix_len, dtype=np.int32, order="C", copy=True)
+    nn, p_nn = _c(n_nodes, np.int32)
+    al, p_al = _c(accept_len, np.int32)
+    an, p_an = _c(accept_nodes, np.int32)
+    B, max_kv = r2s.shape
+    Q = an.shape[1]
+    out = {"req_to_slot": r2s, "prefix_len": plen,
+           "freed_slots": np.empty((B, Q), np.int32), "n_freed": np.empty((B,), np.int32)}
+    rc = lib.ddt_oracle_kv_commit(
+        r2s.ctypes.data_as(ctypes.c_void_p), max_kv, plen.ctypes.data_as(ctypes.c_void_p),
+        p_nn, p_al, p_an, B, Q, out["freed_slots"].ctypes.data_as(ctypes.c_void_p),
+        out["n_freed"].ctypes.data_as(ctypes.c_void_p))
+    if rc != 0:
+        raise ValueError("oracle kv_commit rejected its arguments")
     return out

@@ -358,3 +358,47 @@ int ddt_oracle_tree_accept(const int32_t* node_token, const int32_t* parent,
   }
   return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* KV commit after acceptance ([P1] "What to Build New", item 5: the paged   */
+/* latent KV cache and the append step that ends each DDTree step; [P3]      */
+/* "Architectural Abstraction": tree entries at positions L + depth).        */
+/* One token per page, so committing the accepted root path is a rewrite of  */
+/* the request's slot table.                                                 */
+/* ------------------------------------------------------------------------ */
+
+int ddt_oracle_kv_commit(int32_t* req_to_slot, int max_kv, int32_t* prefix_len,
+                         const int32_t* n_nodes, const int32_t* accept_len,
+                         const int32_t* accept_nodes, int B, int Q,
+                         int32_t* freed_slots, int32_t* n_freed) {
+  if (B < 0 || Q < 1 || Q > 128 || max_kv < 1) return -1;
+  for (int b = 0; b < B; ++b) {
+    int32_t* row = req_to_slot + (size_t)b * max_kv;
+    const int32_t* path = accept_nodes + (size_t)b * Q;
+    int32_t* freed = freed_slots + (size_t)b * Q;
+    const int L = clampi(prefix_len[b], 0, max_kv);
+    const int n = clampi(n_nodes[b], 0, Q < max_kv - L ? Q : max_kv - L);
+    int a = clampi(accept_len[b], 0, n);
+    /* The committed path stops before the first entry that is not a tree node
+       or does not come after the previous one (indices grow along a path). */
+    for (int j = 0; j < a; ++j) {
+      const int node = path[j];
+      if (node < 0 || node >= n || (j > 0 && node <= path[j - 1])) { a = j; break; }
+    }
+    /* Copy the tree entries' slots before rewriting them. */
+    int32_t old[128];
+    int on_path[128];
+    for (int k = 0; k < n; ++k) { old[k] = row[L + k]; on_path[k] = 0; }
+    for (int j = 0; j < a; ++j) on_path[path[j]] = 1;
+    /* Path node j (at depth j) becomes prefix entry L + j. */
+    for (int j = 0; j < n; ++j) row[L + j] = j < a ? old[path[j]] : -1;
+    /* The other tree nodes' slots are released, in node order. */
+    int m = 0;
+    for (int k = 0; k < n; ++k)
+      if (!on_path[k]) freed[m++] = old[k];
+    for (int k = m; k < Q; ++k) freed[k] = -1;
+    n_freed[b] = m;
+    prefix_len[b] = L + a;
+  }
+  return 0;
+}

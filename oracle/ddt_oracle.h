@@ -83,6 +83,23 @@ int ddt_oracle_tree_accept(const int32_t* node_token, const int32_t* parent,
                            int32_t* accept_nodes, int32_t* out_tokens,
                            int32_t* next_root);
 
+/* KV commit after acceptance ([P1] "What to Build New", item 5: append step;
+ * [P3] "Architectural Abstraction": tree entries at positions L + depth).
+ *
+ * in/out: req_to_slot [B][max_kv] (entries [L, L+n) are the tree nodes in node
+ *         order), prefix_len [B].
+ * in    : n_nodes [B], accept_len [B], accept_nodes [B][Q] (root-first path).
+ * out   : freed_slots [B][Q] (released slots in node order, -1 padded),
+ *         n_freed [B].
+ * With L and n clamped as for verification and the path cut before its first
+ * entry outside [0, n) or not above its predecessor: entry L + j (j < a) takes
+ * the slot of path node j, entries L + a .. L + n - 1 become -1, prefix_len =
+ * L + a, and the slots of the other tree nodes are released. */
+int ddt_oracle_kv_commit(int32_t* req_to_slot, int max_kv, int32_t* prefix_len,
+                         const int32_t* n_nodes, const int32_t* accept_len,
+                         const int32_t* accept_nodes, int B, int Q,
+                         int32_t* freed_slots, int32_t* n_freed);
+
 /* Number of OpenMP threads the oracle runs with (1 if built without OpenMP). */
 int ddt_oracle_num_threads(void);
 

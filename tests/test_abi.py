@@ -116,6 +116,18 @@ def test_tree_accept_rejects(lib, B, Q, code, needle):
     assert needle in ddt.last_error()
 
 
+@pytest.mark.parametrize("B,Q,max_kv,null,needle", [(0, 9, 10, False, "B=0"),
+                                                     (1, 0, 10, False, "Q=0"),
+                                                     (1, 129, 10, False, "Q=129"),
+                                                     (1, 9, 0, False, "max_kv=0"),
+                                                     (1, 9, 10, True, "NULL")])
+def test_kv_commit_rejects(lib, B, Q, max_kv, null, needle):
+    p = ctypes.c_void_p(16)
+    assert lib.ddt_kv_commit(p, max_kv, p, p, p, NULL if null else p, B, Q, p, p,
+                             NULL) == ddt.DDT_EINVAL
+    assert needle in ddt.last_error()
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="missing"):
         ddt.load_library(str(tmp_path / "nope.so"))

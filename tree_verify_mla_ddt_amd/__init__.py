@@ -23,7 +23,8 @@ DDT_F32, DDT_BF16 = 0, 1
 MAX_Q = 128
 
 EXPORTED = ("ddt_version", "ddt_last_error", "ddt_tree_build",
-            "ddt_verify_attn_workspace_size", "ddt_verify_attn", "ddt_tree_accept")
+            "ddt_verify_attn_workspace_size", "ddt_verify_attn", "ddt_tree_accept",
+            "ddt_kv_commit")
 
 
 class DDTError(RuntimeError):
@@ -56,6 +57,8 @@ def load_library(path: str | None = None):
     lib.ddt_verify_attn.restype = i32
     lib.ddt_tree_accept.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp]
     lib.ddt_tree_accept.restype = i32
+    lib.ddt_kv_commit.argtypes = [vp, i32, vp, vp, vp, vp, i32, i32, vp, vp, vp]
+    lib.ddt_kv_commit.restype = i32
     if path is None:
         _lib = lib
     return lib
@@ -197,6 +200,31 @@ def tree_accept(node_token: torch.Tensor, parent: torch.Tensor, n_nodes: torch.T
         _ptr(node_token), _ptr(parent), _ptr(n_nodes), _ptr(target_argmax), B, Q,
         _ptr(out["accept_len"]), _ptr(out["accept_nodes"]), _ptr(out["out_tokens"]),
         _ptr(out["next_root"]), _stream())
+    _check(rc)
+    return out
+
+
+def kv_commit(req_to_slot: torch.Tensor, prefix_len: torch.Tensor, n_nodes: torch.Tensor,
+              accept_len: torch.Tensor, accept_nodes: torch.Tensor,
+              out: dict | None = None) -> dict:
+    """Append the accepted path to the committed prefix (ddt_kv_commit).
+
+    Rewrites `req_to_slot` and `prefix_len` in place; returns the released
+    slots ("freed_slots" [B][Q], -1 padded) and their count ("n_freed" [B])."""
+    _dev(req_to_slot, "req_to_slot", torch.int32, 2)
+    _dev(prefix_len, "prefix_len", torch.int32, 1)
+    _dev(n_nodes, "n_nodes", torch.int32, 1)
+    _dev(accept_len, "accept_len", torch.int32, 1)
+    _dev(accept_nodes, "accept_nodes", torch.int32, 2)
+    B, max_kv = req_to_slot.shape
+    Q = accept_nodes.shape[1]
+    dev = req_to_slot.device
+    if out is None:
+        out = {"freed_slots": torch.empty((B, Q), dtype=torch.int32, device=dev),
+               "n_freed": torch.empty((B,), dtype=torch.int32, device=dev)}
+    rc = load_library().ddt_kv_commit(
+        _ptr(req_to_slot), max_kv, _ptr(prefix_len), _ptr(n_nodes), _ptr(accept_len),
+        _ptr(accept_nodes), B, Q, _ptr(out["freed_slots"]), _ptr(out["n_freed"]), _stream())
     _check(rc)
     return out
 

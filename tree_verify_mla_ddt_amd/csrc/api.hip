@@ -135,4 +135,21 @@ int ddt_tree_accept(const int32_t* node_token, const int32_t* parent, const int3
   return launch_status(e, "ddt_tree_accept");
 }
 
+int ddt_kv_commit(int32_t* req_to_slot, int max_kv, int32_t* prefix_len,
+                  const int32_t* n_nodes, const int32_t* accept_len,
+                  const int32_t* accept_nodes, int B, int Q, int32_t* freed_slots,
+                  int32_t* n_freed, void* stream) {
+  if (B < 1) return fail(DDT_EINVAL, "ddt_kv_commit: B=%d must be >= 1", B);
+  if (Q < 1 || Q > DDT_MAX_Q)
+    return fail(DDT_EINVAL, "ddt_kv_commit: Q=%d outside [1, %d]", Q, DDT_MAX_Q);
+  if (max_kv < 1) return fail(DDT_EINVAL, "ddt_kv_commit: max_kv=%d must be >= 1", max_kv);
+  if (!req_to_slot || !prefix_len || !n_nodes || !accept_len || !accept_nodes || !freed_slots ||
+      !n_freed)
+    return fail(DDT_EINVAL, "ddt_kv_commit: NULL array argument");
+  const hipError_t e =
+      ddt::launch_kv_commit(req_to_slot, max_kv, prefix_len, n_nodes, accept_len, accept_nodes,
+                            B, Q, freed_slots, n_freed, static_cast<hipStream_t>(stream));
+  return launch_status(e, "ddt_kv_commit");
+}
+
 }  // extern "C"

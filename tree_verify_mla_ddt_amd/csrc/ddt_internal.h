@@ -29,6 +29,11 @@ hipError_t launch_tree_accept(const int32_t* node_token, const int32_t* parent,
                               int32_t* accept_nodes, int32_t* out_tokens,
                               int32_t* next_root, hipStream_t stream);
 
+hipError_t launch_kv_commit(int32_t* req_to_slot, int max_kv, int32_t* prefix_len,
+                            const int32_t* n_nodes, const int32_t* accept_len,
+                            const int32_t* accept_nodes, int B, int Q, int32_t* freed_slots,
+                            int32_t* n_freed, hipStream_t stream);
+
 // Verify attention: rows of a request are (node, head) pairs, row = i*H + h.
 // The key range of every 128-row tile is split across a fixed grid of
 // workgroups (see verify_attn.hip); partial results go to the workspace and a
