@@ -47,9 +47,11 @@ def _load():
             [p, p, p, p, i64, p, i32, p, p, p, i32, i32, i32, i32, i32, f32, i64, p, p, p])
         lib.ddt_oracle_tree_accept.argtypes = [p, p, p, p, i32, i32, p, p, p, p]
         lib.ddt_oracle_kv_commit.argtypes = [p, i32, p, p, p, p, i32, i32, p, p]
+        lib.ddt_oracle_draft_topk.argtypes = [p, i32, i32, i32, i32, p, p]
         lib.ddt_oracle_num_threads.argtypes = []
         for f in (lib.ddt_oracle_tree_build, lib.ddt_oracle_verify_attn_rows,
                   lib.ddt_oracle_tree_accept, lib.ddt_oracle_kv_commit,
+                  lib.ddt_oracle_draft_topk,
                   lib.ddt_oracle_num_threads):
             f.restype = ctypes.c_int
         _lib = lib
@@ -172,4 +174,21 @@ def kv_commit(req_to_slot, prefix_len, n_nodes, accept_len, accept_nodes) -> dic
         out["n_freed"].ctypes.data_as(ctypes.c_void_p))
     if rc != 0:
         raise ValueError("oracle kv_commit rejected its arguments")
+    return out
+
+
+def draft_topk(logits, K: int) -> dict:
+    """Per-depth top-K log-probs and ids of logits [B][D][V] (f32 or bf16 as a
+    torch tensor / numpy array; bf16 is upcast exactly).  logp is float64."""
+    import torch
+    if isinstance(logits, torch.Tensor):
+        logits = logits.float().numpy()
+    lg, p_lg = _c(logits, np.float32)
+    B, D, V = lg.shape
+    out = {"topk_logp": np.empty((B, D, K), np.float64), "topk_ids": np.empty((B, D, K), np.int32)}
+    rc = _load().ddt_oracle_draft_topk(p_lg, B, D, V, K,
+                                       out["topk_logp"].ctypes.data_as(ctypes.c_void_p),
+                                       out["topk_ids"].ctypes.data_as(ctypes.c_void_p))
+    if rc != 0:
+        raise ValueError("oracle draft_topk rejected its arguments")
     return out

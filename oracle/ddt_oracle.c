@@ -402,3 +402,51 @@ int ddt_oracle_kv_commit(int32_t* req_to_slot, int max_kv, int32_t* prefix_len,
   }
   return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Per-depth top-K extraction ([P1] "What to Build New", item 4: the fused   */
+/* draft helpers' per-depth top-k logit extraction that feeds the builder).  */
+/* Each (request, depth) row: log-softmax over the vocabulary, then the K    */
+/* entries with the largest logits (lower index first among equal logits).   */
+/* NaN logits count as -inf.                                                 */
+/* ------------------------------------------------------------------------ */
+
+int ddt_oracle_draft_topk(const float* logits, int B, int D, int V, int K,
+                          double* topk_logp, int32_t* topk_ids) {
+  if (B < 0 || D < 0 || V < 1 || K < 1 || K > V) return -1;
+  const long long rows = (long long)B * D;
+#pragma omp parallel for schedule(dynamic)
+  for (long long r = 0; r < rows; ++r) {
+    const float* x = logits + r * (long long)V;
+    double m = -INFINITY;
+    for (int v = 0; v < V; ++v) {
+      const double xv = isnan(x[v]) ? -INFINITY : (double)x[v];
+      if (xv > m) m = xv;
+    }
+    double lse = -INFINITY;
+    if (m > -INFINITY) {
+      double sum = 0.0;
+      for (int v = 0; v < V; ++v) {
+        const double xv = isnan(x[v]) ? -INFINITY : (double)x[v];
+        sum += exp(xv - m);
+      }
+      lse = m + log(sum);
+    }
+    /* K rounds of "largest remaining logit, lowest index on a tie". */
+    unsigned char* taken = (unsigned char*)calloc((size_t)V, 1);
+    for (int k = 0; k < K; ++k) {
+      int best = -1;
+      double bv = 0.0;
+      for (int v = 0; v < V; ++v) {
+        if (taken[v]) continue;
+        const double xv = isnan(x[v]) ? -INFINITY : (double)x[v];
+        if (best < 0 || xv > bv) { best = v; bv = xv; }
+      }
+      taken[best] = 1;
+      topk_ids[r * K + k] = best;
+      topk_logp[r * K + k] = (bv == -INFINITY || lse == -INFINITY) ? -INFINITY : bv - lse;
+    }
+    free(taken);
+  }
+  return 0;
+}

@@ -95,6 +95,17 @@ int ddt_oracle_tree_accept(const int32_t* node_token, const int32_t* parent,
  * entry outside [0, n) or not above its predecessor: entry L + j (j < a) takes
  * the slot of path node j, entries L + a .. L + n - 1 become -1, prefix_len =
  * L + a, and the slots of the other tree nodes are released. */
+/* Per-depth top-K extraction ([P1] "What to Build New", item 4: per-depth
+ * top-k logit extraction, the builder's input).
+ *
+ * in : logits [B][D][V] f32 (bf16 inputs upcast exactly by the caller).
+ * out: topk_logp [B][D][K] f64 = logit - logsumexp(row) (natural log; -inf for
+ *      a -inf logit or an all -inf row), topk_ids [B][D][K]: the K largest
+ *      logits of the row, largest first, lower index first among equal logits.
+ * NaN logits count as -inf.  Requires 1 <= K <= V. */
+int ddt_oracle_draft_topk(const float* logits, int B, int D, int V, int K,
+                          double* topk_logp, int32_t* topk_ids);
+
 int ddt_oracle_kv_commit(int32_t* req_to_slot, int max_kv, int32_t* prefix_len,
                          const int32_t* n_nodes, const int32_t* accept_len,
                          const int32_t* accept_nodes, int B, int Q,
