@@ -5,6 +5,7 @@
  * one HIP stream with no host round-trip between them, and a fourth commits
  * the accepted path to the KV cache:
  *
+ *   ddt_draft_topk   drafter logits -> per-depth top-K log-probs (the builder's input)
  *   ddt_tree_build   drafter per-depth top-K log-probs -> draft tree
  *   ddt_verify_attn  every tree node of every request attends, in absorbed MLA
  *                    form, over its committed latent prefix and its ancestors
@@ -14,8 +15,9 @@
  * The operations are the ones described on the pages
  *   [P1] "The Architecture of a Thousand-Parameter Decision: Designing a Native
  *        DDTree Inference Engine for Kimi K2.6", section "What to Build New"
- *        (item 2, tree-verify MLA attention; item 3, GPU tree builder; item 5,
- *        the paged latent KV cache and the append step);
+ *        (item 2, tree-verify MLA attention; item 3, GPU tree builder; item 4,
+ *        per-depth top-k logit extraction; item 5, the paged latent KV cache
+ *        and the append step);
  *   [P2] "The Architecture of Closure: How a Summary Message Encodes an Entire
  *        Engineering Session", section "The Table as a Decision Artifact"
  *        (tree_build, verify_attn, tree_accept and their chaining on device);
@@ -66,12 +68,37 @@ extern "C" {
 #define DDT_MAX_TOPK 64      /* drafter top-K                                     */
 #define DDT_MAX_DK 4096      /* D * K                                             */
 #define DDT_MAX_BATCH_ATTN 512 /* requests per ddt_verify_attn call               */
+#define DDT_MAX_VOCAB 1048576  /* vocabulary of ddt_draft_topk                     */
 
 /* Library version string, e.g. "ddt 0.1.0 gfx950". */
 const char* ddt_version(void);
 
 /* Message of the last failed call on the calling host thread ("" if none). */
 const char* ddt_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * ddt_draft_topk -- per-depth top-K extraction from drafter logits ([P1] "What
+ * to Build New", item 4: the fused draft helpers' per-depth top-k logit
+ * extraction; its output is ddt_tree_build's topk_logp / topk_ids).
+ *
+ * Input (device): logits [B][D][V], element type `dtype` (DDT_F32 or DDT_BF16):
+ *   the drafter's logits at depth d+1 of request b.
+ * Scalars: B >= 1, D >= 1, B*D <= 65535, 1 <= K <= DDT_MAX_TOPK,
+ *   K <= V <= DDT_MAX_VOCAB.
+ * Outputs (device): topk_logp [B][D][K] f32, topk_ids [B][D][K] i32.
+ * Workspace: device scratch of at least ddt_draft_topk_workspace_size(B, D, V, K)
+ *   bytes, owned by the caller, clobbered (0 for invalid scalars).
+ *
+ * Semantics, per row: the K entries with the largest logits, largest first,
+ * the lower index first among equal logits; topk_logp = logit - log sum_v
+ * exp(logit_v) (natural log, fp32 accumulation; -inf for a -inf logit or an
+ * all -inf row).  NaN logits count as -inf, -0 as +0.  The ids are exact; the
+ * log-probs are within about 1e-6 of the exact value for V up to 2^20.
+ * ------------------------------------------------------------------------- */
+size_t ddt_draft_topk_workspace_size(int B, int D, int V, int K);
+
+int ddt_draft_topk(const void* logits, int dtype, int B, int D, int V, int K, float* topk_logp,
+                   int32_t* topk_ids, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * ddt_tree_build -- best-first draft-tree construction ([P1] item 3; [P2]

@@ -128,6 +128,26 @@ def test_kv_commit_rejects(lib, B, Q, max_kv, null, needle):
     assert needle in ddt.last_error()
 
 
+@pytest.mark.parametrize("kw,needle", [(dict(B=0), "B=0"), (dict(D=0), "D=0"),
+                                       (dict(B=300, D=300), "65535"), (dict(K=0), "K=0"),
+                                       (dict(K=65), "K=65"), (dict(V=3, K=4), "V=3"),
+                                       (dict(V=1048577), "V=1048577"), (dict(dtype=5), "dtype=5"),
+                                       (dict(ws=8), "workspace")])
+def test_draft_topk_rejects(lib, kw, needle):
+    a = dict(B=1, D=8, V=160000, K=8, dtype=ddt.DDT_BF16, ws=1 << 40)
+    a.update(kw)
+    p = ctypes.c_void_p(16)
+    assert lib.ddt_draft_topk(p, a["dtype"], a["B"], a["D"], a["V"], a["K"], p, p, p, a["ws"],
+                              NULL) == ddt.DDT_EINVAL
+    assert needle in ddt.last_error()
+
+
+def test_draft_topk_workspace_size(lib):
+    n = lib.ddt_draft_topk_workspace_size(8, 15, 160000, 16)
+    assert n >= 8 * 15 * (16 * 8 + 8)
+    assert lib.ddt_draft_topk_workspace_size(8, 15, 10, 16) == 0
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="missing"):
         ddt.load_library(str(tmp_path / "nope.so"))

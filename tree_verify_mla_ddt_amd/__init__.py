@@ -24,7 +24,7 @@ MAX_Q = 128
 
 EXPORTED = ("ddt_version", "ddt_last_error", "ddt_tree_build",
             "ddt_verify_attn_workspace_size", "ddt_verify_attn", "ddt_tree_accept",
-            "ddt_kv_commit")
+            "ddt_kv_commit", "ddt_draft_topk_workspace_size", "ddt_draft_topk")
 
 
 class DDTError(RuntimeError):
@@ -59,6 +59,10 @@ def load_library(path: str | None = None):
     lib.ddt_tree_accept.restype = i32
     lib.ddt_kv_commit.argtypes = [vp, i32, vp, vp, vp, vp, i32, i32, vp, vp, vp]
     lib.ddt_kv_commit.restype = i32
+    lib.ddt_draft_topk_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.ddt_draft_topk_workspace_size.restype = sz
+    lib.ddt_draft_topk.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, sz, vp]
+    lib.ddt_draft_topk.restype = i32
     if path is None:
         _lib = lib
     return lib
@@ -200,6 +204,30 @@ def tree_accept(node_token: torch.Tensor, parent: torch.Tensor, n_nodes: torch.T
         _ptr(node_token), _ptr(parent), _ptr(n_nodes), _ptr(target_argmax), B, Q,
         _ptr(out["accept_len"]), _ptr(out["accept_nodes"]), _ptr(out["out_tokens"]),
         _ptr(out["next_root"]), _stream())
+    _check(rc)
+    return out
+
+
+def draft_topk(logits: torch.Tensor, K: int, out: dict | None = None,
+               workspace: torch.Tensor | None = None) -> dict:
+    """Per-depth top-K log-probs and ids of drafter logits [B,D,V] (bf16 or f32),
+    in the layout tree_build takes (ddt_draft_topk)."""
+    dt = logits.dtype
+    if dt not in (torch.bfloat16, torch.float32):
+        raise TypeError("logits must be bf16 or f32")
+    _dev(logits, "logits", dt, 3)
+    B, D, V = logits.shape
+    lib = load_library()
+    dev = logits.device
+    if out is None:
+        out = {"topk_logp": torch.empty((B, D, K), dtype=torch.float32, device=dev),
+               "topk_ids": torch.empty((B, D, K), dtype=torch.int32, device=dev)}
+    need = int(lib.ddt_draft_topk_workspace_size(B, D, V, K))
+    if workspace is None:
+        workspace = torch.empty((max(1, need),), dtype=torch.uint8, device=dev)
+    rc = lib.ddt_draft_topk(_ptr(logits), DDT_BF16 if dt == torch.bfloat16 else DDT_F32, B, D, V,
+                            K, _ptr(out["topk_logp"]), _ptr(out["topk_ids"]), _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _stream())
     _check(rc)
     return out
 

@@ -152,4 +152,32 @@ int ddt_kv_commit(int32_t* req_to_slot, int max_kv, int32_t* prefix_len,
   return launch_status(e, "ddt_kv_commit");
 }
 
+size_t ddt_draft_topk_workspace_size(int B, int D, int V, int K) {
+  if (B < 1 || D < 1 || K < 1 || K > DDT_MAX_TOPK || V < K || V > DDT_MAX_VOCAB) return 0;
+  return ddt::draft_topk_ws_bound(B, D, K);
+}
+
+int ddt_draft_topk(const void* logits, int dtype, int B, int D, int V, int K, float* topk_logp,
+                   int32_t* topk_ids, void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 1) return fail(DDT_EINVAL, "ddt_draft_topk: B=%d must be >= 1", B);
+  if (D < 1) return fail(DDT_EINVAL, "ddt_draft_topk: D=%d must be >= 1", D);
+  if ((long long)B * D > 65535)
+    return fail(DDT_EINVAL, "ddt_draft_topk: B*D=%lld exceeds 65535 rows", (long long)B * D);
+  if (K < 1 || K > DDT_MAX_TOPK)
+    return fail(DDT_EINVAL, "ddt_draft_topk: K=%d outside [1, %d]", K, DDT_MAX_TOPK);
+  if (V < K || V > DDT_MAX_VOCAB)
+    return fail(DDT_EINVAL, "ddt_draft_topk: V=%d outside [K=%d, %d]", V, K, DDT_MAX_VOCAB);
+  if (dtype != DDT_F32 && dtype != DDT_BF16)
+    return fail(DDT_EINVAL, "ddt_draft_topk: dtype=%d is neither DDT_F32 nor DDT_BF16", dtype);
+  if (!logits || !topk_logp || !topk_ids || !workspace)
+    return fail(DDT_EINVAL, "ddt_draft_topk: NULL array argument");
+  const ddt::TopkPlan plan = ddt::plan_draft_topk(B, D, V, K, device_cu_count());
+  if (workspace_bytes < plan.ws_bytes)
+    return fail(DDT_EINVAL, "ddt_draft_topk: workspace of %zu bytes, %zu needed", workspace_bytes,
+                plan.ws_bytes);
+  const hipError_t e = ddt::launch_draft_topk(dtype, logits, B, D, V, K, topk_logp, topk_ids,
+                                              workspace, plan, static_cast<hipStream_t>(stream));
+  return launch_status(e, "ddt_draft_topk");
+}
+
 }  // extern "C"

@@ -34,6 +34,19 @@ hipError_t launch_kv_commit(int32_t* req_to_slot, int max_kv, int32_t* prefix_le
                             const int32_t* accept_nodes, int B, int Q, int32_t* freed_slots,
                             int32_t* n_freed, hipStream_t stream);
 
+// Per-depth top-K: each (request, depth) row of logits is cut into `chunks`
+// chunks of `chunk` entries (see draft_topk.hip).
+struct TopkPlan {
+  int chunks;        // chunks per row (1..64)
+  int chunk;         // entries per chunk (multiple of 8, <= 16384)
+  size_t ws_bytes;   // workspace bytes this plan uses
+};
+TopkPlan plan_draft_topk(int B, int D, int V, int K, int num_cu);
+size_t draft_topk_ws_bound(int B, int D, int K);  // enough for any plan
+hipError_t launch_draft_topk(int dtype, const void* logits, int B, int D, int V, int K,
+                             float* topk_logp, int32_t* topk_ids, void* workspace,
+                             const TopkPlan& plan, hipStream_t stream);
+
 // Verify attention: rows of a request are (node, head) pairs, row = i*H + h.
 // The key range of every 128-row tile is split across a fixed grid of
 // workgroups (see verify_attn.hip); partial results go to the workspace and a

@@ -1,0 +1,309 @@
+// draft_topk.hip -- per-depth top-K extraction from drafter logits.
+//
+// The "per-depth top-k logit extraction" of the fused draft helpers ("The
+// Architecture of a Thousand-Parameter Decision ...", "What to Build New",
+// item 4), producing the tree builder's input: for every (request, depth) row
+// of logits over the vocabulary, log-softmax and the K largest logits (largest
+// first, lower index first among equal logits).
+//
+// It is one streaming read of the logits, so HBM bandwidth bounds it.  Rows
+// are cut into chunks of at most 16384 entries so that the grid fills the chip
+// even for a handful of rows:
+//  * draft_topk_partial_kernel (one 256-thread workgroup per chunk): 16-byte
+//    loads into LDS as order-preserving 32-bit keys, the chunk max and sum of
+//    exp(x - max), then the chunk's K-th largest key by radix selection (four
+//    8-bit digits, LDS histograms) and its K best (key, index) pairs -- every
+//    key above the K-th, then the lowest-index ties;
+//  * draft_topk_merge_kernel (one workgroup per row): the chunks' log-sum-exps
+//    combined, their candidates sorted (bitonic, in LDS) and the first K
+//    written as log-probs and ids.
+#include "ddt_internal.h"
+
+namespace ddt {
+namespace {
+
+constexpr int kTopkThreads = 256;
+constexpr int kMaxChunk = 16384;  // entries of one chunk (keys held in LDS)
+constexpr int kMaxChunks = 64;    // chunks per row
+constexpr int kMaxK = 64;
+
+// Order-preserving key of a logit (larger logit -> larger key).  NaN counts as
+// -inf and -0 as +0, so equal logits get equal keys.  Every key is > 0.
+__device__ __forceinline__ uint32_t logit_key(float x) {
+  if (x != x) x = -INFINITY;
+  if (x == 0.0f) x = 0.0f;
+  const uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+template <typename T> struct Vec16;  // 16 bytes of logits
+template <> struct Vec16<float> { static constexpr int kN = 4; };
+template <> struct Vec16<uint16_t> { static constexpr int kN = 8; };
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Candidate: key in the high word, ~index in the low word (larger = better).
+__device__ __forceinline__ uint64_t cand(uint32_t key, int idx) {
+  return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)idx);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kTopkThreads) void draft_topk_partial_kernel(
+    const T* __restrict__ logits, int V, int K, int S, int C, uint64_t* __restrict__ ws_cand,
+    float2* __restrict__ ws_ms) {
+  __shared__ uint32_t s_key[kMaxChunk];
+  __shared__ uint32_t s_hist[256];
+  __shared__ float s_red[kTopkThreads / kWave];
+  __shared__ int s_pick[2];  // digit, count above it
+  __shared__ int s_cnt;
+  __shared__ int s_wties[kTopkThreads / kWave];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = blockIdx.x;
+  const long long row = blockIdx.y;
+  const int v0 = c * C;
+  const int n = V - v0 < C ? V - v0 : C;  // > 0: the host sizes S so every chunk has entries
+  const T* src = logits + row * (long long)V + v0;
+
+  // Load the chunk as keys; this thread's max.
+  float m = -INFINITY;
+  constexpr int kN = Vec16<T>::kN;
+  const bool vec = ((reinterpret_cast<uintptr_t>(src) & 15) == 0);
+  int done = 0;
+  if (vec) {
+    const int nv = n / kN;
+    for (int i = tid; i < nv; i += kTopkThreads) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(src + (long long)i * kN);
+      const T* e = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+      for (int j = 0; j < kN; ++j) {
+        const uint32_t k = logit_key(to_f32(e[j]));
+        s_key[i * kN + j] = k;
+        m = fmaxf(m, key_value(k));
+      }
+    }
+    done = nv * kN;
+  }
+  for (int i = done + tid; i < n; i += kTopkThreads) {
+    const uint32_t k = logit_key(to_f32(src[i]));
+    s_key[i] = k;
+    m = fmaxf(m, key_value(k));
+  }
+  m = wave_max(m);
+  if (lane == 0) s_red[wave] = m;
+  __syncthreads();
+  m = s_red[0];
+#pragma unroll
+  for (int w = 1; w < kTopkThreads / kWave; ++w) m = fmaxf(m, s_red[w]);
+  __syncthreads();
+
+  // Sum of exp(x - max) over the chunk (0 when the chunk is all -inf).
+  float sum = 0.0f;
+  if (m > -INFINITY)
+    for (int i = tid; i < n; i += kTopkThreads) sum += __expf(key_value(s_key[i]) - m);
+  sum = wave_sum(sum);
+  if (lane == 0) s_red[wave] = sum;
+  __syncthreads();
+  if (tid == 0) {
+    float t = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kTopkThreads / kWave; ++w) t += s_red[w];
+    ws_ms[row * S + c] = make_float2(m, t);
+  }
+
+  // Radix selection of the K'-th largest key (K' = min(K, n)), most significant
+  // digit first: `need` counts how many keys equal to or above the selected
+  // prefix are still wanted.
+  const int kk = K < n ? K : n;
+  uint32_t prefix = 0, mask = 0;
+  int need = kk;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    s_hist[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += kTopkThreads) {
+      const uint32_t k = s_key[i];
+      if ((k & mask) == prefix) atomicAdd(&s_hist[(k >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // Bins 255..0 as 4 per lane, lane 0 holding the top ones.
+      int h[4], tot = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        h[j] = (int)s_hist[255 - (lane * 4 + j)];
+        tot += h[j];
+      }
+      // Inclusive scan of the per-lane totals (counts from the top).
+      int inc = tot;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(inc, o);
+        if (lane >= o) inc += t;
+      }
+      const int exc = inc - tot;
+      const uint64_t hit = __ballot(exc < need && inc >= need);
+      const int wl = __ffsll((unsigned long long)hit) - 1;
+      if (lane == wl) {
+        int above = exc;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (above + h[j] >= need) {
+            s_pick[0] = 255 - (lane * 4 + j);
+            s_pick[1] = above;
+            break;
+          }
+          above += h[j];
+        }
+      }
+    }
+    __syncthreads();
+    prefix |= (uint32_t)s_pick[0] << shift;
+    mask |= 255u << shift;
+    need -= s_pick[1];
+    __syncthreads();
+  }
+  // prefix is now the K'-th largest key; `need` of the keys equal to it are
+  // taken (the lowest indices), with every key above it.
+  uint64_t* out = ws_cand + (row * S + c) * (long long)K;
+  if (tid == 0) s_cnt = 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += kTopkThreads) {
+    const uint32_t k = s_key[i];
+    if (k > prefix) out[atomicAdd(&s_cnt, 1)] = cand(k, v0 + i);
+  }
+  int taken = 0;
+  const int base_gt = kk - need;
+  for (int b0 = 0; b0 < n && taken < need; b0 += kTopkThreads) {
+    const int i = b0 + tid;
+    const bool tie = i < n && s_key[i] == prefix;
+    const uint64_t bal = __ballot(tie);
+    if (lane == 0) s_wties[wave] = __popcll(bal);
+    __syncthreads();
+    int before = taken;
+    for (int w = 0; w < wave; ++w) before += s_wties[w];
+    const int rank = before + (int)__builtin_amdgcn_mbcnt_hi(
+                                  (unsigned)(bal >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
+    if (tie && rank < need) out[base_gt + rank] = cand(prefix, v0 + i);
+    int tot = 0;
+    for (int w = 0; w < kTopkThreads / kWave; ++w) tot += s_wties[w];
+    taken += tot;
+    __syncthreads();
+  }
+  // Chunks shorter than K pad with 0 (below every real candidate).
+  for (int j = kk + tid; j < K; j += kTopkThreads) out[j] = 0;
+}
+
+__global__ __launch_bounds__(kTopkThreads) void draft_topk_merge_kernel(
+    int K, int S, const uint64_t* __restrict__ ws_cand, const float2* __restrict__ ws_ms,
+    float* __restrict__ topk_logp, int32_t* __restrict__ topk_ids) {
+  __shared__ uint64_t s_c[kMaxChunks * kMaxK];
+  __shared__ float s_lse;
+  const int tid = threadIdx.x;
+  const long long row = blockIdx.x;
+  const int n = S * K;
+  int P = 1;
+  while (P < n) P <<= 1;
+  const uint64_t* src = ws_cand + row * (long long)S * K;
+  for (int i = tid; i < P; i += kTopkThreads) s_c[i] = i < n ? src[i] : 0ull;
+  if (tid == 0) {
+    // Combined log-sum-exp of the chunks (each chunk: max, sum of exp(x - max)).
+    float M = -INFINITY;
+    for (int c = 0; c < S; ++c) M = fmaxf(M, ws_ms[row * S + c].x);
+    float tot = 0.0f;
+    if (M > -INFINITY)
+      for (int c = 0; c < S; ++c) {
+        const float2 ms = ws_ms[row * S + c];
+        if (ms.x > -INFINITY) tot += ms.y * __expf(ms.x - M);
+      }
+    s_lse = M > -INFINITY ? M + __logf(tot) : -INFINITY;
+  }
+  __syncthreads();
+  // Bitonic sort, descending.
+  for (int size = 2; size <= P; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < P / 2; i += kTopkThreads) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool desc = (lo & size) == 0;
+        const uint64_t a = s_c[lo], b = s_c[hi];
+        if ((a < b) == desc) {
+          s_c[lo] = b;
+          s_c[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  const float lse = s_lse;
+  for (int k = tid; k < K; k += kTopkThreads) {
+    const uint64_t e = s_c[k];
+    const float x = key_value((uint32_t)(e >> 32));
+    topk_ids[row * K + k] = (int32_t)(0xFFFFFFFFu - (uint32_t)e);
+    topk_logp[row * K + k] = (x == -INFINITY || lse == -INFINITY) ? -INFINITY : x - lse;
+  }
+}
+
+}  // namespace
+
+TopkPlan plan_draft_topk(int B, int D, int V, int K, int num_cu) {
+  TopkPlan p;
+  const long long rows = (long long)B * D;
+  const int s_min = (V + kMaxChunk - 1) / kMaxChunk;
+  const long long want = 4LL * (num_cu > 0 ? num_cu : 256);  // workgroups to fill the chip
+  long long s = (want + rows - 1) / rows;
+  if (s < s_min) s = s_min;
+  if (s > kMaxChunks) s = kMaxChunks;
+  // No chunk may be empty: at most one chunk per 8 entries.
+  const long long s_cap = (V + 7) / 8;
+  if (s > s_cap) s = s_cap;
+  if (s < 1) s = 1;
+  int C = (int)((V + s - 1) / s);
+  C = (C + 7) / 8 * 8;
+  p.chunks = (int)((V + C - 1) / C);
+  p.chunk = C;
+  p.ws_bytes = (size_t)rows * p.chunks * ((size_t)K * sizeof(uint64_t) + sizeof(float2));
+  return p;
+}
+
+size_t draft_topk_ws_bound(int B, int D, int K) {
+  return (size_t)B * D * kMaxChunks * ((size_t)K * sizeof(uint64_t) + sizeof(float2));
+}
+
+hipError_t launch_draft_topk(int dtype, const void* logits, int B, int D, int V, int K,
+                             float* topk_logp, int32_t* topk_ids, void* workspace,
+                             const TopkPlan& plan, hipStream_t stream) {
+  const int rows = B * D;
+  uint64_t* ws_cand = static_cast<uint64_t*>(workspace);
+  float2* ws_ms = reinterpret_cast<float2*>(ws_cand + (size_t)rows * plan.chunks * K);
+  const dim3 grid1(plan.chunks, rows);
+  if (dtype == 1)
+    hipLaunchKernelGGL(draft_topk_partial_kernel<uint16_t>, grid1, dim3(kTopkThreads), 0, stream,
+                       static_cast<const uint16_t*>(logits), V, K, plan.chunks, plan.chunk,
+                       ws_cand, ws_ms);
+  else
+    hipLaunchKernelGGL(draft_topk_partial_kernel<float>, grid1, dim3(kTopkThreads), 0, stream,
+                       static_cast<const float*>(logits), V, K, plan.chunks, plan.chunk, ws_cand,
+                       ws_ms);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(draft_topk_merge_kernel, dim3(rows), dim3(kTopkThreads), 0, stream, K,
+                     plan.chunks, ws_cand, ws_ms, topk_logp, topk_ids);
+  return hipGetLastError();
+}
+
+}  // namespace ddt
