@@ -260,6 +260,26 @@ class StepRunner:
         t_w2 = self.time_graph(g_w, steps, 10)
         return max(t_c - 0.5 * (t_w + t_w2), 0.0)
 
+    def topk_stats(self, steps=200):
+        """ddt_draft_topk on this workload's drafter shape: D depths of logits over
+        the workload's vocabulary (bf16, or fp32 for the fp32 workload), timed by
+        graph replays; HBM-bound, so the roofline is bytes read and written."""
+        torch, ddt, wl = self.torch, self.ddt, self.wl
+        dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+        g = torch.Generator(device="cuda").manual_seed(11)
+        logits = (torch.randn((wl.B, wl.D, wl.vocab), generator=g, device="cuda") * 2).to(dt)
+        out = {"topk_logp": torch.empty((wl.B, wl.D, wl.K), dtype=torch.float32, device="cuda"),
+               "topk_ids": torch.empty((wl.B, wl.D, wl.K), dtype=torch.int32, device="cuda")}
+        ws = torch.empty((int(ddt.load_library().ddt_draft_topk_workspace_size(
+            wl.B, wl.D, wl.vocab, wl.K)),), dtype=torch.uint8, device="cuda")
+        gr = self.capture(lambda: ddt.draft_topk(logits, wl.K, out=out, workspace=ws))
+        ms = self.time_graph(gr, steps, 10)
+        nbytes = logits.numel() * logits.element_size() + wl.B * wl.D * wl.K * 8
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        return {"ms": round(ms, 5), "bytes": nbytes, "gbs": round(gbs, 1),
+                "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "vocab": wl.vocab, "K": wl.K,
+                "D": wl.D}
+
     def roofline(self, attn_ms, name):
         wl = self.wl
         peak = PEAK_F32_TFLOPS if wl.dtype == "f32" else PEAK_BF16_TFLOPS
@@ -372,6 +392,7 @@ def main():
         "roofline": roof,
         "step_eager_ms": round(ms_eager, 5),
         "kv_commit_step_ms": round(runner.commit_ms(), 5),
+        "draft_topk": runner.topk_stats(),
     }
 
     extras = {}
@@ -388,7 +409,8 @@ def main():
                             "attn_ms": round(ms_a, 5), "attn_tflops": rf["achieved"],
                             "attn_frac_peak": rf["frac"], "attn_hbm_gbs": rf["hbm_gbs_algorithmic"],
                             "traffic": rf["traffic"], "dtype": r.wl.dtype,
-                            "kv_commit_step_ms": round(r.commit_ms(), 5)}
+                            "kv_commit_step_ms": round(r.commit_ms(), 5),
+                            "draft_topk": r.topk_stats()}
             log(f"[bench] {name}: step {ms_s * 1e3:.1f} us, attention {ms_a * 1e3:.1f} us = "
                 f"{rf['achieved']:.1f} TFLOP/s ({100 * rf['frac']:.1f}% of {rf['peak']})")
             del r, gs, ga

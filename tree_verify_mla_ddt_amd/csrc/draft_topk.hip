@@ -7,13 +7,16 @@
 // first, lower index first among equal logits).
 //
 // It is one streaming read of the logits, so HBM bandwidth bounds it.  Rows
-// are cut into chunks of at most 16384 entries so that the grid fills the chip
+// are cut into chunks of at most 12288 entries so that the grid fills the chip
 // even for a handful of rows:
 //  * draft_topk_partial_kernel (one 256-thread workgroup per chunk): 16-byte
 //    loads into LDS as order-preserving 32-bit keys, the chunk max and sum of
-//    exp(x - max), then the chunk's K-th largest key by radix selection (four
-//    8-bit digits, LDS histograms) and its K best (key, index) pairs -- every
-//    key above the K-th, then the lowest-index ties;
+//    exp(x - max), then the chunk's K best (key, index) pairs.  The K-th
+//    largest of the 256 threads' maxima is a lower bound of the chunk's K-th
+//    largest key, so the keys at or above it -- usually a few more than K --
+//    are gathered and sorted; when wide ties make them too many, a radix
+//    selection (four 8-bit digits, LDS histograms) finds the K-th key exactly
+//    and the lowest-index ties are taken in index order;
 //  * draft_topk_merge_kernel (one workgroup per row): the chunks' log-sum-exps
 //    combined, their candidates sorted (bitonic, in LDS) and the first K
 //    written as log-probs and ids.
@@ -23,9 +26,10 @@ namespace ddt {
 namespace {
 
 constexpr int kTopkThreads = 256;
-constexpr int kMaxChunk = 16384;  // entries of one chunk (keys held in LDS)
-constexpr int kMaxChunks = 64;    // chunks per row
+constexpr int kMaxChunk = 12288;  // entries of one chunk (keys held in LDS)
+constexpr int kMaxChunks = 128;   // chunks per row
 constexpr int kMaxK = 64;
+constexpr int kCandCap = 1024;    // candidates of the threshold pass held in LDS
 
 // Order-preserving key of a logit (larger logit -> larger key).  NaN counts as
 // -inf and -0 as +0, so equal logits get equal keys.  Every key is > 0.
@@ -62,15 +66,54 @@ __device__ __forceinline__ uint64_t cand(uint32_t key, int idx) {
   return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)idx);
 }
 
+// Descending bitonic sort of P (a power of two) entries in LDS by all threads.
+template <typename U>
+__device__ __forceinline__ void bitonic_desc(U* a, int P) {
+  for (int size = 2; size <= P; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < P / 2; i += kTopkThreads) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool desc = (lo & size) == 0;
+        const U x = a[lo], y = a[hi];
+        if ((x < y) == desc) {
+          a[lo] = y;
+          a[hi] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Writes the kk best of the nc distinct candidates in a[0..nc) to out[0..kk),
+// best first: each candidate's rank is the number of larger ones (reads of one
+// LDS word by a whole wave are broadcasts).  For up to a few hundred entries
+// this beats a bitonic sort's barrier per step.
+__device__ __forceinline__ void rank_select(const uint64_t* a, int nc, int kk, uint64_t* out) {
+  for (int i = threadIdx.x; i < nc; i += kTopkThreads) {
+    const uint64_t x = a[i];
+    int r = 0;
+    for (int j = 0; j < nc; ++j) r += a[j] > x ? 1 : 0;
+    if (r < kk) out[r] = x;
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(kTopkThreads) void draft_topk_partial_kernel(
     const T* __restrict__ logits, int V, int K, int S, int C, uint64_t* __restrict__ ws_cand,
     float2* __restrict__ ws_ms) {
-  __shared__ uint32_t s_key[kMaxChunk];
+  constexpr int kN = Vec16<T>::kN;
+  constexpr int kVPT = kMaxChunk / kN / kTopkThreads;  // 16-byte loads per thread at most
+  constexpr int kE = kVPT * kN;                         // keys per thread at most
+  static_assert(kE * kTopkThreads == kMaxChunk, "chunk tiling");
+  __shared__ uint64_t s_cand[kCandCap];
+  __shared__ uint32_t s_wmax[kTopkThreads];  // each wave's thread maxima, sorted
   __shared__ uint32_t s_hist[256];
   __shared__ float s_red[kTopkThreads / kWave];
   __shared__ int s_pick[2];  // digit, count above it
   __shared__ int s_cnt;
+  __shared__ uint32_t s_tau;
   __shared__ int s_wties[kTopkThreads / kWave];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -80,30 +123,42 @@ __global__ __launch_bounds__(kTopkThreads) void draft_topk_partial_kernel(
   const int n = V - v0 < C ? V - v0 : C;  // > 0: the host sizes S so every chunk has entries
   const T* src = logits + row * (long long)V + v0;
 
-  // Load the chunk as keys; this thread's max.
-  float m = -INFINITY;
-  constexpr int kN = Vec16<T>::kN;
-  const bool vec = ((reinterpret_cast<uintptr_t>(src) & 15) == 0);
-  int done = 0;
+  // The chunk's keys stay in registers (0 = no entry; every real key is > 0).
+  // With 16-byte loads key j of a thread is entry (tid + 256*(j/kN))*kN + j%kN,
+  // otherwise entry tid + 256*j.
+  const bool vec = ((reinterpret_cast<uintptr_t>(src) & 15) == 0) && n % kN == 0;
+  uint32_t key[kE];
   if (vec) {
     const int nv = n / kN;
-    for (int i = tid; i < nv; i += kTopkThreads) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(src + (long long)i * kN);
-      const T* e = reinterpret_cast<const T*>(&raw);
+    uint4 raw[kVPT];
 #pragma unroll
-      for (int j = 0; j < kN; ++j) {
-        const uint32_t k = logit_key(to_f32(e[j]));
-        s_key[i * kN + j] = k;
-        m = fmaxf(m, key_value(k));
-      }
+    for (int u = 0; u < kVPT; ++u) {
+      const int i = tid + u * kTopkThreads;
+      raw[u] = make_uint4(0, 0, 0, 0);
+      if (i < nv) raw[u] = *reinterpret_cast<const uint4*>(src + (long long)i * kN);
     }
-    done = nv * kN;
+#pragma unroll
+    for (int u = 0; u < kVPT; ++u) {
+      const bool in = tid + u * kTopkThreads < nv;
+      const T* e = reinterpret_cast<const T*>(&raw[u]);
+#pragma unroll
+      for (int j = 0; j < kN; ++j) key[u * kN + j] = in ? logit_key(to_f32(e[j])) : 0u;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kE; ++j) {
+      const int i = tid + j * kTopkThreads;
+      key[j] = i < n ? logit_key(to_f32(src[i])) : 0u;
+    }
   }
-  for (int i = done + tid; i < n; i += kTopkThreads) {
-    const uint32_t k = logit_key(to_f32(src[i]));
-    s_key[i] = k;
-    m = fmaxf(m, key_value(k));
-  }
+  auto entry = [&](int j) -> int {
+    return vec ? (tid + kTopkThreads * (j / kN)) * kN + j % kN : tid + kTopkThreads * j;
+  };
+
+  uint32_t tmax = 0;
+#pragma unroll
+  for (int j = 0; j < kE; ++j) tmax = key[j] > tmax ? key[j] : tmax;
+  float m = tmax != 0 ? key_value(tmax) : -INFINITY;
   m = wave_max(m);
   if (lane == 0) s_red[wave] = m;
   __syncthreads();
@@ -114,10 +169,33 @@ __global__ __launch_bounds__(kTopkThreads) void draft_topk_partial_kernel(
 
   // Sum of exp(x - max) over the chunk (0 when the chunk is all -inf).
   float sum = 0.0f;
-  if (m > -INFINITY)
-    for (int i = tid; i < n; i += kTopkThreads) sum += __expf(key_value(s_key[i]) - m);
+  if (m > -INFINITY) {
+#pragma unroll
+    for (int j = 0; j < kE; ++j)
+      if (key[j] != 0) sum += __expf(key_value(key[j]) - m);
+  }
   sum = wave_sum(sum);
   if (lane == 0) s_red[wave] = sum;
+
+  // Threshold: the kk-th largest of the 256 threads' maxima bounds the chunk's
+  // kk-th largest key from below (kk threads hold a key at least that large),
+  // so the keys at or above it are a superset of the answer, usually a few more.
+  // Each wave sorts its maxima with a lane-exchange bitonic network; one thread
+  // merges the four sorted lists far enough.
+  const int kk = K < n ? K : n;
+  uint32_t v = tmax;
+#pragma unroll
+  for (int size = 2; size <= kWave; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const uint32_t o = (uint32_t)__shfl_xor((int)v, stride);
+      const bool desc = (lane & size) == 0 || size == kWave;
+      const bool lower = (lane & stride) == 0;
+      v = (lower == desc) ? (v > o ? v : o) : (v < o ? v : o);
+    }
+  }
+  s_wmax[tid] = v;
+  if (tid == 0) s_cnt = 0;
   __syncthreads();
   if (tid == 0) {
     float t = 0.0f;
@@ -125,19 +203,59 @@ __global__ __launch_bounds__(kTopkThreads) void draft_topk_partial_kernel(
     for (int w = 0; w < kTopkThreads / kWave; ++w) t += s_red[w];
     ws_ms[row * S + c] = make_float2(m, t);
   }
+  {
+    // The kk-th largest of the four sorted lists: the value whose count of
+    // larger values is below kk and whose count of larger-or-equal values
+    // reaches kk (binary searches in each list).
+    int gt = 0, ge = 0;
+#pragma unroll
+    for (int w = 0; w < kTopkThreads / kWave; ++w) {
+      const uint32_t* L = s_wmax + w * kWave;
+      int lo = 0, hi = kWave;  // first position with L[pos] <= v (descending list)
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (L[mid] > v) lo = mid + 1; else hi = mid;
+      }
+      gt += lo;
+      int lo2 = lo, hi2 = kWave;  // first position with L[pos] < v
+      while (lo2 < hi2) {
+        const int mid = (lo2 + hi2) >> 1;
+        if (L[mid] >= v) lo2 = mid + 1; else hi2 = mid;
+      }
+      ge += lo2;
+    }
+    if (gt < kk && ge >= kk) s_tau = v;  // every such thread holds the same value
+  }
+  __syncthreads();
+  const uint32_t tau = s_tau;
+#pragma unroll
+  for (int j = 0; j < kE; ++j) {
+    if (key[j] >= tau && key[j] != 0) {
+      const int at = atomicAdd(&s_cnt, 1);
+      if (at < kCandCap) s_cand[at] = cand(key[j], v0 + entry(j));
+    }
+  }
+  __syncthreads();
+  uint64_t* out = ws_cand + (row * S + c) * (long long)K;
+  const int nc = s_cnt;
+  if (nc <= kCandCap) {
+    rank_select(s_cand, nc, kk, out);
+    for (int j = kk + tid; j < K; j += kTopkThreads) out[j] = 0;
+    return;
+  }
 
-  // Radix selection of the K'-th largest key (K' = min(K, n)), most significant
-  // digit first: `need` counts how many keys equal to or above the selected
-  // prefix are still wanted.
-  const int kk = K < n ? K : n;
+  // Many keys at the threshold (wide ties): radix selection of the kk-th
+  // largest key over the registers, most significant digit first: `need` counts
+  // how many keys equal to or above the selected prefix are still wanted.
   uint32_t prefix = 0, mask = 0;
   int need = kk;
   for (int shift = 24; shift >= 0; shift -= 8) {
     s_hist[tid] = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += kTopkThreads) {
-      const uint32_t k = s_key[i];
-      if ((k & mask) == prefix) atomicAdd(&s_hist[(k >> shift) & 255u], 1u);
+#pragma unroll
+    for (int j = 0; j < kE; ++j) {
+      const uint32_t k = key[j];
+      if (k != 0 && (k & mask) == prefix) atomicAdd(&s_hist[(k >> shift) & 255u], 1u);
     }
     __syncthreads();
     if (wave == 0) {
@@ -177,20 +295,20 @@ __global__ __launch_bounds__(kTopkThreads) void draft_topk_partial_kernel(
     need -= s_pick[1];
     __syncthreads();
   }
-  // prefix is now the K'-th largest key; `need` of the keys equal to it are
+  // prefix is now the kk-th largest key; `need` of the keys equal to it are
   // taken (the lowest indices), with every key above it.
-  uint64_t* out = ws_cand + (row * S + c) * (long long)K;
   if (tid == 0) s_cnt = 0;
   __syncthreads();
-  for (int i = tid; i < n; i += kTopkThreads) {
-    const uint32_t k = s_key[i];
-    if (k > prefix) out[atomicAdd(&s_cnt, 1)] = cand(k, v0 + i);
-  }
+#pragma unroll
+  for (int j = 0; j < kE; ++j)
+    if (key[j] > prefix) out[atomicAdd(&s_cnt, 1)] = cand(key[j], v0 + entry(j));
+  // Ties in index order: the chunk is read again (from the caches) 256
+  // consecutive entries at a time.
   int taken = 0;
   const int base_gt = kk - need;
   for (int b0 = 0; b0 < n && taken < need; b0 += kTopkThreads) {
     const int i = b0 + tid;
-    const bool tie = i < n && s_key[i] == prefix;
+    const bool tie = i < n && logit_key(to_f32(src[i])) == prefix;
     const uint64_t bal = __ballot(tie);
     if (lane == 0) s_wties[wave] = __popcll(bal);
     __syncthreads();
@@ -211,7 +329,7 @@ __global__ __launch_bounds__(kTopkThreads) void draft_topk_partial_kernel(
 __global__ __launch_bounds__(kTopkThreads) void draft_topk_merge_kernel(
     int K, int S, const uint64_t* __restrict__ ws_cand, const float2* __restrict__ ws_ms,
     float* __restrict__ topk_logp, int32_t* __restrict__ topk_ids) {
-  __shared__ uint64_t s_c[kMaxChunks * kMaxK];
+  __shared__ uint64_t s_c[kMaxChunks * kMaxK];  // 64 KiB
   __shared__ float s_lse;
   const int tid = threadIdx.x;
   const long long row = blockIdx.x;
@@ -233,25 +351,18 @@ __global__ __launch_bounds__(kTopkThreads) void draft_topk_merge_kernel(
     s_lse = M > -INFINITY ? M + __logf(tot) : -INFINITY;
   }
   __syncthreads();
-  // Bitonic sort, descending.
-  for (int size = 2; size <= P; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < P / 2; i += kTopkThreads) {
-        const int lo = 2 * i - (i & (stride - 1));
-        const int hi = lo + stride;
-        const bool desc = (lo & size) == 0;
-        const uint64_t a = s_c[lo], b = s_c[hi];
-        if ((a < b) == desc) {
-          s_c[lo] = b;
-          s_c[hi] = a;
-        }
-      }
-      __syncthreads();
-    }
+  __shared__ uint64_t s_top[kMaxK];
+  const uint64_t* best = s_c;
+  if (n <= 1024) {
+    rank_select(s_c, n, K, s_top);
+    __syncthreads();
+    best = s_top;
+  } else {
+    bitonic_desc(s_c, P);
   }
   const float lse = s_lse;
   for (int k = tid; k < K; k += kTopkThreads) {
-    const uint64_t e = s_c[k];
+    const uint64_t e = best[k];
     const float x = key_value((uint32_t)(e >> 32));
     topk_ids[row * K + k] = (int32_t)(0xFFFFFFFFu - (uint32_t)e);
     topk_logp[row * K + k] = (x == -INFINITY || lse == -INFINITY) ? -INFINITY : x - lse;
@@ -264,8 +375,11 @@ TopkPlan plan_draft_topk(int B, int D, int V, int K, int num_cu) {
   TopkPlan p;
   const long long rows = (long long)B * D;
   const int s_min = (V + kMaxChunk - 1) / kMaxChunk;
-  const long long want = 4LL * (num_cu > 0 ? num_cu : 256);  // workgroups to fill the chip
+  // About two workgroups per CU, at most 64 chunks per row unless the chunk
+  // size forces more.
+  const long long want = 2LL * (num_cu > 0 ? num_cu : 256);
   long long s = (want + rows - 1) / rows;
+  if (s > 64) s = 64;
   if (s < s_min) s = s_min;
   if (s > kMaxChunks) s = kMaxChunks;
   // No chunk may be empty: at most one chunk per 8 entries.
