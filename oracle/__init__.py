@@ -48,10 +48,12 @@ def _load():
         lib.ddt_oracle_tree_accept.argtypes = [p, p, p, p, i32, i32, p, p, p, p]
         lib.ddt_oracle_kv_commit.argtypes = [p, i32, p, p, p, p, i32, i32, p, p]
         lib.ddt_oracle_draft_topk.argtypes = [p, i32, i32, i32, i32, p, p]
+        lib.ddt_oracle_tree_accept_sampling.argtypes = (
+            [p, i32, p, p, p, p, p, p, i32, i32, ctypes.c_double] + [p] * 7)
         lib.ddt_oracle_num_threads.argtypes = []
         for f in (lib.ddt_oracle_tree_build, lib.ddt_oracle_verify_attn_rows,
                   lib.ddt_oracle_tree_accept, lib.ddt_oracle_kv_commit,
-                  lib.ddt_oracle_draft_topk,
+                  lib.ddt_oracle_draft_topk, lib.ddt_oracle_tree_accept_sampling,
                   lib.ddt_oracle_num_threads):
             f.restype = ctypes.c_int
         _lib = lib
@@ -191,4 +193,39 @@ def draft_topk(logits, K: int) -> dict:
                                        out["topk_ids"].ctypes.data_as(ctypes.c_void_p))
     if rc != 0:
         raise ValueError("oracle draft_topk rejected its arguments")
+    return out
+
+
+def tree_accept_sampling(logits, temperature, node_token, parent, n_nodes, coins, coin_final,
+                         band_eps: float = 0.0) -> dict:
+    """Sampling acceptance over target logits [B][Q][V] (f32 or bf16 as a torch
+    tensor / numpy array; bf16 is upcast exactly).  Returns the greedy
+    acceptance outputs plus the diagnostics margin, bonus_lo and bonus_hi."""
+    import torch
+    if isinstance(logits, torch.Tensor):
+        logits = logits.float().numpy()
+    lg, p_lg = _c(logits, np.float32)
+    B, Q, V = lg.shape
+    tmp, p_tmp = _c(temperature, np.float32)
+    tok, p_tok = _c(node_token, np.int32)
+    par, p_par = _c(parent, np.int32)
+    nn, p_nn = _c(n_nodes, np.int32)
+    cn, p_cn = _c(coins, np.float32)
+    cf, p_cf = _c(coin_final, np.float32)
+    assert tmp.shape == (B,) and tok.shape == (B, Q) and par.shape == (B, Q)
+    assert nn.shape == (B,) and cn.shape == (B, Q) and cf.shape == (B,)
+    out = {"accept_len": np.empty((B,), np.int32),
+           "accept_nodes": np.empty((B, Q), np.int32),
+           "out_tokens": np.empty((B, Q), np.int32),
+           "next_root": np.empty((B,), np.int32),
+           "margin": np.empty((B,), np.float64),
+           "bonus_lo": np.empty((B,), np.int32),
+           "bonus_hi": np.empty((B,), np.int32)}
+    ptr = {k: v.ctypes.data_as(ctypes.c_void_p) for k, v in out.items()}
+    rc = _load().ddt_oracle_tree_accept_sampling(
+        p_lg, V, p_tmp, p_tok, p_par, p_nn, p_cn, p_cf, B, Q, float(band_eps),
+        ptr["accept_len"], ptr["accept_nodes"], ptr["out_tokens"], ptr["next_root"],
+        ptr["margin"], ptr["bonus_lo"], ptr["bonus_hi"])
+    if rc != 0:
+        raise ValueError("oracle tree_accept_sampling rejected its arguments")
     return out

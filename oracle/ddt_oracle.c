@@ -450,3 +450,150 @@ int ddt_oracle_draft_topk(const float* logits, int B, int D, int V, int K,
   }
   return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Sampling acceptance ([P1] "What to Build New", item 2: the sampling-      */
+/* probability path of tree verification, normalized target probabilities   */
+/* at every tree node; [P1] "What to Reuse": the target-only tree            */
+/* speculative-sampling step that samples from the verified distribution;   */
+/* item 5: the temperature commit path).                                     */
+/*                                                                           */
+/* Readings (the pages name the step but do not spell it out):               */
+/*   R16 The drafted tokens are fixed choices, so the draft distribution is   */
+/*       a point mass on each drafted token and only the target's            */
+/*       probabilities enter ("target only").  At node `cur` the target       */
+/*       distribution is p = softmax(logits[cur] / T).  Its children are     */
+/*       tried in index order; a child with token t is accepted when          */
+/*       coin[child] < p(t) / (1 - R), R the mass of the tokens already      */
+/*       rejected at this node; otherwise t joins the rejected set.  A token  */
+/*       outside [0, V), or one already rejected, has probability 0 and is   */
+/*       never accepted.  The walk moves to the accepted child.  When no      */
+/*       child is accepted, the bonus token is drawn from the residual        */
+/*       r(v) = p(v) for v not rejected (0 otherwise) by inverse CDF: the     */
+/*       first v in index order with r(v) > 0 and r(0) + ... + r(v) >         */
+/*       coin_final * (r(0) + ... + r(V-1)); if none qualifies (rounding, or  */
+/*       coin_final >= 1) the last v with r(v) > 0; if the residual is       */
+/*       empty, the argmax.                                                   */
+/*   R17 A request whose temperature is not a finite value > 0, and a node    */
+/*       whose largest logit is not finite (all -inf, or a +inf entry), is    */
+/*       taken greedily: p is a point mass on the argmax (lowest index among  */
+/*       equal logits; NaN counts as -inf).  Coins are then not consulted,    */
+/*       and the result equals greedy acceptance against the argmax tokens.  */
+/* ------------------------------------------------------------------------ */
+
+int ddt_oracle_tree_accept_sampling(const float* logits, int V, const float* temperature,
+                                    const int32_t* node_token, const int32_t* parent,
+                                    const int32_t* n_nodes, const float* coins,
+                                    const float* coin_final, int B, int Q, double band_eps,
+                                    int32_t* accept_len, int32_t* accept_nodes,
+                                    int32_t* out_tokens, int32_t* next_root, double* margin,
+                                    int32_t* bonus_lo, int32_t* bonus_hi) {
+  if (B < 0 || Q < 1 || V < 1) return -1;
+#pragma omp parallel for schedule(dynamic)
+  for (int b = 0; b < B; ++b) {
+    const int32_t* tok = node_token + (size_t)b * Q;
+    const int32_t* par = parent + (size_t)b * Q;
+    const float* coin = coins + (size_t)b * Q;
+    int32_t* path = accept_nodes + (size_t)b * Q;
+    int32_t* outt = out_tokens + (size_t)b * Q;
+    const int nb = clampi(n_nodes[b], 1, Q);
+    const double T = (double)temperature[b];
+    const int greedy_req = !(T > 0.0 && isfinite(T));
+    double* p = (double*)malloc((size_t)V * sizeof(double));
+    unsigned char* rejected = (unsigned char*)calloc((size_t)V, 1);
+    double min_margin = INFINITY;
+    for (int i = 0; i < Q; ++i) path[i] = outt[i] = -1;
+
+    int len = 1, cur = 0, bonus = -1, blo = -1, bhi = -1;
+    path[0] = 0;
+    for (;;) {
+      /* The target distribution at node cur. */
+      const float* x = logits + ((size_t)b * Q + cur) * (size_t)V;
+      double M = -INFINITY;
+      int amax = 0;
+      for (int v = 0; v < V; ++v) {
+        const double xv = isnan(x[v]) ? -INFINITY : (double)x[v];
+        if (xv > M) { M = xv; amax = v; }
+      }
+      const int greedy = greedy_req || !isfinite(M);
+      if (greedy) {
+        for (int v = 0; v < V; ++v) p[v] = v == amax ? 1.0 : 0.0;
+      } else {
+        double Z = 0.0;
+        for (int v = 0; v < V; ++v) {
+          const double xv = isnan(x[v]) ? -INFINITY : (double)x[v];
+          p[v] = exp((xv - M) / T);
+          Z += p[v];
+        }
+        for (int v = 0; v < V; ++v) p[v] /= Z;
+      }
+      /* Try the children in index order. */
+      memset(rejected, 0, (size_t)V);
+      double R = 0.0;
+      int next = -1;
+      for (int c = cur + 1; c < nb; ++c) {
+        if (par[c] != cur) continue;
+        const int t = tok[c];
+        if (t < 0 || t >= V || rejected[t] || !(p[t] > 0.0)) continue;
+        if (greedy) { next = c; break; }  /* t is the argmax */
+        const double pres = p[t] / (1.0 - R);
+        const double d = fabs((double)coin[c] - pres);
+        if (d < min_margin) min_margin = d;
+        if ((double)coin[c] < pres) { next = c; break; }
+        rejected[t] = 1;
+        R += p[t];
+      }
+      if (next >= 0) {
+        path[len++] = next;
+        cur = next;
+        continue;
+      }
+      /* No child accepted: the bonus token from the residual distribution. */
+      if (greedy) {
+        bonus = blo = bhi = amax;
+        break;
+      }
+      double Zr = 0.0;
+      int last = -1;
+      for (int v = 0; v < V; ++v)
+        if (!rejected[v] && p[v] > 0.0) { Zr += p[v]; last = v; }
+      if (last < 0) {
+        bonus = blo = bhi = amax;
+        break;
+      }
+      const double target = (double)coin_final[b] * Zr;
+      double cum = 0.0;
+      for (int v = 0; v < V; ++v) {
+        if (rejected[v] || !(p[v] > 0.0)) continue;
+        cum += p[v];
+        if (cum > target) { bonus = v; break; }
+      }
+      if (bonus < 0) bonus = last;
+      /* Entries whose residual CDF interval comes within band_eps * Zr of the
+         target: every one of them is a correct draw for a coin that far off. */
+      cum = 0.0;
+      for (int v = 0; v < V; ++v) {
+        if (rejected[v] || !(p[v] > 0.0)) continue;
+        const double lo = cum;
+        cum += p[v];
+        if (cum >= target - band_eps * Zr && lo <= target + band_eps * Zr) {
+          if (blo < 0) blo = v;
+          bhi = v;
+        }
+      }
+      if (blo < 0 || bonus < blo) blo = bonus;
+      if (bonus > bhi) bhi = bonus;
+      break;
+    }
+    for (int k = 1; k < len; ++k) outt[k - 1] = tok[path[k]];
+    outt[len - 1] = bonus;
+    accept_len[b] = len;
+    next_root[b] = bonus;
+    if (margin) margin[b] = min_margin;
+    if (bonus_lo) bonus_lo[b] = blo;
+    if (bonus_hi) bonus_hi[b] = bhi;
+    free(p);
+    free(rejected);
+  }
+  return 0;
+}

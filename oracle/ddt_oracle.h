@@ -111,6 +111,32 @@ int ddt_oracle_kv_commit(int32_t* req_to_slot, int max_kv, int32_t* prefix_len,
                          const int32_t* accept_nodes, int B, int Q,
                          int32_t* freed_slots, int32_t* n_freed);
 
+/* Sampling acceptance ([P1] "What to Build New", item 2: the sampling-
+ * probability path; "What to Reuse", item 3: target-only tree speculative
+ * sampling from the verified distribution; item 5: the temperature commit).
+ *
+ * in : logits [B][Q][V] f32 (the target's logits at every tree node; bf16
+ *      upcast exactly by the caller), temperature [B], node_token, parent
+ *      [B][Q], n_nodes [B] (clamped to [1, Q]), coins [B][Q] (the uniform draw
+ *      used when node c is tried as a child), coin_final [B] (the draw for the
+ *      bonus token).
+ * out: accept_len [B], accept_nodes [B][Q], out_tokens [B][Q], next_root [B]
+ *      as for greedy acceptance.
+ * Diagnostics (each may be NULL): margin [B] = the smallest |coin - p_res| of
+ *      the request's sampled acceptance tests (+inf if none); bonus_lo/hi [B] =
+ *      the index range of residual entries whose CDF interval comes within
+ *      band_eps * (residual mass) of the bonus draw's target.
+ * Readings R16 (target-only rejection sampling, children in index order,
+ * inverse-CDF bonus) and R17 (greedy requests and nodes) are spelt out above
+ * the definition. */
+int ddt_oracle_tree_accept_sampling(const float* logits, int V, const float* temperature,
+                                    const int32_t* node_token, const int32_t* parent,
+                                    const int32_t* n_nodes, const float* coins,
+                                    const float* coin_final, int B, int Q, double band_eps,
+                                    int32_t* accept_len, int32_t* accept_nodes,
+                                    int32_t* out_tokens, int32_t* next_root, double* margin,
+                                    int32_t* bonus_lo, int32_t* bonus_hi);
+
 /* Number of OpenMP threads the oracle runs with (1 if built without OpenMP). */
 int ddt_oracle_num_threads(void);
 

@@ -10,23 +10,24 @@
 // are cut into chunks of at most 12288 entries so that the grid fills the chip
 // even for a handful of rows:
 //  * draft_topk_partial_kernel (one 256-thread workgroup per chunk): 16-byte
-//    loads into LDS as order-preserving 32-bit keys, the chunk max and sum of
-//    exp(x - max), then the chunk's K best (key, index) pairs.  The K-th
-//    largest of the 256 threads' maxima is a lower bound of the chunk's K-th
-//    largest key, so the keys at or above it -- usually a few more than K --
-//    are gathered and sorted; when wide ties make them too many, a radix
-//    selection (four 8-bit digits, LDS histograms) finds the K-th key exactly
-//    and the lowest-index ties are taken in index order;
+//    loads straight into registers as order-preserving 32-bit keys, the chunk
+//    max and sum of exp(x - max), then the chunk's K best (key, index) pairs.
+//    The K-th largest of the 256 threads' maxima is a lower bound of the
+//    chunk's K-th largest key, so the keys at or above it -- usually a few more
+//    than K -- are gathered into LDS and ranked (each candidate counts the
+//    larger ones); when wide ties make them too many, a radix selection (four
+//    8-bit digits, LDS histograms) finds the K-th key exactly and the
+//    lowest-index ties are taken in index order;
 //  * draft_topk_merge_kernel (one workgroup per row): the chunks' log-sum-exps
-//    combined, their candidates sorted (bitonic, in LDS) and the first K
-//    written as log-probs and ids.
+//    combined, their candidates ranked (or bitonic-sorted in LDS when there are
+//    more than 1024) and the first K written as log-probs and ids.
 #include "ddt_internal.h"
 
 namespace ddt {
 namespace {
 
 constexpr int kTopkThreads = 256;
-constexpr int kMaxChunk = 12288;  // entries of one chunk (keys held in LDS)
+constexpr int kMaxChunk = 12288;  // entries of one chunk (keys held in registers)
 constexpr int kMaxChunks = 128;   // chunks per row
 constexpr int kMaxK = 64;
 constexpr int kCandCap = 1024;    // candidates of the threshold pass held in LDS

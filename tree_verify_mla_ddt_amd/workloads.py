@@ -228,3 +228,41 @@ def synth_target_argmax(wl: Workload, node_token: np.ndarray, parent: np.ndarray
             t = int(rng.integers(0, V))
         tgt[b, node] = t
     return tgt.astype(np.int32)
+
+
+SAMPLING_TEMPERATURES = (0.0, 0.7, 1.0, 1.5)
+
+
+def sampling_inputs(node_token: np.ndarray, parent: np.ndarray, n_nodes: np.ndarray, V: int,
+                    seed: int = 0, temperatures=SAMPLING_TEMPERATURES, sigma: float = 2.0,
+                    p_hit: float = 0.7, dtype=torch.bfloat16):
+    """Target-side inputs of sampling acceptance for a drafted tree.
+
+    logits [B,Q,V]: N(0, sigma) per node; at a node with children, with
+    probability p_hit one child's token (uniform among the children) gets the
+    row's log-sum-exp plus delta ~ U(-1, 3), so the target gives it roughly
+    27%..95% of its mass at temperature 1 and drafts are accepted at a useful
+    rate.  Returned as a torch tensor of `dtype` (the boosted entry is set
+    after rounding the row).  temperature [B] cycles through `temperatures`;
+    coins [B,Q] and coin_final [B] are U[0, 1) float32."""
+    rng = np.random.default_rng((seed, 11))
+    B, Q = node_token.shape
+    x = torch.from_numpy(rng.standard_normal((B, Q, V), dtype=np.float32) * np.float32(sigma))
+    x = x.to(dtype)
+    for b in range(B):
+        nb = int(n_nodes[b])
+        for n in range(nb):
+            kids = [c for c in range(n + 1, nb) if parent[b, c] == n]
+            if not kids or rng.random() >= p_hit:
+                continue
+            c = kids[int(rng.integers(0, len(kids)))]
+            t = int(node_token[b, c])
+            if not 0 <= t < V:
+                continue
+            row = x[b, n].double()
+            lse = float(torch.logsumexp(row, 0))
+            x[b, n, t] = lse + float(rng.uniform(-1.0, 3.0))
+    temperature = np.array([temperatures[b % len(temperatures)] for b in range(B)], np.float32)
+    coins = rng.random((B, Q), dtype=np.float32)
+    coin_final = rng.random((B,), dtype=np.float32)
+    return x, temperature, coins, coin_final
