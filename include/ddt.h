@@ -10,14 +10,18 @@
  *   ddt_verify_attn  every tree node of every request attends, in absorbed MLA
  *                    form, over its committed latent prefix and its ancestors
  *   ddt_tree_accept  greedy walk of the verified tree -> accepted tokens
+ *   ddt_tree_accept_sampling  the same walk under temperature sampling, from the
+ *                    target's logits at every tree node
  *   ddt_kv_commit    accepted path -> committed prefix slots (slot table rewrite)
  *
  * The operations are the ones described on the pages
  *   [P1] "The Architecture of a Thousand-Parameter Decision: Designing a Native
  *        DDTree Inference Engine for Kimi K2.6", section "What to Build New"
- *        (item 2, tree-verify MLA attention; item 3, GPU tree builder; item 4,
- *        per-depth top-k logit extraction; item 5, the paged latent KV cache
- *        and the append step);
+ *        (item 2, tree-verify MLA attention and its greedy and sampling-
+ *        probability paths; item 3, GPU tree builder; item 4, per-depth top-k
+ *        logit extraction; item 5, the paged latent KV cache, the append step
+ *        and the greedy and temperature commit paths) and section "What to
+ *        Reuse" (item 3, target-only tree speculative sampling);
  *   [P2] "The Architecture of Closure: How a Summary Message Encodes an Entire
  *        Engineering Session", section "The Table as a Decision Artifact"
  *        (tree_build, verify_attn, tree_accept and their chaining on device);
@@ -203,6 +207,58 @@ int ddt_tree_accept(const int32_t* node_token, const int32_t* parent,
                     const int32_t* n_nodes, const int32_t* target_argmax,
                     int B, int Q, int32_t* accept_len, int32_t* accept_nodes,
                     int32_t* out_tokens, int32_t* next_root, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * ddt_tree_accept_sampling -- acceptance under temperature sampling ([P1]
+ * "What to Build New", item 2: the sampling-probability path of tree
+ * verification, normalized target probabilities at the tree nodes; "What to
+ * Reuse", item 3: target-only tree speculative sampling from the verified
+ * distribution; item 5: the temperature commit path).
+ *
+ * Inputs (device):
+ *   target_logits [B][Q][V], element type `dtype` (DDT_F32 or DDT_BF16): the
+ *                  target model's logits at every tree node (row i predicts the
+ *                  token after node i); rows of nodes >= n_b are not read.
+ *   temperature   [B] f32; a value that is not finite and > 0 (0, negative,
+ *                  inf, NaN) makes the request greedy.
+ *   node_token, parent [B][Q] i32 and n_nodes [B] from ddt_tree_build (n_b
+ *                  clamped to [1, Q]).
+ *   coins         [B][Q] f32 in [0, 1): the uniform draw used when node c is
+ *                  tried as a child (each node is tried at most once).
+ *   coin_final    [B] f32 in [0, 1): the draw for the bonus token.
+ *   The caller draws the coins, so a seeded generator makes a call
+ *   reproducible.
+ * Scalars: 1 <= B, 1 <= Q <= DDT_MAX_Q, B*Q <= 2^24, 1 <= V <= DDT_MAX_VOCAB.
+ * Outputs (device): accept_len, accept_nodes, out_tokens, next_root exactly as
+ *   for ddt_tree_accept.
+ * Workspace: device scratch of at least
+ *   ddt_tree_accept_sampling_workspace_size(B, Q, V) bytes (0 for invalid
+ *   scalars), owned by the caller, clobbered.
+ * Semantics, per request, with p = softmax(logits[node] / T) (NaN logits count
+ * as -inf): from the root, the children c of the current node (parent[c] ==
+ * cur, c > cur, c < n_b) are tried in index order; a child whose token t lies
+ * in [0, V) and was not tried before at this node is accepted when
+ * coins[c] < p(t) / (1 - R), R the mass of the tokens rejected so far at this
+ * node, and the walk moves to it.  When no child is accepted, the bonus token
+ * is the first index v, in index order, of the residual r = p without the
+ * rejected tokens whose running sum r(0) + ... + r(v) exceeds coin_final *
+ * sum(r); the last v with r(v) > 0 if none does; the argmax if r is empty.  A
+ * greedy request, and a node whose largest logit is not finite, use a point
+ * mass on the argmax (the lowest index among the largest logits) and ignore
+ * the coins: then the result equals ddt_tree_accept against the argmax tokens,
+ * bit for bit.  Probabilities are computed in fp32 (about 1e-6 relative), so a
+ * decision whose coin lies within that distance of its threshold may go the
+ * other way than in exact arithmetic, and the bonus token may be a neighbour
+ * of the exact one when the draw lies that close to an entry's boundary.
+ * ------------------------------------------------------------------------- */
+size_t ddt_tree_accept_sampling_workspace_size(int B, int Q, int V);
+
+int ddt_tree_accept_sampling(const void* target_logits, int dtype, int V,
+                             const float* temperature, const int32_t* node_token,
+                             const int32_t* parent, const int32_t* n_nodes, const float* coins,
+                             const float* coin_final, int B, int Q, int32_t* accept_len,
+                             int32_t* accept_nodes, int32_t* out_tokens, int32_t* next_root,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * ddt_kv_commit -- append the accepted path to the committed prefix ([P1]

@@ -148,6 +148,28 @@ def test_draft_topk_workspace_size(lib):
     assert lib.ddt_draft_topk_workspace_size(8, 15, 10, 16) == 0
 
 
+@pytest.mark.parametrize("kw,needle", [(dict(B=0), "B=0"), (dict(Q=0), "Q=0"),
+                                       (dict(Q=129), "Q=129"), (dict(B=(1 << 17) + 1, Q=128), "2^24"),
+                                       (dict(V=0), "V=0"), (dict(V=1048577), "V=1048577"),
+                                       (dict(dtype=7), "dtype=7"), (dict(null=True), "NULL"),
+                                       (dict(ws=16), "workspace")])
+def test_tree_accept_sampling_rejects(lib, kw, needle):
+    a = dict(B=8, Q=65, V=160000, dtype=ddt.DDT_BF16, ws=1 << 40, null=False)
+    a.update(kw)
+    p = ctypes.c_void_p(16)
+    coins = NULL if a["null"] else p
+    assert lib.ddt_tree_accept_sampling(p, a["dtype"], a["V"], p, p, p, p, coins, p, a["B"],
+                                        a["Q"], p, p, p, p, p, a["ws"], NULL) == ddt.DDT_EINVAL
+    assert needle in ddt.last_error()
+
+
+def test_tree_accept_sampling_workspace_size(lib):
+    n = lib.ddt_tree_accept_sampling_workspace_size(8, 65, 160000)
+    assert n >= 8 * 65 * 14 * 16  # at least 14 chunks of <= 12288 entries per row
+    assert lib.ddt_tree_accept_sampling_workspace_size(8, 129, 160000) == 0
+    assert lib.ddt_tree_accept_sampling_workspace_size(8, 65, 0) == 0
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="missing"):
         ddt.load_library(str(tmp_path / "nope.so"))

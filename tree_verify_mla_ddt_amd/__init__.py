@@ -24,7 +24,8 @@ MAX_Q = 128
 
 EXPORTED = ("ddt_version", "ddt_last_error", "ddt_tree_build",
             "ddt_verify_attn_workspace_size", "ddt_verify_attn", "ddt_tree_accept",
-            "ddt_kv_commit", "ddt_draft_topk_workspace_size", "ddt_draft_topk")
+            "ddt_kv_commit", "ddt_draft_topk_workspace_size", "ddt_draft_topk",
+            "ddt_tree_accept_sampling_workspace_size", "ddt_tree_accept_sampling")
 
 
 class DDTError(RuntimeError):
@@ -63,6 +64,11 @@ def load_library(path: str | None = None):
     lib.ddt_draft_topk_workspace_size.restype = sz
     lib.ddt_draft_topk.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, sz, vp]
     lib.ddt_draft_topk.restype = i32
+    lib.ddt_tree_accept_sampling_workspace_size.argtypes = [i32, i32, i32]
+    lib.ddt_tree_accept_sampling_workspace_size.restype = sz
+    lib.ddt_tree_accept_sampling.argtypes = ([vp, i32, i32] + [vp] * 6 + [i32, i32] + [vp] * 5
+                                             + [sz, vp])
+    lib.ddt_tree_accept_sampling.restype = i32
     if path is None:
         _lib = lib
     return lib
@@ -204,6 +210,48 @@ def tree_accept(node_token: torch.Tensor, parent: torch.Tensor, n_nodes: torch.T
         _ptr(node_token), _ptr(parent), _ptr(n_nodes), _ptr(target_argmax), B, Q,
         _ptr(out["accept_len"]), _ptr(out["accept_nodes"]), _ptr(out["out_tokens"]),
         _ptr(out["next_root"]), _stream())
+    _check(rc)
+    return out
+
+
+def tree_accept_sampling(target_logits: torch.Tensor, temperature: torch.Tensor,
+                         node_token: torch.Tensor, parent: torch.Tensor, n_nodes: torch.Tensor,
+                         coins: torch.Tensor, coin_final: torch.Tensor, out: dict | None = None,
+                         workspace: torch.Tensor | None = None) -> dict:
+    """Acceptance under temperature sampling from the target's logits [B,Q,V]
+    (bf16 or f32) at every tree node (ddt_tree_accept_sampling).  Outputs as
+    for tree_accept; coins [B,Q] and coin_final [B] are the caller's U[0,1)
+    draws."""
+    dt = target_logits.dtype
+    if dt not in (torch.bfloat16, torch.float32):
+        raise TypeError("target_logits must be bf16 or f32")
+    _dev(target_logits, "target_logits", dt, 3)
+    _dev(temperature, "temperature", torch.float32, 1)
+    _dev(node_token, "node_token", torch.int32, 2)
+    _dev(parent, "parent", torch.int32, 2)
+    _dev(n_nodes, "n_nodes", torch.int32, 1)
+    _dev(coins, "coins", torch.float32, 2)
+    _dev(coin_final, "coin_final", torch.float32, 1)
+    B, Q, V = target_logits.shape
+    if (node_token.shape != (B, Q) or parent.shape != (B, Q) or coins.shape != (B, Q)
+            or n_nodes.shape != (B,) or temperature.shape != (B,) or coin_final.shape != (B,)):
+        raise ValueError("shapes of the tree, temperature and coins must match target_logits")
+    lib = load_library()
+    dev = target_logits.device
+    if out is None:
+        out = {"accept_len": torch.empty((B,), dtype=torch.int32, device=dev),
+               "accept_nodes": torch.empty((B, Q), dtype=torch.int32, device=dev),
+               "out_tokens": torch.empty((B, Q), dtype=torch.int32, device=dev),
+               "next_root": torch.empty((B,), dtype=torch.int32, device=dev)}
+    need = int(lib.ddt_tree_accept_sampling_workspace_size(B, Q, V))
+    if workspace is None:
+        workspace = torch.empty((max(1, need),), dtype=torch.uint8, device=dev)
+    rc = lib.ddt_tree_accept_sampling(
+        _ptr(target_logits), DDT_BF16 if dt == torch.bfloat16 else DDT_F32, V, _ptr(temperature),
+        _ptr(node_token), _ptr(parent), _ptr(n_nodes), _ptr(coins), _ptr(coin_final), B, Q,
+        _ptr(out["accept_len"]), _ptr(out["accept_nodes"]), _ptr(out["out_tokens"]),
+        _ptr(out["next_root"]), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream())
     _check(rc)
     return out
 

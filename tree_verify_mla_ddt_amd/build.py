@@ -11,8 +11,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "libddt.so")
-SOURCES = ["api.hip", "draft_topk.hip", "tree_build.hip", "tree_accept.hip", "kv_commit.hip",
-           "verify_attn.hip"]
+SOURCES = ["api.hip", "draft_topk.hip", "tree_build.hip", "tree_accept.hip",
+           "tree_accept_sampling.hip", "kv_commit.hip", "verify_attn.hip"]
 ARCH = os.environ.get("DDT_OFFLOAD_ARCH", "gfx950")
 
 

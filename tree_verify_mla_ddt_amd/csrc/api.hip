@@ -180,4 +180,40 @@ int ddt_draft_topk(const void* logits, int dtype, int B, int D, int V, int K, fl
   return launch_status(e, "ddt_draft_topk");
 }
 
+size_t ddt_tree_accept_sampling_workspace_size(int B, int Q, int V) {
+  if (B < 1 || Q < 1 || Q > DDT_MAX_Q || V < 1 || V > DDT_MAX_VOCAB ||
+      (long long)B * Q > (1 << 24))
+    return 0;
+  return ddt::tree_accept_sampling_ws_bound(B, Q);
+}
+
+int ddt_tree_accept_sampling(const void* target_logits, int dtype, int V,
+                             const float* temperature, const int32_t* node_token,
+                             const int32_t* parent, const int32_t* n_nodes, const float* coins,
+                             const float* coin_final, int B, int Q, int32_t* accept_len,
+                             int32_t* accept_nodes, int32_t* out_tokens, int32_t* next_root,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  static const char* fn = "ddt_tree_accept_sampling";
+  if (B < 1) return fail(DDT_EINVAL, "%s: B=%d must be >= 1", fn, B);
+  if (Q < 1 || Q > DDT_MAX_Q) return fail(DDT_EINVAL, "%s: Q=%d outside [1, %d]", fn, Q, DDT_MAX_Q);
+  if ((long long)B * Q > (1 << 24))
+    return fail(DDT_EINVAL, "%s: B*Q=%lld exceeds 2^24 rows", fn, (long long)B * Q);
+  if (V < 1 || V > DDT_MAX_VOCAB)
+    return fail(DDT_EINVAL, "%s: V=%d outside [1, %d]", fn, V, DDT_MAX_VOCAB);
+  if (dtype != DDT_F32 && dtype != DDT_BF16)
+    return fail(DDT_EINVAL, "%s: dtype=%d is neither DDT_F32 nor DDT_BF16", fn, dtype);
+  if (!target_logits || !temperature || !node_token || !parent || !n_nodes || !coins ||
+      !coin_final || !accept_len || !accept_nodes || !out_tokens || !next_root || !workspace)
+    return fail(DDT_EINVAL, "%s: NULL array argument", fn);
+  const ddt::SamplingPlan plan = ddt::plan_tree_accept_sampling(B, Q, V, device_cu_count());
+  if (workspace_bytes < plan.ws_bytes)
+    return fail(DDT_EINVAL, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes,
+                plan.ws_bytes);
+  const hipError_t e = ddt::launch_tree_accept_sampling(
+      dtype, target_logits, V, temperature, node_token, parent, n_nodes, coins, coin_final, B, Q,
+      accept_len, accept_nodes, out_tokens, next_root, workspace, plan,
+      static_cast<hipStream_t>(stream));
+  return launch_status(e, fn);
+}
+
 }  // extern "C"

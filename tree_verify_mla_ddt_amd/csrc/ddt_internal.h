@@ -37,8 +37,8 @@ hipError_t launch_kv_commit(int32_t* req_to_slot, int max_kv, int32_t* prefix_le
 // Per-depth top-K: each (request, depth) row of logits is cut into `chunks`
 // chunks of `chunk` entries (see draft_topk.hip).
 struct TopkPlan {
-  int chunks;        // chunks per row (1..64)
-  int chunk;         // entries per chunk (multiple of 8, <= 16384)
+  int chunks;        // chunks per row (1..128)
+  int chunk;         // entries per chunk (multiple of 8, <= 12288)
   size_t ws_bytes;   // workspace bytes this plan uses
 };
 TopkPlan plan_draft_topk(int B, int D, int V, int K, int num_cu);
@@ -46,6 +46,23 @@ size_t draft_topk_ws_bound(int B, int D, int K);  // enough for any plan
 hipError_t launch_draft_topk(int dtype, const void* logits, int B, int D, int V, int K,
                              float* topk_logp, int32_t* topk_ids, void* workspace,
                              const TopkPlan& plan, hipStream_t stream);
+
+// Sampling acceptance: every (request, node) row of target logits is cut into
+// `chunks` chunks of `chunk` entries (see tree_accept_sampling.hip).
+struct SamplingPlan {
+  int chunks;        // chunks per row (1..128)
+  int chunk;         // entries per chunk (multiple of 8, <= 12288)
+  size_t ws_bytes;   // workspace bytes this plan uses
+};
+SamplingPlan plan_tree_accept_sampling(int B, int Q, int V, int num_cu);
+size_t tree_accept_sampling_ws_bound(int B, int Q);  // enough for any plan
+hipError_t launch_tree_accept_sampling(int dtype, const void* logits, int V,
+                                       const float* temperature, const int32_t* node_token,
+                                       const int32_t* parent, const int32_t* n_nodes,
+                                       const float* coins, const float* coin_final, int B, int Q,
+                                       int32_t* accept_len, int32_t* accept_nodes,
+                                       int32_t* out_tokens, int32_t* next_root, void* workspace,
+                                       const SamplingPlan& plan, hipStream_t stream);
 
 // Verify attention: rows of a request are (node, head) pairs, row = i*H + h.
 // The key range of every 128-row tile is split across a fixed grid of

@@ -21,14 +21,14 @@
 //  * draft_topk_merge_kernel (one workgroup per row): the chunks' log-sum-exps
 //    combined, their candidates ranked (or bitonic-sorted in LDS when there are
 //    more than 1024) and the first K written as log-probs and ids.
-#include "ddt_internal.h"
+#include "logit_rows.h"
 
 namespace ddt {
 namespace {
 
-constexpr int kTopkThreads = 256;
-constexpr int kMaxChunk = 12288;  // entries of one chunk (keys held in registers)
-constexpr int kMaxChunks = 128;   // chunks per row
+constexpr int kTopkThreads = kRowThreads;
+constexpr int kMaxChunk = kRowChunkMax;  // entries of one chunk (keys held in registers)
+constexpr int kMaxChunks = kRowChunksMax;
 constexpr int kMaxK = 64;
 constexpr int kCandCap = 1024;    // candidates of the threshold pass held in LDS
 
@@ -42,24 +42,6 @@ __device__ __forceinline__ uint32_t logit_key(float x) {
 }
 __device__ __forceinline__ float key_value(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
-
-__device__ __forceinline__ float to_f32(float x) { return x; }
-__device__ __forceinline__ float to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
-
-template <typename T> struct Vec16;  // 16 bytes of logits
-template <> struct Vec16<float> { static constexpr int kN = 4; };
-template <> struct Vec16<uint16_t> { static constexpr int kN = 8; };
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
 }
 
 // Candidate: key in the high word, ~index in the low word (larger = better).
@@ -373,24 +355,11 @@ __global__ __launch_bounds__(kTopkThreads) void draft_topk_merge_kernel(
 }  // namespace
 
 TopkPlan plan_draft_topk(int B, int D, int V, int K, int num_cu) {
-  TopkPlan p;
   const long long rows = (long long)B * D;
-  const int s_min = (V + kMaxChunk - 1) / kMaxChunk;
-  // About two workgroups per CU, at most 64 chunks per row unless the chunk
-  // size forces more.
-  const long long want = 2LL * (num_cu > 0 ? num_cu : 256);
-  long long s = (want + rows - 1) / rows;
-  if (s > 64) s = 64;
-  if (s < s_min) s = s_min;
-  if (s > kMaxChunks) s = kMaxChunks;
-  // No chunk may be empty: at most one chunk per 8 entries.
-  const long long s_cap = (V + 7) / 8;
-  if (s > s_cap) s = s_cap;
-  if (s < 1) s = 1;
-  int C = (int)((V + s - 1) / s);
-  C = (C + 7) / 8 * 8;
-  p.chunks = (int)((V + C - 1) / C);
-  p.chunk = C;
+  const RowChunks rc = plan_row_chunks(rows, V, num_cu);
+  TopkPlan p;
+  p.chunks = rc.chunks;
+  p.chunk = rc.chunk;
   p.ws_bytes = (size_t)rows * p.chunks * ((size_t)K * sizeof(uint64_t) + sizeof(float2));
   return p;
 }

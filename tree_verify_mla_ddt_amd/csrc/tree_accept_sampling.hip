@@ -1,0 +1,482 @@
+// tree_accept_sampling.hip -- sampling acceptance of a verified draft tree.
+//
+// The sampling-probability path of tree verification ("The Architecture of a
+// Thousand-Parameter Decision ...", "What to Build New", item 2: normalized
+// target probabilities at the tree nodes; "What to Reuse", item 3: target-only
+// tree speculative sampling from the verified distribution; item 5: the
+// temperature commit path).  Per request, with p = softmax(logits[node] / T):
+// from the root, the children of the current node are tried in index order and
+// a child with token t is accepted when coin[child] < p(t) / (1 - R), R the
+// mass of the tokens rejected so far at that node; the walk moves to the
+// accepted child.  When none is accepted the bonus token is the first entry of
+// the residual (p without the rejected tokens) whose running sum exceeds
+// coin_final times the residual mass.  A temperature that is not a finite
+// value > 0, and a node whose largest logit is not finite, make the node greedy
+// (a point mass on the lowest-index argmax).
+//
+// Two kernels on one stream:
+//  * sampling_stats_kernel, one 256-thread workgroup per (node row, chunk)
+//    (rows along the grid's x, so any batch fits):
+//    16-byte loads of the chunk into registers, its max, the lowest index
+//    holding it, and the sum of exp((x - max) / T).  This pass reads every
+//    live node's logits once and bounds the path by HBM bandwidth.
+//  * sampling_accept_kernel, one workgroup per request: combines the chunk
+//    statistics of every node, reads the one logit each child's acceptance
+//    needs, walks the tree on one wavefront (a prefix sum over the siblings
+//    gives each one's rejected mass, a ballot the first accepted), then draws
+//    the bonus token: the chunk holding the draw comes from the chunks'
+//    residual masses, and a block-wide scan of that chunk finds the entry.
+#include <float.h>
+
+#include "logit_rows.h"
+
+namespace ddt {
+namespace {
+
+constexpr int kMaxQ = 128;
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct ChunkStat {
+  float m;   // chunk max (NaN counted as -inf)
+  float s;   // sum of exp((x - m) / T) over the chunk (0 for greedy requests)
+  int amax;  // lowest row index holding m
+  int pad;
+};
+
+// exp((x - ref) / T) with k2 = log2(e) / T: exactly 1 at x == ref (also when
+// k2 overflowed), 0 for x = -inf.  x is never NaN here.
+__device__ __forceinline__ float weight(float x, float ref, float k2) {
+  const float d = x - ref;
+  return d == 0.0f ? 1.0f : exp2f(d * k2);
+}
+
+__device__ __forceinline__ float no_nan(float x) { return x != x ? -INFINITY : x; }
+
+__device__ __forceinline__ int clamp_nodes(int n, int Q) { return n < 1 ? 1 : (n > Q ? Q : n); }
+
+__device__ __forceinline__ bool sampled_temperature(float T) { return T > 0.0f && T <= FLT_MAX; }
+
+__device__ __forceinline__ float wave_excl_scan(float v, int lane) {
+  float inc = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const float t = __shfl_up(inc, o);
+    if (lane >= o) inc += t;
+  }
+  const float ex = __shfl_up(inc, 1);
+  return lane == 0 ? 0.0f : ex;
+}
+
+template <typename E>
+__global__ __launch_bounds__(kRowThreads) void sampling_stats_kernel(
+    const E* __restrict__ logits, int V, int Q, const float* __restrict__ temperature,
+    const int32_t* __restrict__ n_nodes, int S, int C, ChunkStat* __restrict__ ws) {
+  constexpr int kN = Vec16<E>::kN;
+  constexpr int kVPT = kRowChunkMax / kN / kRowThreads;
+  constexpr int kE = kVPT * kN;
+  __shared__ float s_m[kRowThreads / kWave];
+  __shared__ int s_a[kRowThreads / kWave];
+  __shared__ float s_s[kRowThreads / kWave];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = blockIdx.x;
+  const int c = blockIdx.y;
+  const int b = row / Q, node = row - b * Q;
+  if (node >= clamp_nodes(n_nodes[b], Q)) return;  // a pad slot: never read
+  const float T = temperature[b];
+  const bool sampled = sampled_temperature(T);
+  const int v0 = c * C;
+  const int n = V - v0 < C ? V - v0 : C;  // > 0: the host sizes chunks so none is empty
+  const E* src = logits + (long long)row * V + v0;
+
+  // Entries in registers, -inf where a thread has none; with 16-byte loads
+  // value j of a thread is entry (tid + 256*(j/kN))*kN + j%kN, otherwise
+  // tid + 256*j -- increasing in j either way.
+  const bool vec = ((reinterpret_cast<uintptr_t>(src) & 15) == 0) && n % kN == 0;
+  float x[kE];
+  if (vec) {
+    const int nv = n / kN;
+    uint4 raw[kVPT];
+#pragma unroll
+    for (int u = 0; u < kVPT; ++u) {
+      const int i = tid + u * kRowThreads;
+      raw[u] = make_uint4(0, 0, 0, 0);
+      if (i < nv) raw[u] = *reinterpret_cast<const uint4*>(src + (long long)i * kN);
+    }
+#pragma unroll
+    for (int u = 0; u < kVPT; ++u) {
+      const bool in = tid + u * kRowThreads < nv;
+      const E* e = reinterpret_cast<const E*>(&raw[u]);
+#pragma unroll
+      for (int j = 0; j < kN; ++j) x[u * kN + j] = in ? no_nan(to_f32(e[j])) : -INFINITY;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kE; ++j) {
+      const int i = tid + j * kRowThreads;
+      x[j] = i < n ? no_nan(to_f32(src[i])) : -INFINITY;
+    }
+  }
+  auto entry = [&](int j) -> int {
+    return vec ? (tid + kRowThreads * (j / kN)) * kN + j % kN : tid + kRowThreads * j;
+  };
+
+  // The thread's max and the first of its entries holding it.  A thread with
+  // no entries reports an index >= n, after every real one.
+  float tm = x[0];
+  int ta = entry(0);
+#pragma unroll
+  for (int j = 1; j < kE; ++j)
+    if (x[j] > tm) {
+      tm = x[j];
+      ta = entry(j);
+    }
+  float m = wave_max(tm);
+  int a = tm == m ? ta : 0x7FFFFFFF;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) a = min(a, __shfl_xor(a, o));
+  if (lane == 0) {
+    s_m[wave] = m;
+    s_a[wave] = a;
+  }
+  __syncthreads();
+  m = s_m[0];
+  a = s_a[0];
+#pragma unroll
+  for (int w = 1; w < kRowThreads / kWave; ++w) {
+    if (s_m[w] > m) {
+      m = s_m[w];
+      a = s_a[w];
+    } else if (s_m[w] == m) {
+      a = min(a, s_a[w]);
+    }
+  }
+
+  float sum = 0.0f;
+  if (sampled && m > -INFINITY && m < INFINITY) {
+    const float k2 = kLog2e / T;
+#pragma unroll
+    for (int j = 0; j < kE; ++j) sum += weight(x[j], m, k2);
+  }
+  sum = wave_sum(sum);
+  if (lane == 0) s_s[wave] = sum;
+  __syncthreads();
+  if (tid == 0) {
+    float t = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kRowThreads / kWave; ++w) t += s_s[w];
+    ChunkStat st;
+    st.m = m;
+    st.s = t;
+    st.amax = v0 + a;
+    st.pad = 0;
+    ws[(long long)row * S + c] = st;
+  }
+}
+
+template <typename E>
+__global__ __launch_bounds__(kRowThreads) void sampling_accept_kernel(
+    const E* __restrict__ logits, int V, int Q, const float* __restrict__ temperature,
+    const int32_t* __restrict__ node_token, const int32_t* __restrict__ parent,
+    const int32_t* __restrict__ n_nodes, const float* __restrict__ coins,
+    const float* __restrict__ coin_final, int S, int C, const ChunkStat* __restrict__ ws,
+    int32_t* __restrict__ accept_len, int32_t* __restrict__ accept_nodes,
+    int32_t* __restrict__ out_tokens, int32_t* __restrict__ next_root) {
+  __shared__ float s_M[kMaxQ], s_Z[kMaxQ], s_e[kMaxQ], s_coin[kMaxQ];
+  __shared__ int s_amax[kMaxQ], s_tok[kMaxQ], s_par[kMaxQ], s_greedy[kMaxQ];
+  __shared__ int s_path[kMaxQ];
+  __shared__ int s_rtok[kMaxQ];  // tokens rejected at the last node, with their masses
+  __shared__ float s_re[kMaxQ];
+  __shared__ float s_w[kRowChunksMax];
+  __shared__ int s_len, s_nrej, s_chunk, s_first, s_lastpos, s_bonus;
+  __shared__ float s_tgt;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.x;
+  const int n = clamp_nodes(n_nodes[b], Q);
+  const float T = temperature[b];
+  const bool sampled = sampled_temperature(T);
+  const float k2 = sampled ? kLog2e / T : 0.0f;
+  const E* rows = logits + (long long)b * Q * V;
+
+  // Target statistics of every node: the chunks' maxima and sums combined.
+  if (tid < n) {
+    const ChunkStat* st = ws + ((long long)b * Q + tid) * S;
+    const ChunkStat f = st[0];
+    float M = f.m, Z = f.s;
+    int am = f.amax;
+    for (int c = 1; c < S; ++c) {
+      const ChunkStat g = st[c];
+      if (g.m > M) {
+        Z = (M > -INFINITY ? Z * weight(M, g.m, k2) : 0.0f) + g.s;
+        M = g.m;
+        am = g.amax;
+      } else if (g.m > -INFINITY) {
+        Z += g.s * weight(g.m, M, k2);
+      }
+    }
+    const bool greedy = !sampled || !(M > -INFINITY && M < INFINITY);
+    s_M[tid] = M;
+    s_Z[tid] = greedy ? 1.0f : Z;
+    s_amax[tid] = am;
+    s_greedy[tid] = greedy ? 1 : 0;
+    s_tok[tid] = node_token[b * Q + tid];
+    s_par[tid] = parent[b * Q + tid];
+    s_coin[tid] = coins[b * Q + tid];
+  }
+  __syncthreads();
+  // Unnormalized target mass of each child's token at its parent.
+  if (tid < n) {
+    const int p = s_par[tid], t = s_tok[tid];
+    float e = 0.0f;
+    if (tid >= 1 && p >= 0 && p < tid && t >= 0 && t < V) {
+      if (s_greedy[p])
+        e = t == s_amax[p] ? 1.0f : 0.0f;
+      else
+        e = weight(no_nan(to_f32(rows[(long long)p * V + t])), s_M[p], k2);
+    }
+    s_e[tid] = e;
+  }
+  __syncthreads();
+
+  // The walk, on wavefront 0: lane l looks after nodes l and l + 64.
+  if (wave == 0) {
+    const uint64_t below = (1ull << lane) - 1;
+    int cur = 0, len = 1;
+    if (lane == 0) s_path[0] = 0;
+    for (;;) {
+      const int c0 = lane, c1 = lane + kWave;
+      const bool ch0 = c0 < n && c0 > cur && s_par[c0] == cur;
+      const bool ch1 = c1 < n && c1 > cur && s_par[c1] == cur;
+      const uint64_t m0 = __ballot(ch0), m1 = __ballot(ch1);
+      float e0 = ch0 ? s_e[c0] : 0.0f, e1 = ch1 ? s_e[c1] : 0.0f;
+      // A token already tried at this node (an earlier sibling with the same
+      // token) has no mass left.
+      if (e0 > 0.0f) {
+        for (uint64_t mm = m0 & below; mm; mm &= mm - 1)
+          if (s_tok[__ffsll((unsigned long long)mm) - 1] == s_tok[c0]) { e0 = 0.0f; break; }
+      }
+      if (e1 > 0.0f) {
+        for (uint64_t mm = m0; mm; mm &= mm - 1)
+          if (s_tok[__ffsll((unsigned long long)mm) - 1] == s_tok[c1]) { e1 = 0.0f; break; }
+        if (e1 > 0.0f)
+          for (uint64_t mm = m1 & below; mm; mm &= mm - 1)
+            if (s_tok[kWave + __ffsll((unsigned long long)mm) - 1] == s_tok[c1]) { e1 = 0.0f; break; }
+      }
+      // Mass of the earlier siblings, in index order.
+      const float r0 = wave_excl_scan(e0, lane);
+      const float tot0 = __shfl(r0 + e0, kWave - 1);
+      const float r1 = tot0 + wave_excl_scan(e1, lane);
+      bool a0, a1;
+      if (s_greedy[cur]) {
+        a0 = e0 > 0.0f;
+        a1 = e1 > 0.0f;
+      } else {
+        // coin < e / (Z - r), written without the division.
+        const float Z = s_Z[cur];
+        a0 = e0 > 0.0f && s_coin[c0] * (Z - r0) < e0;
+        a1 = e1 > 0.0f && s_coin[c1] * (Z - r1) < e1;
+      }
+      const uint64_t acc0 = __ballot(a0), acc1 = __ballot(a1);
+      int next = -1;
+      if (acc0)
+        next = __ffsll((unsigned long long)acc0) - 1;
+      else if (acc1)
+        next = kWave + __ffsll((unsigned long long)acc1) - 1;
+      if (next < 0) {
+        // Every child with mass was tried and rejected: list them for the bonus draw.
+        const uint64_t rj0 = __ballot(e0 > 0.0f), rj1 = __ballot(e1 > 0.0f);
+        const int base1 = __popcll(rj0);
+        if (e0 > 0.0f) {
+          const int k = __popcll(rj0 & below);
+          s_rtok[k] = s_tok[c0];
+          s_re[k] = e0;
+        }
+        if (e1 > 0.0f) {
+          const int k = base1 + __popcll(rj1 & below);
+          s_rtok[k] = s_tok[c1];
+          s_re[k] = e1;
+        }
+        if (lane == 0) {
+          s_nrej = base1 + __popcll(rj1);
+          s_len = len;
+        }
+        break;
+      }
+      if (lane == 0) s_path[len] = next;
+      ++len;
+      cur = next;  // strictly increasing, so the walk ends within n steps
+    }
+  }
+  if (tid == 0) {
+    s_first = 0x7FFFFFFF;
+    s_lastpos = -1;
+  }
+  __syncthreads();
+
+  const int len = s_len, cur = s_path[len - 1];
+  if (s_greedy[cur]) {
+    if (tid == 0) s_bonus = s_amax[cur];
+  } else {
+    // The bonus token from the residual distribution at `cur`.
+    const int nrej = s_nrej;
+    const float M = s_M[cur];
+    const ChunkStat* st = ws + ((long long)b * Q + cur) * S;
+    for (int c = tid; c < S; c += kRowThreads) {
+      const ChunkStat g = st[c];
+      const float mass = g.m > -INFINITY ? g.s * weight(g.m, M, k2) : 0.0f;
+      float w = mass;
+      for (int j = 0; j < nrej; ++j) {
+        const int t = s_rtok[j];
+        if (t >= c * C && t < c * C + C) w -= s_re[j];
+      }
+      // What is left below the rounding of the chunk's own sum is nothing.
+      s_w[c] = w > 1e-6f * mass ? w : 0.0f;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      float Zr = 0.0f;
+      for (int c = 0; c < S; ++c) Zr += s_w[c];
+      const float target = coin_final[b] * Zr;
+      float cum = 0.0f;
+      int ch = -1, last = -1;
+      for (int c = 0; c < S; ++c) {
+        if (!(s_w[c] > 0.0f)) continue;
+        last = c;
+        if (cum + s_w[c] > target) {
+          ch = c;
+          break;
+        }
+        cum += s_w[c];
+      }
+      // No crossing (a draw >= 1, NaN, or rounding): the last entry left.
+      s_chunk = ch >= 0 ? ch : last;
+      s_tgt = ch >= 0 ? target - cum : INFINITY;
+    }
+    __syncthreads();
+    const int ch = s_chunk;
+    if (ch < 0) {
+      if (tid == 0) s_bonus = s_amax[cur];  // no residual mass at all
+    } else {
+      // Thread t scans a run of consecutive entries of the chunk.
+      const int v0 = ch * C;
+      const int nc = V - v0 < C ? V - v0 : C;
+      const int run = (nc + kRowThreads - 1) / kRowThreads;
+      const int lo = min(nc, tid * run), hi = min(nc, lo + run);
+      const E* src = rows + (long long)cur * V + v0;
+      auto resid = [&](int i) -> float {
+        const int v = v0 + i;
+        for (int j = 0; j < nrej; ++j)
+          if (s_rtok[j] == v) return 0.0f;
+        return weight(no_nan(to_f32(src[i])), M, k2);
+      };
+      float sum = 0.0f;
+      int lastpos = -1;
+      for (int i = lo; i < hi; ++i) {
+        const float r = resid(i);
+        if (r > 0.0f) {
+          sum += r;
+          lastpos = v0 + i;
+        }
+      }
+      // Exclusive scan of the runs' sums over the block.
+      float inc = sum;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const float t = __shfl_up(inc, o);
+        if (lane >= o) inc += t;
+      }
+      if (lane == kWave - 1) s_w[wave] = inc;  // the chunk masses are no longer needed
+      __syncthreads();
+      float excl = __shfl_up(inc, 1);
+      if (lane == 0) excl = 0.0f;
+      for (int w = 0; w < wave; ++w) excl += s_w[w];
+      const float tgt = s_tgt;
+      // The first run whose end passes the target holds the draw; its own
+      // running sum ends at exactly the value tested here.
+      if (excl + sum > tgt) atomicMin(&s_first, tid);
+      if (lastpos >= 0) atomicMax(&s_lastpos, lastpos);
+      __syncthreads();
+      if (tid == s_first) {
+        float part = 0.0f;
+        for (int i = lo; i < hi; ++i) {
+          const float r = resid(i);
+          if (r > 0.0f) {
+            part += r;
+            if (excl + part > tgt) {
+              s_bonus = v0 + i;
+              break;
+            }
+          }
+        }
+      } else if (tid == 0 && s_first == 0x7FFFFFFF) {
+        s_bonus = s_lastpos >= 0 ? s_lastpos : s_amax[cur];
+      }
+    }
+  }
+  __syncthreads();
+
+  const int bonus = s_bonus;
+  if (tid < Q) {
+    accept_nodes[b * Q + tid] = tid < len ? s_path[tid] : -1;
+    int o = -1;
+    if (tid < len - 1)
+      o = s_tok[s_path[tid + 1]];
+    else if (tid == len - 1)
+      o = bonus;
+    out_tokens[b * Q + tid] = o;
+  }
+  if (tid == 0) {
+    accept_len[b] = len;
+    next_root[b] = bonus;
+  }
+}
+
+}  // namespace
+
+SamplingPlan plan_tree_accept_sampling(int B, int Q, int V, int num_cu) {
+  const RowChunks rc = plan_row_chunks((long long)B * Q, V, num_cu);
+  SamplingPlan p;
+  p.chunks = rc.chunks;
+  p.chunk = rc.chunk;
+  p.ws_bytes = (size_t)B * Q * rc.chunks * sizeof(ChunkStat);
+  return p;
+}
+
+size_t tree_accept_sampling_ws_bound(int B, int Q) {
+  return (size_t)B * Q * kRowChunksMax * sizeof(ChunkStat);
+}
+
+hipError_t launch_tree_accept_sampling(int dtype, const void* logits, int V,
+                                       const float* temperature, const int32_t* node_token,
+                                       const int32_t* parent, const int32_t* n_nodes,
+                                       const float* coins, const float* coin_final, int B, int Q,
+                                       int32_t* accept_len, int32_t* accept_nodes,
+                                       int32_t* out_tokens, int32_t* next_root, void* workspace,
+                                       const SamplingPlan& plan, hipStream_t stream) {
+  ChunkStat* ws = static_cast<ChunkStat*>(workspace);
+  const dim3 grid1(B * Q, plan.chunks);
+  if (dtype == 1)
+    hipLaunchKernelGGL(sampling_stats_kernel<uint16_t>, grid1, dim3(kRowThreads), 0, stream,
+                       static_cast<const uint16_t*>(logits), V, Q, temperature, n_nodes,
+                       plan.chunks, plan.chunk, ws);
+  else
+    hipLaunchKernelGGL(sampling_stats_kernel<float>, grid1, dim3(kRowThreads), 0, stream,
+                       static_cast<const float*>(logits), V, Q, temperature, n_nodes,
+                       plan.chunks, plan.chunk, ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (dtype == 1)
+    hipLaunchKernelGGL(sampling_accept_kernel<uint16_t>, dim3(B), dim3(kRowThreads), 0, stream,
+                       static_cast<const uint16_t*>(logits), V, Q, temperature, node_token,
+                       parent, n_nodes, coins, coin_final, plan.chunks, plan.chunk, ws,
+                       accept_len, accept_nodes, out_tokens, next_root);
+  else
+    hipLaunchKernelGGL(sampling_accept_kernel<float>, dim3(B), dim3(kRowThreads), 0, stream,
+                       static_cast<const float*>(logits), V, Q, temperature, node_token, parent,
+                       n_nodes, coins, coin_final, plan.chunks, plan.chunk, ws, accept_len,
+                       accept_nodes, out_tokens, next_root);
+  return hipGetLastError();
+}
+
+}  // namespace ddt
