@@ -78,6 +78,6 @@ def test_shapes_ties_and_masks(dtype, V, K):
 
 
 def test_equal_logits_and_signed_zero():
-    x = torch.zeros(1, 2, 3000)
+    x = torch.zeros(1, 2, 3000, dtype=torch.float32)
     x[0, 1, ::2] = -0.0
     check(x, 16)

@@ -25,7 +25,16 @@ import torch
 
 import oracle
 
-torch.set_default_dtype(torch.float64)
+
+
+@pytest.fixture(autouse=True)
+def _float64_default():
+    """Float64 as torch's default dtype inside this module's tests only (set at
+    import time it would leak into every module collected after this one)."""
+    prev = torch.get_default_dtype()
+    torch.set_default_dtype(torch.float64)
+    yield
+    torch.set_default_dtype(prev)
 
 
 def f32(x):
