@@ -280,6 +280,46 @@ class StepRunner:
                 "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "vocab": wl.vocab, "K": wl.K,
                 "D": wl.D}
 
+    def sampling_stats(self, steps=200):
+        """ddt_tree_accept_sampling on this workload's drafted tree at temperature 1:
+        target logits N(0, 2) over the workload's vocabulary at every tree node (bf16,
+        or fp32 for the fp32 workload), with each node's lowest-index child's token set
+        to 16 (about 0.9 of the node's mass at V = 160000) so that drafts are accepted;
+        timed by graph replays.  The
+        statistics pass reads every live node's logits once, so the roofline is HBM
+        bytes."""
+        torch, ddt, wl = self.torch, self.ddt, self.wl
+        dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+        g = torch.Generator(device="cuda").manual_seed(12)
+        B, Q, V = wl.B, wl.Q, wl.vocab
+        logits = (torch.randn((B, Q, V), generator=g, device="cuda") * 2).to(dt)
+        ht = self.host_tree
+        for b in range(B):
+            seen = set()
+            for c in range(1, int(ht["n_nodes"][b])):
+                p = int(ht["parent"][b, c])
+                if p not in seen:
+                    seen.add(p)
+                    logits[b, p, int(ht["node_token"][b, c])] = 16.0
+        temp = torch.ones((B,), dtype=torch.float32, device="cuda")
+        coins = torch.rand((B, Q), generator=g, device="cuda")
+        cfin = torch.rand((B,), generator=g, device="cuda")
+        out = {k: torch.empty_like(v) for k, v in self.acc.items()}
+        ws = torch.empty((max(1, int(ddt.load_library().ddt_tree_accept_sampling_workspace_size(
+            B, Q, V))),), dtype=torch.uint8, device="cuda")
+        tr = self.tree
+        fn = lambda: ddt.tree_accept_sampling(logits, temp, tr["node_token"], tr["parent"],
+                                              tr["n_nodes"], coins, cfin, out=out, workspace=ws)
+        gr = self.capture(fn)
+        ms = self.time_graph(gr, steps, 10)
+        live = int(ht["n_nodes"][:B].sum())
+        nbytes = live * V * logits.element_size() + B * Q * 4 * 4
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        mean_len = float(out["accept_len"].float().mean())
+        return {"ms": round(ms, 5), "bytes": nbytes, "gbs": round(gbs, 1),
+                "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "vocab": V,
+                "mean_accept_len": round(mean_len, 3)}
+
     def roofline(self, attn_ms, name):
         wl = self.wl
         peak = PEAK_F32_TFLOPS if wl.dtype == "f32" else PEAK_BF16_TFLOPS
@@ -393,6 +433,7 @@ def main():
         "step_eager_ms": round(ms_eager, 5),
         "kv_commit_step_ms": round(runner.commit_ms(), 5),
         "draft_topk": runner.topk_stats(),
+        "accept_sampling": runner.sampling_stats(),
     }
 
     extras = {}
@@ -410,7 +451,8 @@ def main():
                             "attn_frac_peak": rf["frac"], "attn_hbm_gbs": rf["hbm_gbs_algorithmic"],
                             "traffic": rf["traffic"], "dtype": r.wl.dtype,
                             "kv_commit_step_ms": round(r.commit_ms(), 5),
-                            "draft_topk": r.topk_stats()}
+                            "draft_topk": r.topk_stats(),
+                            "accept_sampling": r.sampling_stats()}
             log(f"[bench] {name}: step {ms_s * 1e3:.1f} us, attention {ms_a * 1e3:.1f} us = "
                 f"{rf['achieved']:.1f} TFLOP/s ({100 * rf['frac']:.1f}% of {rf['peak']})")
             del r, gs, ga

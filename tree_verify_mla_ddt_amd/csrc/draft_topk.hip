@@ -83,20 +83,20 @@ __device__ __forceinline__ void rank_select(const uint64_t* a, int nc, int kk, u
 }
 
 template <typename T>
-__global__ __launch_bounds__(kTopkThreads) void draft_topk_partial_kernel(
+__global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 8 : 5))) void draft_topk_partial_kernel(
     const T* __restrict__ logits, int V, int K, int S, int C, uint64_t* __restrict__ ws_cand,
     float2* __restrict__ ws_ms) {
   constexpr int kN = Vec16<T>::kN;
   constexpr int kVPT = kMaxChunk / kN / kTopkThreads;  // 16-byte loads per thread at most
-  constexpr int kE = kVPT * kN;                         // keys per thread at most
-  static_assert(kE * kTopkThreads == kMaxChunk, "chunk tiling");
+  static_assert(kVPT * kN * kTopkThreads == kMaxChunk, "chunk tiling");
+  constexpr float kLog2e = 1.4426950408889634f;
   __shared__ uint64_t s_cand[kCandCap];
-  __shared__ uint32_t s_wmax[kTopkThreads];  // each wave's thread maxima, sorted
   __shared__ uint32_t s_hist[256];
-  __shared__ float s_red[kTopkThreads / kWave];
+  __shared__ float s_max[kTopkThreads / kWave];
+  __shared__ float s_sum[kTopkThreads / kWave];
+  __shared__ uint32_t s_wtau[kTopkThreads / kWave];
   __shared__ int s_pick[2];  // digit, count above it
   __shared__ int s_cnt;
-  __shared__ uint32_t s_tau;
   __shared__ int s_wties[kTopkThreads / kWave];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -106,67 +106,60 @@ __global__ __launch_bounds__(kTopkThreads) void draft_topk_partial_kernel(
   const int n = V - v0 < C ? V - v0 : C;  // > 0: the host sizes S so every chunk has entries
   const T* src = logits + row * (long long)V + v0;
 
-  // The chunk's keys stay in registers (0 = no entry; every real key is > 0).
-  // With 16-byte loads key j of a thread is entry (tid + 256*(j/kN))*kN + j%kN,
-  // otherwise entry tid + 256*j.
-  const bool vec = ((reinterpret_cast<uintptr_t>(src) & 15) == 0) && n % kN == 0;
-  uint32_t key[kE];
-  if (vec) {
-    const int nv = n / kN;
-    uint4 raw[kVPT];
+  // The chunk stays in registers as loaded (entry j of group u of a thread is
+  // chunk entry (tid + 256*u)*kN + j, -inf where the chunk has none).
+  constexpr int kW = kVPT * 4;
+  uint32_t w[kW];
+  load_chunk_words<T, kVPT>(src, n, tid, w);
+  auto val = [&](int u, int j) -> float { return word_entry<T>(w[4 * u + j / (kN / 4)], j); };
+  auto entry = [&](int u, int j) -> int { return (tid + kTopkThreads * u) * kN + j; };
+  auto refresh = [&]() { mark_rewritten<kW>(w); };
+
+  // The thread's max tm and sum ts of exp(x - tm), in one pass over its loads
+  // (the sum is rescaled when a load raises the max).  A NaN never wins a
+  // comparison, so it counts as -inf for the max; in the sum it turns ts into
+  // NaN, and only then does the thread sum again, skipping NaN entries.
+  float tm = -INFINITY, ts = 0.0f;
 #pragma unroll
-    for (int u = 0; u < kVPT; ++u) {
-      const int i = tid + u * kTopkThreads;
-      raw[u] = make_uint4(0, 0, 0, 0);
-      if (i < nv) raw[u] = *reinterpret_cast<const uint4*>(src + (long long)i * kN);
+  for (int u = 0; u < kVPT; ++u) {
+    float lm = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kN; ++j) {
+      const float x = val(u, j);
+      lm = x > lm ? x : lm;
     }
-#pragma unroll
-    for (int u = 0; u < kVPT; ++u) {
-      const bool in = tid + u * kTopkThreads < nv;
-      const T* e = reinterpret_cast<const T*>(&raw[u]);
-#pragma unroll
-      for (int j = 0; j < kN; ++j) key[u * kN + j] = in ? logit_key(to_f32(e[j])) : 0u;
+    if (lm > tm) {
+      ts *= __builtin_amdgcn_exp2f((tm - lm) * kLog2e);  // 0 while tm is -inf
+      tm = lm;
     }
-  } else {
+    if (tm > -INFINITY) {
+      const float mk = tm * kLog2e;
 #pragma unroll
-    for (int j = 0; j < kE; ++j) {
-      const int i = tid + j * kTopkThreads;
-      key[j] = i < n ? logit_key(to_f32(src[i])) : 0u;
+      for (int j = 0; j < kN; ++j) ts += __builtin_amdgcn_exp2f(__builtin_fmaf(val(u, j), kLog2e, -mk));
     }
   }
-  auto entry = [&](int j) -> int {
-    return vec ? (tid + kTopkThreads * (j / kN)) * kN + j % kN : tid + kTopkThreads * j;
-  };
-
-  uint32_t tmax = 0;
+  refresh();
+  if (ts != ts) {
+    ts = 0.0f;
+    const float mk = tm * kLog2e;
 #pragma unroll
-  for (int j = 0; j < kE; ++j) tmax = key[j] > tmax ? key[j] : tmax;
-  float m = tmax != 0 ? key_value(tmax) : -INFINITY;
-  m = wave_max(m);
-  if (lane == 0) s_red[wave] = m;
-  __syncthreads();
-  m = s_red[0];
+    for (int u = 0; u < kVPT; ++u)
 #pragma unroll
-  for (int w = 1; w < kTopkThreads / kWave; ++w) m = fmaxf(m, s_red[w]);
-  __syncthreads();
-
-  // Sum of exp(x - max) over the chunk (0 when the chunk is all -inf).
-  float sum = 0.0f;
-  if (m > -INFINITY) {
-#pragma unroll
-    for (int j = 0; j < kE; ++j)
-      if (key[j] != 0) sum += __expf(key_value(key[j]) - m);
+      for (int j = 0; j < kN; ++j) {
+        const float x = val(u, j);
+        if (x == x) ts += __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -mk));
+      }
   }
-  sum = wave_sum(sum);
-  if (lane == 0) s_red[wave] = sum;
+  const float wm = wave_max(tm);
+  if (lane == 0) s_max[wave] = wm;
 
-  // Threshold: the kk-th largest of the 256 threads' maxima bounds the chunk's
-  // kk-th largest key from below (kk threads hold a key at least that large),
-  // so the keys at or above it are a superset of the answer, usually a few more.
-  // Each wave sorts its maxima with a lane-exchange bitonic network; one thread
-  // merges the four sorted lists far enough.
+  // Threshold: each wave sorts its threads' maxima (lane-exchange bitonic
+  // network, descending); the kk-th largest of a wave has at least kk entries
+  // at or above it, so the largest of the four is a lower bound of the chunk's
+  // kk-th largest entry, and the entries at or above it -- at most a few times
+  // kk on ordinary rows -- hold the chunk's answer.
   const int kk = K < n ? K : n;
-  uint32_t v = tmax;
+  uint32_t v = logit_key(tm);
 #pragma unroll
   for (int size = 2; size <= kWave; size <<= 1) {
 #pragma unroll
@@ -177,69 +170,74 @@ __global__ __launch_bounds__(kTopkThreads) void draft_topk_partial_kernel(
       v = (lower == desc) ? (v > o ? v : o) : (v < o ? v : o);
     }
   }
-  s_wmax[tid] = v;
+  if (lane == kk - 1) s_wtau[wave] = v;
   if (tid == 0) s_cnt = 0;
+  __syncthreads();
+  float M = s_max[0];
+  uint32_t tau = s_wtau[0];
+#pragma unroll
+  for (int w = 1; w < kTopkThreads / kWave; ++w) {
+    M = fmaxf(M, s_max[w]);
+    tau = s_wtau[w] > tau ? s_wtau[w] : tau;
+  }
+  // The thread's share of the chunk's sum of exp(x - M) (M >= tm).
+  float part = tm > -INFINITY ? ts * __builtin_amdgcn_exp2f((tm - M) * kLog2e) : 0.0f;
+  part = wave_sum(part);
+  if (lane == 0) s_sum[wave] = part;
+
+  // Fast path (threshold above -inf): threads whose max reaches it gather their
+  // entries at or above it; NaN and missing entries never qualify.
+  refresh();
+  const bool fast = tau > logit_key(-INFINITY);
+  const float tau_f = key_value(tau);
+  if (fast && tm >= tau_f) {
+#pragma unroll
+    for (int u = 0; u < kVPT; ++u)
+#pragma unroll
+      for (int j = 0; j < kN; ++j) {
+        const float x = val(u, j);
+        if (x >= tau_f) {
+          const int at = atomicAdd(&s_cnt, 1);
+          if (at < kCandCap) s_cand[at] = cand(logit_key(x), v0 + entry(u, j));
+        }
+      }
+  }
   __syncthreads();
   if (tid == 0) {
     float t = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kTopkThreads / kWave; ++w) t += s_red[w];
-    ws_ms[row * S + c] = make_float2(m, t);
+    for (int w = 0; w < kTopkThreads / kWave; ++w) t += s_sum[w];
+    ws_ms[row * S + c] = make_float2(M, t);
   }
-  {
-    // The kk-th largest of the four sorted lists: the value whose count of
-    // larger values is below kk and whose count of larger-or-equal values
-    // reaches kk (binary searches in each list).
-    int gt = 0, ge = 0;
-#pragma unroll
-    for (int w = 0; w < kTopkThreads / kWave; ++w) {
-      const uint32_t* L = s_wmax + w * kWave;
-      int lo = 0, hi = kWave;  // first position with L[pos] <= v (descending list)
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (L[mid] > v) lo = mid + 1; else hi = mid;
-      }
-      gt += lo;
-      int lo2 = lo, hi2 = kWave;  // first position with L[pos] < v
-      while (lo2 < hi2) {
-        const int mid = (lo2 + hi2) >> 1;
-        if (L[mid] >= v) lo2 = mid + 1; else hi2 = mid;
-      }
-      ge += lo2;
-    }
-    if (gt < kk && ge >= kk) s_tau = v;  // every such thread holds the same value
-  }
-  __syncthreads();
-  const uint32_t tau = s_tau;
-#pragma unroll
-  for (int j = 0; j < kE; ++j) {
-    if (key[j] >= tau && key[j] != 0) {
-      const int at = atomicAdd(&s_cnt, 1);
-      if (at < kCandCap) s_cand[at] = cand(key[j], v0 + entry(j));
-    }
-  }
-  __syncthreads();
   uint64_t* out = ws_cand + (row * S + c) * (long long)K;
-  const int nc = s_cnt;
+  const int nc = fast ? s_cnt : kCandCap + 1;
   if (nc <= kCandCap) {
     rank_select(s_cand, nc, kk, out);
     for (int j = kk + tid; j < K; j += kTopkThreads) out[j] = 0;
     return;
   }
 
-  // Many keys at the threshold (wide ties): radix selection of the kk-th
-  // largest key over the registers, most significant digit first: `need` counts
-  // how many keys equal to or above the selected prefix are still wanted.
+  // Slow path (the threshold is -inf, or many entries tie at it): radix
+  // selection of the kk-th largest key over the registers, most significant
+  // digit first; `need` counts how many keys equal to or above the selected
+  // prefix are still wanted.  Key 0 marks a missing entry (every real key is > 0).
+  refresh();
+  auto key_at = [&](int u, int j) -> uint32_t {
+    return entry(u, j) < n ? logit_key(val(u, j)) : 0u;
+  };
   uint32_t prefix = 0, mask = 0;
   int need = kk;
   for (int shift = 24; shift >= 0; shift -= 8) {
+    refresh();  // keys are formed again in every pass, never kept
     s_hist[tid] = 0;
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < kE; ++j) {
-      const uint32_t k = key[j];
-      if (k != 0 && (k & mask) == prefix) atomicAdd(&s_hist[(k >> shift) & 255u], 1u);
-    }
+    for (int u = 0; u < kVPT; ++u)
+#pragma unroll
+      for (int j = 0; j < kN; ++j) {
+        const uint32_t k = key_at(u, j);
+        if (k != 0 && (k & mask) == prefix) atomicAdd(&s_hist[(k >> shift) & 255u], 1u);
+      }
     __syncthreads();
     if (wave == 0) {
       // Bins 255..0 as 4 per lane, lane 0 holding the top ones.
@@ -282,9 +280,14 @@ __global__ __launch_bounds__(kTopkThreads) void draft_topk_partial_kernel(
   // taken (the lowest indices), with every key above it.
   if (tid == 0) s_cnt = 0;
   __syncthreads();
+  refresh();
 #pragma unroll
-  for (int j = 0; j < kE; ++j)
-    if (key[j] > prefix) out[atomicAdd(&s_cnt, 1)] = cand(key[j], v0 + entry(j));
+  for (int u = 0; u < kVPT; ++u)
+#pragma unroll
+    for (int j = 0; j < kN; ++j) {
+      const uint32_t k = key_at(u, j);
+      if (k > prefix) out[atomicAdd(&s_cnt, 1)] = cand(k, v0 + entry(u, j));
+    }
   // Ties in index order: the chunk is read again (from the caches) 256
   // consecutive entries at a time.
   int taken = 0;
@@ -321,16 +324,32 @@ __global__ __launch_bounds__(kTopkThreads) void draft_topk_merge_kernel(
   while (P < n) P <<= 1;
   const uint64_t* src = ws_cand + row * (long long)S * K;
   for (int i = tid; i < P; i += kTopkThreads) s_c[i] = i < n ? src[i] : 0ull;
+  // Combined log-sum-exp of the chunks (each chunk: max, sum of exp(x - max)),
+  // one chunk per thread.
+  static_assert(kMaxChunks <= kTopkThreads, "one chunk per thread");
+  __shared__ float s_rm[kTopkThreads / kWave];
+  __shared__ float s_rs[kTopkThreads / kWave];
+  const int lane = tid & 63, wave = tid >> 6;
+  float cm = -INFINITY, cs = 0.0f;
+  if (tid < S) {
+    const float2 ms = ws_ms[row * S + tid];
+    cm = ms.x;
+    cs = ms.y;
+  }
+  float M = wave_max(cm);
+  if (lane == 0) s_rm[wave] = M;
+  __syncthreads();
+  M = s_rm[0];
+#pragma unroll
+  for (int w = 1; w < kTopkThreads / kWave; ++w) M = fmaxf(M, s_rm[w]);
+  float part = cm > -INFINITY ? cs * __expf(cm - M) : 0.0f;
+  part = wave_sum(part);
+  if (lane == 0) s_rs[wave] = part;
+  __syncthreads();
   if (tid == 0) {
-    // Combined log-sum-exp of the chunks (each chunk: max, sum of exp(x - max)).
-    float M = -INFINITY;
-    for (int c = 0; c < S; ++c) M = fmaxf(M, ws_ms[row * S + c].x);
     float tot = 0.0f;
-    if (M > -INFINITY)
-      for (int c = 0; c < S; ++c) {
-        const float2 ms = ws_ms[row * S + c];
-        if (ms.x > -INFINITY) tot += ms.y * __expf(ms.x - M);
-      }
+#pragma unroll
+    for (int w = 0; w < kTopkThreads / kWave; ++w) tot += s_rs[w];
     s_lse = M > -INFINITY ? M + __logf(tot) : -INFINITY;
   }
   __syncthreads();

@@ -46,6 +46,64 @@ template <typename T> struct Vec16;  // 16 bytes of logits
 template <> struct Vec16<float> { static constexpr int kN = 4; };
 template <> struct Vec16<uint16_t> { static constexpr int kN = 8; };
 
+// The 32-bit word holding entries i0 .. i0 + 4/sizeof(T) - 1 of a chunk of n
+// entries (-inf for entries past n).
+__device__ __forceinline__ uint32_t load_word(const float* src, int i0, int n) {
+  return i0 < n ? __float_as_uint(src[i0]) : 0xFF800000u;
+}
+__device__ __forceinline__ uint32_t load_word(const uint16_t* src, int i0, int n) {
+  const uint32_t lo = i0 < n ? src[i0] : 0xFF80u;
+  const uint32_t hi = i0 + 1 < n ? src[i0 + 1] : 0xFF80u;
+  return lo | (hi << 16);
+}
+
+// A thread's share of a chunk of n entries, kept in registers as loaded, in
+// 32-bit words: entry j of 16-byte group u is chunk entry (tid + 256*u)*kN + j
+// (kN entries per group), or -inf where the chunk has none.  16-byte loads when
+// the chunk is aligned and a whole number of groups, else word by word.
+template <typename T, int kVPT>
+__device__ __forceinline__ void load_chunk_words(const T* src, int n, int tid,
+                                                 uint32_t (&w)[kVPT * 4]) {
+  constexpr int kN = Vec16<T>::kN;
+  constexpr uint32_t kFill = kN == 8 ? 0xFF80FF80u : 0xFF800000u;
+  if (((reinterpret_cast<uintptr_t>(src) & 15) == 0) && n % kN == 0) {
+    const int nv = n / kN;
+#pragma unroll
+    for (int u = 0; u < kVPT; ++u) {
+      const int i = tid + u * kRowThreads;
+      uint4 r = make_uint4(kFill, kFill, kFill, kFill);
+      if (i < nv) r = *reinterpret_cast<const uint4*>(src + (long long)i * kN);
+      w[4 * u] = r.x;
+      w[4 * u + 1] = r.y;
+      w[4 * u + 2] = r.z;
+      w[4 * u + 3] = r.w;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < kVPT * 4; ++q) {
+      const int u = q >> 2;
+      w[q] = load_word(src, (tid + u * kRowThreads) * kN + (q & 3) * (kN / 4), n);
+    }
+  }
+}
+
+// Entry j of a 16-byte group, from the word that holds it.
+template <typename T> __device__ __forceinline__ float word_entry(uint32_t word, int j);
+template <> __device__ __forceinline__ float word_entry<float>(uint32_t word, int) {
+  return __uint_as_float(word);
+}
+template <> __device__ __forceinline__ float word_entry<uint16_t>(uint32_t word, int j) {
+  return __uint_as_float((j & 1) ? (word & 0xFFFF0000u) : (word << 16));
+}
+
+// Marks the words as rewritten (an empty asm statement), so that a later pass
+// converts them again instead of the compiler keeping every entry as a float.
+template <int kW>
+__device__ __forceinline__ void mark_rewritten(uint32_t (&w)[kW]) {
+#pragma unroll
+  for (int q = 0; q < kW; ++q) asm volatile("" : "+v"(w[q]));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

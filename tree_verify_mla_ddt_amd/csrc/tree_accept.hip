@@ -23,6 +23,7 @@ __global__ __launch_bounds__(kWave) void tree_accept_kernel(
     int Q, int32_t* __restrict__ accept_len, int32_t* __restrict__ accept_nodes,
     int32_t* __restrict__ out_tokens, int32_t* __restrict__ next_root) {
   __shared__ int32_t s_path[kMaxQ];
+  __shared__ int32_t s_tok[kMaxQ];  // s_tok[k]: token of path node k+1 (= the target's token at node k)
   const int b = blockIdx.x;
   const int lane = threadIdx.x;
   const size_t base = (size_t)b * Q;
@@ -54,7 +55,10 @@ __global__ __launch_bounds__(kWave) void tree_accept_kernel(
     if (b0 == 0 && b1 == 0) break;
     const int nxt = b0 ? (__ffsll((unsigned long long)b0) - 1)
                        : (kWave + __ffsll((unsigned long long)b1) - 1);
-    if (lane == 0) s_path[len] = nxt;
+    if (lane == 0) {
+      s_path[len] = nxt;
+      s_tok[len - 1] = want;  // the matched child carries the wanted token
+    }
     ++len;
     cur = nxt;
   }
@@ -63,7 +67,7 @@ __global__ __launch_bounds__(kWave) void tree_accept_kernel(
   for (int i = lane; i < Q; i += kWave) {
     accept_nodes[base + i] = i < len ? s_path[i] : -1;
     int t = -1;
-    if (i + 1 < len) t = node_token[base + s_path[i + 1]];
+    if (i + 1 < len) t = s_tok[i];
     else if (i + 1 == len) t = want;  // bonus token
     out_tokens[base + i] = t;
   }

@@ -68,12 +68,13 @@ __device__ __forceinline__ float wave_excl_scan(float v, int lane) {
 }
 
 template <typename E>
-__global__ __launch_bounds__(kRowThreads) void sampling_stats_kernel(
+__global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(sizeof(E) == 2 ? 8 : 5)))
+void sampling_stats_kernel(
     const E* __restrict__ logits, int V, int Q, const float* __restrict__ temperature,
     const int32_t* __restrict__ n_nodes, int S, int C, ChunkStat* __restrict__ ws) {
   constexpr int kN = Vec16<E>::kN;
   constexpr int kVPT = kRowChunkMax / kN / kRowThreads;
-  constexpr int kE = kVPT * kN;
+  constexpr int kW = kVPT * 4;
   __shared__ float s_m[kRowThreads / kWave];
   __shared__ int s_a[kRowThreads / kWave];
   __shared__ float s_s[kRowThreads / kWave];
@@ -85,90 +86,101 @@ __global__ __launch_bounds__(kRowThreads) void sampling_stats_kernel(
   if (node >= clamp_nodes(n_nodes[b], Q)) return;  // a pad slot: never read
   const float T = temperature[b];
   const bool sampled = sampled_temperature(T);
+  // log2(e) / T, kept finite so that (x - ref) * k2 is 0 at x == ref for any T.
+  const float k2 = sampled ? fminf(kLog2e / T, FLT_MAX) : 0.0f;
   const int v0 = c * C;
   const int n = V - v0 < C ? V - v0 : C;  // > 0: the host sizes chunks so none is empty
   const E* src = logits + (long long)row * V + v0;
 
-  // Entries in registers, -inf where a thread has none; with 16-byte loads
-  // value j of a thread is entry (tid + 256*(j/kN))*kN + j%kN, otherwise
-  // tid + 256*j -- increasing in j either way.
-  const bool vec = ((reinterpret_cast<uintptr_t>(src) & 15) == 0) && n % kN == 0;
-  float x[kE];
-  if (vec) {
-    const int nv = n / kN;
-    uint4 raw[kVPT];
-#pragma unroll
-    for (int u = 0; u < kVPT; ++u) {
-      const int i = tid + u * kRowThreads;
-      raw[u] = make_uint4(0, 0, 0, 0);
-      if (i < nv) raw[u] = *reinterpret_cast<const uint4*>(src + (long long)i * kN);
-    }
-#pragma unroll
-    for (int u = 0; u < kVPT; ++u) {
-      const bool in = tid + u * kRowThreads < nv;
-      const E* e = reinterpret_cast<const E*>(&raw[u]);
-#pragma unroll
-      for (int j = 0; j < kN; ++j) x[u * kN + j] = in ? no_nan(to_f32(e[j])) : -INFINITY;
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < kE; ++j) {
-      const int i = tid + j * kRowThreads;
-      x[j] = i < n ? no_nan(to_f32(src[i])) : -INFINITY;
-    }
-  }
-  auto entry = [&](int j) -> int {
-    return vec ? (tid + kRowThreads * (j / kN)) * kN + j % kN : tid + kRowThreads * j;
-  };
+  // The chunk in registers as loaded (entry j of group u of a thread is chunk
+  // entry (tid + 256*u)*kN + j, -inf where the chunk has none).
+  uint32_t w[kW];
+  load_chunk_words<E, kVPT>(src, n, tid, w);
+  auto val = [&](int u, int j) -> float { return word_entry<E>(w[4 * u + j / (kN / 4)], j); };
 
-  // The thread's max and the first of its entries holding it.  A thread with
-  // no entries reports an index >= n, after every real one.
-  float tm = x[0];
-  int ta = entry(0);
+  // The thread's max tm and, for a sampled request, its sum ts of
+  // exp((x - tm) / T), in one pass (the sum is rescaled when a group raises the
+  // max).  A NaN never wins a comparison, so it counts as -inf for the max; in
+  // the sum it turns ts into NaN, and only then does the thread sum again,
+  // skipping NaN entries.
+  float tm = -INFINITY, ts = 0.0f;
 #pragma unroll
-  for (int j = 1; j < kE; ++j)
-    if (x[j] > tm) {
-      tm = x[j];
-      ta = entry(j);
+  for (int u = 0; u < kVPT; ++u) {
+    float lm = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kN; ++j) {
+      const float x = val(u, j);
+      lm = x > lm ? x : lm;
     }
-  float m = wave_max(tm);
-  int a = tm == m ? ta : 0x7FFFFFFF;
+    if (sampled) {
+      if (lm > tm) {
+        ts *= __builtin_amdgcn_exp2f((tm - lm) * k2);  // 0 while tm is -inf
+        tm = lm;
+      }
+      if (tm > -INFINITY && tm < INFINITY) {
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) a = min(a, __shfl_xor(a, o));
-  if (lane == 0) {
-    s_m[wave] = m;
-    s_a[wave] = a;
+        for (int j = 0; j < kN; ++j) ts += __builtin_amdgcn_exp2f((val(u, j) - tm) * k2);
+      }
+    } else {
+      tm = lm > tm ? lm : tm;
+    }
   }
+  mark_rewritten<kW>(w);
+  if (ts != ts && tm < INFINITY) {
+    ts = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kVPT; ++u)
+#pragma unroll
+      for (int j = 0; j < kN; ++j) {
+        const float x = val(u, j);
+        if (x == x) ts += __builtin_amdgcn_exp2f((x - tm) * k2);
+      }
+  }
+  float m = wave_max(tm);
+  if (lane == 0) s_m[wave] = m;
   __syncthreads();
   m = s_m[0];
-  a = s_a[0];
 #pragma unroll
-  for (int w = 1; w < kRowThreads / kWave; ++w) {
-    if (s_m[w] > m) {
-      m = s_m[w];
-      a = s_a[w];
-    } else if (s_m[w] == m) {
-      a = min(a, s_a[w]);
-    }
-  }
+  for (int q = 1; q < kRowThreads / kWave; ++q) m = fmaxf(m, s_m[q]);
 
-  float sum = 0.0f;
-  if (sampled && m > -INFINITY && m < INFINITY) {
-    const float k2 = kLog2e / T;
+  // The lowest index holding the max: only threads whose max equals it look,
+  // in index order.  If the max is -inf every entry counts as -inf (NaN
+  // included), so it is the chunk's first entry.
+  int a = 0x7FFFFFFF;
+  if (m == -INFINITY) {
+    a = 0;
+  } else if (tm == m) {
+    mark_rewritten<kW>(w);
 #pragma unroll
-    for (int j = 0; j < kE; ++j) sum += weight(x[j], m, k2);
+    for (int u = kVPT - 1; u >= 0; --u)
+#pragma unroll
+      for (int j = kN - 1; j >= 0; --j)
+        if (val(u, j) == m) a = (tid + kRowThreads * u) * kN + j;
   }
-  sum = wave_sum(sum);
-  if (lane == 0) s_s[wave] = sum;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) a = min(a, __shfl_xor(a, o));
+  // The thread's share of the chunk's sum of exp((x - m) / T) (m >= tm).
+  float part = 0.0f;
+  if (sampled && m > -INFINITY && m < INFINITY && tm > -INFINITY)
+    part = ts * __builtin_amdgcn_exp2f((tm - m) * k2);
+  part = wave_sum(part);
+  if (lane == 0) {
+    s_a[wave] = a;
+    s_s[wave] = part;
+  }
   __syncthreads();
   if (tid == 0) {
     float t = 0.0f;
+    int am = s_a[0];
 #pragma unroll
-    for (int w = 0; w < kRowThreads / kWave; ++w) t += s_s[w];
+    for (int q = 0; q < kRowThreads / kWave; ++q) {
+      t += s_s[q];
+      am = min(am, s_a[q]);
+    }
     ChunkStat st;
     st.m = m;
     st.s = t;
-    st.amax = v0 + a;
+    st.amax = v0 + am;
     st.pad = 0;
     ws[(long long)row * S + c] = st;
   }
@@ -199,27 +211,44 @@ __global__ __launch_bounds__(kRowThreads) void sampling_accept_kernel(
   const float k2 = sampled ? kLog2e / T : 0.0f;
   const E* rows = logits + (long long)b * Q * V;
 
-  // Target statistics of every node: the chunks' maxima and sums combined.
-  if (tid < n) {
-    const ChunkStat* st = ws + ((long long)b * Q + tid) * S;
-    const ChunkStat f = st[0];
-    float M = f.m, Z = f.s;
-    int am = f.amax;
-    for (int c = 1; c < S; ++c) {
+  // Target statistics of every node: the chunks' maxima and sums combined, one
+  // node per wavefront at a time with the lanes over its chunks, so that the
+  // chunk records are read in parallel rather than one after another.
+  for (int node = wave; node < n; node += kRowThreads / kWave) {
+    const ChunkStat* st = ws + ((long long)b * Q + node) * S;
+    float M = -INFINITY, Z = 0.0f;
+    int am = 0x7FFFFFFF;
+    for (int c = lane; c < S; c += kWave) {
       const ChunkStat g = st[c];
       if (g.m > M) {
         Z = (M > -INFINITY ? Z * weight(M, g.m, k2) : 0.0f) + g.s;
         M = g.m;
         am = g.amax;
+      } else if (g.m == M) {
+        Z += g.s;
+        am = min(am, g.amax);
       } else if (g.m > -INFINITY) {
         Z += g.s * weight(g.m, M, k2);
       }
     }
-    const bool greedy = !sampled || !(M > -INFINITY && M < INFINITY);
-    s_M[tid] = M;
-    s_Z[tid] = greedy ? 1.0f : Z;
-    s_amax[tid] = am;
-    s_greedy[tid] = greedy ? 1 : 0;
+    // Every lane's (M, Z) against the wave's max; the lowest index among the
+    // lanes holding the max.  An all -inf row keeps M = -inf and the lowest
+    // chunk's index.
+    const float Mw = wave_max(M);
+    const float z = M > -INFINITY ? Z * weight(M, Mw, k2) : 0.0f;
+    const float Zw = wave_sum(z);
+    int a = M == Mw ? am : 0x7FFFFFFF;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) a = min(a, __shfl_xor(a, o));
+    if (lane == 0) {
+      const bool greedy = !sampled || !(Mw > -INFINITY && Mw < INFINITY);
+      s_M[node] = Mw;
+      s_Z[node] = greedy ? 1.0f : Zw;
+      s_amax[node] = a;
+      s_greedy[node] = greedy ? 1 : 0;
+    }
+  }
+  if (tid < n) {
     s_tok[tid] = node_token[b * Q + tid];
     s_par[tid] = parent[b * Q + tid];
     s_coin[tid] = coins[b * Q + tid];
