@@ -375,7 +375,9 @@ __global__ __launch_bounds__(kTopkThreads) void draft_topk_merge_kernel(
 
 TopkPlan plan_draft_topk(int B, int D, int V, int K, int num_cu) {
   const long long rows = (long long)B * D;
-  const RowChunks rc = plan_row_chunks(rows, V, num_cu);
+  // One workgroup per compute unit: with few rows, more chunks would mostly add
+  // candidates for the merge to rank (S * K of them per row).
+  const RowChunks rc = plan_row_chunks(rows, V, num_cu, 1);
   TopkPlan p;
   p.chunks = rc.chunks;
   p.chunk = rc.chunk;

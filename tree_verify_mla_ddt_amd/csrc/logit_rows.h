@@ -19,11 +19,11 @@ struct RowChunks {
   int chunk;   // entries per chunk: a multiple of 8, <= kRowChunkMax; no chunk is empty
 };
 
-// About two workgroups per compute unit, at most 64 chunks per row unless the
-// chunk size forces more.
-inline RowChunks plan_row_chunks(long long rows, int V, int num_cu) {
+// About `per_cu` workgroups per compute unit, at most 64 chunks per row unless
+// the chunk size forces more.
+inline RowChunks plan_row_chunks(long long rows, int V, int num_cu, int per_cu) {
   const int s_min = (V + kRowChunkMax - 1) / kRowChunkMax;
-  const long long want = 2LL * (num_cu > 0 ? num_cu : 256);
+  const long long want = (long long)per_cu * (num_cu > 0 ? num_cu : 256);
   long long s = (want + rows - 1) / rows;
   if (s > 64) s = 64;
   if (s < s_min) s = s_min;

@@ -200,6 +200,7 @@ __global__ __launch_bounds__(kRowThreads) void sampling_accept_kernel(
   __shared__ int s_rtok[kMaxQ];  // tokens rejected at the last node, with their masses
   __shared__ float s_re[kMaxQ];
   __shared__ float s_w[kRowChunksMax];
+  __shared__ float s_r[kRowChunkMax];  // residual weights of the chunk holding the bonus draw
   __shared__ int s_len, s_nrej, s_chunk, s_first, s_lastpos, s_bonus;
   __shared__ float s_tgt;
 
@@ -387,22 +388,26 @@ __global__ __launch_bounds__(kRowThreads) void sampling_accept_kernel(
     if (ch < 0) {
       if (tid == 0) s_bonus = s_amax[cur];  // no residual mass at all
     } else {
-      // Thread t scans a run of consecutive entries of the chunk.
+      // The chunk's residual weights, staged in LDS with coalesced loads: each
+      // entry's weight against the node's max, 0 for the rejected tokens.
       const int v0 = ch * C;
       const int nc = V - v0 < C ? V - v0 : C;
+      const E* src = rows + (long long)cur * V + v0;
+#pragma unroll 8
+      for (int i = tid; i < nc; i += kRowThreads) s_r[i] = weight(no_nan(to_f32(src[i])), M, k2);
+      __syncthreads();
+      if (tid < nrej) {
+        const int t = s_rtok[tid] - v0;
+        if (t >= 0 && t < nc) s_r[t] = 0.0f;
+      }
+      __syncthreads();
+      // Thread t scans a run of consecutive entries of the chunk.
       const int run = (nc + kRowThreads - 1) / kRowThreads;
       const int lo = min(nc, tid * run), hi = min(nc, lo + run);
-      const E* src = rows + (long long)cur * V + v0;
-      auto resid = [&](int i) -> float {
-        const int v = v0 + i;
-        for (int j = 0; j < nrej; ++j)
-          if (s_rtok[j] == v) return 0.0f;
-        return weight(no_nan(to_f32(src[i])), M, k2);
-      };
       float sum = 0.0f;
       int lastpos = -1;
       for (int i = lo; i < hi; ++i) {
-        const float r = resid(i);
+        const float r = s_r[i];
         if (r > 0.0f) {
           sum += r;
           lastpos = v0 + i;
@@ -429,7 +434,7 @@ __global__ __launch_bounds__(kRowThreads) void sampling_accept_kernel(
       if (tid == s_first) {
         float part = 0.0f;
         for (int i = lo; i < hi; ++i) {
-          const float r = resid(i);
+          const float r = s_r[i];
           if (r > 0.0f) {
             part += r;
             if (excl + part > tgt) {
@@ -464,7 +469,7 @@ __global__ __launch_bounds__(kRowThreads) void sampling_accept_kernel(
 }  // namespace
 
 SamplingPlan plan_tree_accept_sampling(int B, int Q, int V, int num_cu) {
-  const RowChunks rc = plan_row_chunks((long long)B * Q, V, num_cu);
+  const RowChunks rc = plan_row_chunks((long long)B * Q, V, num_cu, 2);
   SamplingPlan p;
   p.chunks = rc.chunks;
   p.chunk = rc.chunk;
