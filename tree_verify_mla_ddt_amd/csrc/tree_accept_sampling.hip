@@ -34,6 +34,9 @@ namespace ddt {
 namespace {
 
 constexpr int kMaxQ = 128;
+constexpr int kStatBatch = 512;  // chunk records staged in LDS at a time
+constexpr int kSerialChunks = 16;  // up to this many chunks a thread combines a node alone
+static_assert(kRowChunksMax <= kStatBatch, "a batch holds at least one node");
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct ChunkStat {
@@ -56,15 +59,22 @@ __device__ __forceinline__ int clamp_nodes(int n, int Q) { return n < 1 ? 1 : (n
 
 __device__ __forceinline__ bool sampled_temperature(float T) { return T > 0.0f && T <= FLT_MAX; }
 
-__device__ __forceinline__ float wave_excl_scan(float v, int lane) {
-  float inc = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const float t = __shfl_up(inc, o);
-    if (lane >= o) inc += t;
-  }
-  const float ex = __shfl_up(inc, 1);
-  return lane == 0 ? 0.0f : ex;
+// v from the lane CTRL selects, 0 where that lane is outside the row or the row
+// is masked off (DPP with bound_ctrl off and a zero old value).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp0(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
+
+// Inclusive sum over lanes 0..lane with DPP row shifts and row broadcasts.
+__device__ __forceinline__ float wave_incl_scan(float v) {
+  v += dpp0<0x111, 0xF>(v);  // row_shr:1
+  v += dpp0<0x112, 0xF>(v);  // row_shr:2
+  v += dpp0<0x114, 0xF>(v);  // row_shr:4
+  v += dpp0<0x118, 0xF>(v);  // row_shr:8
+  v += dpp0<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp0<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
 }
 
 template <typename E>
@@ -201,6 +211,7 @@ __global__ __launch_bounds__(kRowThreads) void sampling_accept_kernel(
   __shared__ float s_re[kMaxQ];
   __shared__ float s_w[kRowChunksMax];
   __shared__ float s_r[kRowChunkMax];  // residual weights of the chunk holding the bonus draw
+  __shared__ ChunkStat s_cs[kStatBatch];  // chunk records of a batch of nodes
   __shared__ int s_len, s_nrej, s_chunk, s_first, s_lastpos, s_bonus;
   __shared__ float s_tgt;
 
@@ -212,49 +223,86 @@ __global__ __launch_bounds__(kRowThreads) void sampling_accept_kernel(
   const float k2 = sampled ? kLog2e / T : 0.0f;
   const E* rows = logits + (long long)b * Q * V;
 
-  // Target statistics of every node: the chunks' maxima and sums combined, one
-  // node per wavefront at a time with the lanes over its chunks, so that the
-  // chunk records are read in parallel rather than one after another.
-  for (int node = wave; node < n; node += kRowThreads / kWave) {
-    const ChunkStat* st = ws + ((long long)b * Q + node) * S;
-    float M = -INFINITY, Z = 0.0f;
-    int am = 0x7FFFFFFF;
-    for (int c = lane; c < S; c += kWave) {
-      const ChunkStat g = st[c];
-      if (g.m > M) {
-        Z = (M > -INFINITY ? Z * weight(M, g.m, k2) : 0.0f) + g.s;
-        M = g.m;
-        am = g.amax;
-      } else if (g.m == M) {
-        Z += g.s;
-        am = min(am, g.amax);
-      } else if (g.m > -INFINITY) {
-        Z += g.s * weight(g.m, M, k2);
-      }
-    }
-    // Every lane's (M, Z) against the wave's max; the lowest index among the
-    // lanes holding the max.  An all -inf row keeps M = -inf and the lowest
-    // chunk's index.
-    const float Mw = wave_max(M);
-    const float z = M > -INFINITY ? Z * weight(M, Mw, k2) : 0.0f;
-    const float Zw = wave_sum(z);
-    int a = M == Mw ? am : 0x7FFFFFFF;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) a = min(a, __shfl_xor(a, o));
-    if (lane == 0) {
-      const bool greedy = !sampled || !(Mw > -INFINITY && Mw < INFINITY);
-      s_M[node] = Mw;
-      s_Z[node] = greedy ? 1.0f : Zw;
-      s_amax[node] = a;
-      s_greedy[node] = greedy ? 1 : 0;
-    }
-  }
-  if (tid < n) {
+  // Target statistics of every node: the chunks' maxima and sums combined.  The
+  // chunk records of a batch of nodes are first staged in LDS by all threads
+  // (one round trip to memory per batch, not one per node); then each thread
+  // combines one node's chunks in chunk order when there are few chunks, else
+  // each wavefront one node at a time with the lanes over the chunks.
+  if (tid < n) {  // requested first: the statistics below do not depend on them
     s_tok[tid] = node_token[b * Q + tid];
     s_par[tid] = parent[b * Q + tid];
     s_coin[tid] = coins[b * Q + tid];
   }
-  __syncthreads();
+  // Nodes per batch (S <= kRowChunksMax <= kStatBatch), one per thread.
+  const int npb = min(kStatBatch / S, kRowThreads);
+  for (int nb0 = 0; nb0 < n; nb0 += npb) {
+    const int nn = min(npb, n - nb0);
+    const ChunkStat* src = ws + ((long long)b * Q + nb0) * S;
+#pragma unroll 2
+    for (int i = tid; i < nn * S; i += kRowThreads) s_cs[i] = src[i];
+    __syncthreads();
+    if (S <= kSerialChunks) {
+      if (tid < nn) {  // one node per thread, its chunks in order
+        const ChunkStat* st = s_cs + tid * S;
+        const ChunkStat f = st[0];
+        float M = f.m, Z = f.s;
+        int am = f.amax;
+        for (int c = 1; c < S; ++c) {
+          const ChunkStat g = st[c];
+          if (g.m > M) {
+            Z = (M > -INFINITY ? Z * weight(M, g.m, k2) : 0.0f) + g.s;
+            M = g.m;
+            am = g.amax;
+          } else if (g.m > -INFINITY) {
+            Z += g.s * weight(g.m, M, k2);
+          }
+        }
+        const int node = nb0 + tid;
+        const bool greedy = !sampled || !(M > -INFINITY && M < INFINITY);
+        s_M[node] = M;
+        s_Z[node] = greedy ? 1.0f : Z;
+        s_amax[node] = am;
+        s_greedy[node] = greedy ? 1 : 0;
+      }
+    } else {
+      // One node per wavefront at a time, lanes over its chunks.
+      for (int k = wave; k < nn; k += kRowThreads / kWave) {
+        const ChunkStat* st = s_cs + k * S;
+        float M = -INFINITY, Z = 0.0f;
+        int am = 0x7FFFFFFF;
+        for (int c = lane; c < S; c += kWave) {
+          const ChunkStat g = st[c];
+          if (g.m > M) {
+            Z = (M > -INFINITY ? Z * weight(M, g.m, k2) : 0.0f) + g.s;
+            M = g.m;
+            am = g.amax;
+          } else if (g.m == M) {
+            Z += g.s;
+            am = min(am, g.amax);
+          } else if (g.m > -INFINITY) {
+            Z += g.s * weight(g.m, M, k2);
+          }
+        }
+        // Every lane's (M, Z) against the wave's max; the lowest index among
+        // the lanes holding the max (the lowest chunk's when all are -inf).
+        const float Mw = wave_max(M);
+        const float z = M > -INFINITY ? Z * weight(M, Mw, k2) : 0.0f;
+        const float Zw = wave_sum(z);
+        int a = M == Mw ? am : 0x7FFFFFFF;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) a = min(a, __shfl_xor(a, o));
+        if (lane == 0) {
+          const int node = nb0 + k;
+          const bool greedy = !sampled || !(Mw > -INFINITY && Mw < INFINITY);
+          s_M[node] = Mw;
+          s_Z[node] = greedy ? 1.0f : Zw;
+          s_amax[node] = a;
+          s_greedy[node] = greedy ? 1 : 0;
+        }
+      }
+    }
+    __syncthreads();
+  }
   // Unnormalized target mass of each child's token at its parent.
   if (tid < n) {
     const int p = s_par[tid], t = s_tok[tid];
@@ -271,32 +319,44 @@ __global__ __launch_bounds__(kRowThreads) void sampling_accept_kernel(
 
   // The walk, on wavefront 0: lane l looks after nodes l and l + 64.
   if (wave == 0) {
+    // Per-node values of nodes lane and lane + 64, read once.
+    const bool in_a = lane < n, in_b = lane + kWave < n;
+    const int tok_a = in_a ? s_tok[lane] : -1, tok_b = in_b ? s_tok[lane + kWave] : -1;
+    const int par_a = in_a ? s_par[lane] : -1, par_b = in_b ? s_par[lane + kWave] : -1;
+    const float e_a = in_a ? s_e[lane] : 0.0f, e_b = in_b ? s_e[lane + kWave] : 0.0f;
+    const float coin_a = in_a ? s_coin[lane] : 0.0f, coin_b = in_b ? s_coin[lane + kWave] : 0.0f;
     const uint64_t below = (1ull << lane) - 1;
     int cur = 0, len = 1;
     if (lane == 0) s_path[0] = 0;
     for (;;) {
       const int c0 = lane, c1 = lane + kWave;
-      const bool ch0 = c0 < n && c0 > cur && s_par[c0] == cur;
-      const bool ch1 = c1 < n && c1 > cur && s_par[c1] == cur;
+      const bool ch0 = in_a && c0 > cur && par_a == cur;
+      const bool ch1 = in_b && c1 > cur && par_b == cur;
       const uint64_t m0 = __ballot(ch0), m1 = __ballot(ch1);
-      float e0 = ch0 ? s_e[c0] : 0.0f, e1 = ch1 ? s_e[c1] : 0.0f;
+      float e0 = ch0 ? e_a : 0.0f, e1 = ch1 ? e_b : 0.0f;
       // A token already tried at this node (an earlier sibling with the same
-      // token) has no mass left.
-      if (e0 > 0.0f) {
-        for (uint64_t mm = m0 & below; mm; mm &= mm - 1)
-          if (s_tok[__ffsll((unsigned long long)mm) - 1] == s_tok[c0]) { e0 = 0.0f; break; }
+      // token) has no mass left.  The siblings are visited in index order by a
+      // wave-uniform loop; their tokens come from registers.
+      bool dup0 = false, dup1 = false;
+      for (uint64_t mm = m0; mm; mm &= mm - 1) {
+        const int sl = __ffsll((unsigned long long)mm) - 1;
+        const int ts = __builtin_amdgcn_readlane(tok_a, sl);
+        dup0 |= lane > sl && tok_a == ts;
+        dup1 |= tok_b == ts;  // every sibling below 64 precedes c1
       }
-      if (e1 > 0.0f) {
-        for (uint64_t mm = m0; mm; mm &= mm - 1)
-          if (s_tok[__ffsll((unsigned long long)mm) - 1] == s_tok[c1]) { e1 = 0.0f; break; }
-        if (e1 > 0.0f)
-          for (uint64_t mm = m1 & below; mm; mm &= mm - 1)
-            if (s_tok[kWave + __ffsll((unsigned long long)mm) - 1] == s_tok[c1]) { e1 = 0.0f; break; }
+      for (uint64_t mm = m1; mm; mm &= mm - 1) {
+        const int sl = __ffsll((unsigned long long)mm) - 1;
+        const int ts = __builtin_amdgcn_readlane(tok_b, sl);
+        dup1 |= lane > sl && tok_b == ts;
       }
+      if (dup0) e0 = 0.0f;
+      if (dup1) e1 = 0.0f;
       // Mass of the earlier siblings, in index order.
-      const float r0 = wave_excl_scan(e0, lane);
-      const float tot0 = __shfl(r0 + e0, kWave - 1);
-      const float r1 = tot0 + wave_excl_scan(e1, lane);
+      const float i0 = wave_incl_scan(e0);
+      const float tot0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(i0), kWave - 1));
+      const float i1 = wave_incl_scan(e1);
+      const float r0 = i0 - e0;
+      const float r1 = tot0 + (i1 - e1);
       bool a0, a1;
       if (s_greedy[cur]) {
         a0 = e0 > 0.0f;
@@ -304,8 +364,8 @@ __global__ __launch_bounds__(kRowThreads) void sampling_accept_kernel(
       } else {
         // coin < e / (Z - r), written without the division.
         const float Z = s_Z[cur];
-        a0 = e0 > 0.0f && s_coin[c0] * (Z - r0) < e0;
-        a1 = e1 > 0.0f && s_coin[c1] * (Z - r1) < e1;
+        a0 = e0 > 0.0f && coin_a * (Z - r0) < e0;
+        a1 = e1 > 0.0f && coin_b * (Z - r1) < e1;
       }
       const uint64_t acc0 = __ballot(a0), acc1 = __ballot(a1);
       int next = -1;
@@ -319,12 +379,12 @@ __global__ __launch_bounds__(kRowThreads) void sampling_accept_kernel(
         const int base1 = __popcll(rj0);
         if (e0 > 0.0f) {
           const int k = __popcll(rj0 & below);
-          s_rtok[k] = s_tok[c0];
+          s_rtok[k] = tok_a;
           s_re[k] = e0;
         }
         if (e1 > 0.0f) {
           const int k = base1 + __popcll(rj1 & below);
-          s_rtok[k] = s_tok[c1];
+          s_rtok[k] = tok_b;
           s_re[k] = e1;
         }
         if (lane == 0) {
@@ -393,8 +453,23 @@ __global__ __launch_bounds__(kRowThreads) void sampling_accept_kernel(
       const int v0 = ch * C;
       const int nc = V - v0 < C ? V - v0 : C;
       const E* src = rows + (long long)cur * V + v0;
-#pragma unroll 8
-      for (int i = tid; i < nc; i += kRowThreads) s_r[i] = weight(no_nan(to_f32(src[i])), M, k2);
+      {
+        // All of a thread's loads are issued before any is used (entry j of
+        // group u is chunk entry (tid + 256*u)*kN + j, -inf past the chunk).
+        constexpr int kN = Vec16<E>::kN;
+        constexpr int kVPT = kRowChunkMax / kN / kRowThreads;
+        uint32_t w[kVPT * 4];
+        load_chunk_words<E, kVPT>(src, nc, tid, w);
+#pragma unroll
+        for (int u = 0; u < kVPT; ++u) {
+          const int e0 = (tid + kRowThreads * u) * kN;
+          if (e0 < nc) {
+#pragma unroll
+            for (int j = 0; j < kN; ++j)
+              s_r[e0 + j] = weight(no_nan(word_entry<E>(w[4 * u + j / (kN / 4)], j)), M, k2);
+          }
+        }
+      }
       __syncthreads();
       if (tid < nrej) {
         const int t = s_rtok[tid] - v0;

@@ -92,7 +92,6 @@ __global__ __launch_bounds__(kWave) void tree_build_kernel(
 
   const int b = blockIdx.x;
   const int lane = threadIdx.x;
-  const int32_t L = prefix_len[b];  // requested first: only the final stores use it
   const int DK = D * K;
   const size_t in0 = (size_t)b * DK;
   for (int t = lane; t < DK; t += kWave) {
@@ -194,6 +193,7 @@ __global__ __launch_bounds__(kWave) void tree_build_kernel(
   __syncthreads();
 
   const int W = (Q + 63) >> 6;
+  const int32_t L = prefix_len[b];
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int i = lane + k * kWave;
