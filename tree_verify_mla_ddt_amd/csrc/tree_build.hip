@@ -11,9 +11,10 @@
 // live candidates) lives in registers, two slots per lane, each as a 64-bit key
 // whose unsigned order is the pop order: the fp32 score mapped to an
 // order-preserving integer in the high word, then 0xFFFF - parent and
-// 0xFFFF - rank in the low word, so a wave-wide max is "highest score, then
-// lowest parent index, then lowest rank".  Every pop is one DPP max reduction
-// plus one ballot to find the owning slot; the popped slot is reused for the
+// 0xFFFF - rank in the low word, so the largest key is "highest score, then
+// lowest parent index, then lowest rank".  Every pop is a 32-bit DPP max
+// reduction of the high words (a second one over the low words only when
+// scores tie) plus a ballot to find the owning slot; the popped slot is reused for the
 // child and a fresh slot takes the sibling.  Node i's fields live in lane i%64
 // (register i/64) and are read back with readlane; its visibility row is its
 // parent's row plus its own bit, set when it is popped.
@@ -40,29 +41,24 @@ __device__ __forceinline__ uint64_t frontier_key(float s, int parent, int rank) 
          ((uint64_t)(uint32_t)(0xFFFF - parent) << 16) | (uint64_t)(uint32_t)(0xFFFF - rank);
 }
 
-// One DPP step of a 64-bit max: combine with the lane selected by CTRL (rows
-// outside ROW_MASK, and lanes whose source is out of range, keep their value).
+// One DPP step of a 32-bit max: combine with the lane selected by CTRL (rows
+// outside ROW_MASK contribute 0, the identity of an unsigned max).
 template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ uint64_t max_dpp(uint64_t v) {
-  const int lo = (int)(uint32_t)v, hi = (int)(uint32_t)(v >> 32);
-  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROW_MASK, 0xF, false);
-  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROW_MASK, 0xF, false);
-  const uint64_t o = ((uint64_t)ohi << 32) | olo;
+__device__ __forceinline__ uint32_t max_dpp(uint32_t v) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
   return o > v ? o : v;
 }
 
-// Wave-wide max: pair swaps, quad swaps, half-row and row mirrors give every
-// lane its row's max; two row broadcasts carry it to lane 63.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+// Wave-wide unsigned max: pair swaps, quad swaps, half-row and row mirrors give
+// every lane its row's max; two row broadcasts carry it to lane 63.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   v = max_dpp<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
   v = max_dpp<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
   v = max_dpp<0x141, 0xF>(v);  // row_half_mirror
   v = max_dpp<0x140, 0xF>(v);  // row_mirror
   v = max_dpp<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
   v = max_dpp<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
-  return ((uint64_t)hi << 32) | lo;
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 __device__ __forceinline__ int read_i(int v0, int v1, int idx) {
@@ -131,22 +127,42 @@ __global__ __launch_bounds__(kWave) void tree_build_kernel(
 
   int n = 1;
   while (n < Q) {
-    const uint64_t best = wave_max_u64(key0 > key1 ? key0 : key1);
-    if (best == 0) break;  // nothing left on offer: underfull tree
-    const uint64_t m0 = __ballot(key0 == best);
-    const uint64_t m1 = __ballot(key1 == best);
+    // The best key: the largest score word (one 32-bit DPP max), then, only
+    // when several slots share it, the largest low word among them.  Live
+    // candidates have distinct (parent, rank), so one slot remains.
+    const uint32_t h0 = (uint32_t)(key0 >> 32), h1 = (uint32_t)(key1 >> 32);
+    const uint32_t hbest = wave_max_u32(h0 > h1 ? h0 : h1);
+    if (hbest == 0) break;  // nothing left on offer: underfull tree
+    uint64_t m0 = __ballot(h0 == hbest);
+    uint64_t m1 = __ballot(h1 == hbest);
+    if (__popcll(m0) + __popcll(m1) > 1) {
+      const uint32_t l0 = h0 == hbest ? (uint32_t)key0 : 0u;
+      const uint32_t l1 = h1 == hbest ? (uint32_t)key1 : 0u;
+      const uint32_t lbest = wave_max_u32(l0 > l1 ? l0 : l1);
+      m0 = __ballot(h0 == hbest && (uint32_t)key0 == lbest);
+      m1 = __ballot(h1 == hbest && (uint32_t)key1 == lbest);
+    }
     const int slot = m0 ? (__ffsll((unsigned long long)m0) - 1)
                         : (64 + __ffsll((unsigned long long)m1) - 1);
+    const uint32_t low = (uint32_t)read_i((int)(uint32_t)key0, (int)(uint32_t)key1, slot);
     const int cdep = read_i(fd0, fd1, slot);
-    const float csc = unorder_bits((uint32_t)(best >> 32));
-    const int cpar = 0xFFFF - (int)((best >> 16) & 0xFFFFu);
-    const int crank = 0xFFFF - (int)(best & 0xFFFFu);
+    const float csc = unorder_bits(hbest);
+    const int cpar = 0xFFFF - (int)(low >> 16);
+    const int crank = 0xFFFF - (int)(low & 0xFFFFu);
     const int i = n++;
+
+    // Table reads of this pop, issued together: the node's token, its rank-0
+    // child's log-prob and its next sibling's (indices clamped in range; the
+    // values are used only where the candidate exists).
+    const int row = (cdep - 1) * K;
+    const int ctok = s_ids[row + crank];
+    const float lp_child = s_logp[(cdep < D ? cdep : cdep - 1) * K];
+    const float lp_sib = s_logp[row + (crank + 1 < K ? crank + 1 : crank)];
+    const float psc = read_f(sc0, sc1, cpar);
 
     // The new node: fields into its owner lane, visibility = parent's + self.
     const uint64_t pva = read_u64(va0, va1, cpar);
     const uint64_t pvb = read_u64(vb0, vb1, cpar);
-    const int ctok = s_ids[(cdep - 1) * K + crank];
     if (lane == (i & 63)) {
       const uint64_t nva = pva | (i < 64 ? (1ull << i) : 0ull);
       const uint64_t nvb = pvb | (i >= 64 ? (1ull << (i - 64)) : 0ull);
@@ -156,15 +172,10 @@ __global__ __launch_bounds__(kWave) void tree_build_kernel(
 
     // Offer the new node's rank-0 child and its next-ranked sibling.
     uint64_t kc = 0, ks = 0;
-    if (cdep < D) {
-      const float s = __fadd_rn(csc, s_logp[cdep * K]);
-      if (s > -INFINITY) kc = frontier_key(s, i, 0);
-    }
-    if (crank + 1 < K) {
-      const float psc = read_f(sc0, sc1, cpar);
-      const float s = __fadd_rn(psc, s_logp[(cdep - 1) * K + crank + 1]);
-      if (s > -INFINITY) ks = frontier_key(s, cpar, crank + 1);
-    }
+    const float s_child = __fadd_rn(csc, lp_child);
+    if (cdep < D && s_child > -INFINITY) kc = frontier_key(s_child, i, 0);
+    const float s_sib = __fadd_rn(psc, lp_sib);
+    if (crank + 1 < K && s_sib > -INFINITY) ks = frontier_key(s_sib, cpar, crank + 1);
     int slot_a = slot, slot_b = -1, dep_a = 0, dep_b = cdep;
     uint64_t key_a = 0, key_b = 0;
     if (kc) {
