@@ -386,8 +386,8 @@ def main():
         write_traffic(args.workload, *args.traffic_from)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not "
-              f"supported (the step is single-GPU: no sharding or collectives).", file=sys.stderr)
+        print(f"bench.py: the verify step runs on one GPU; --gpus {args.gpus} is not "
+              f"supported (no sharding or collectives across GPUs).", file=sys.stderr)
         sys.exit(2)
 
     import torch
