@@ -45,9 +45,8 @@ __global__ __launch_bounds__(kWave) void tree_accept_kernel(
 
   int cur = 0, len = 1, want = 0;
   for (;;) {
-    const int w0 = __shfl(tgt0, cur & 63);
-    const int w1 = __shfl(tgt1, cur & 63);
-    want = cur < kWave ? w0 : w1;
+    // cur is the same in every lane: read the target token straight from its lane.
+    want = __builtin_amdgcn_readlane(cur < kWave ? tgt0 : tgt1, cur & 63);
     const bool hit0 = lane < nb && lane > cur && par0 == cur && tok0 == want;
     const bool hit1 = lane + kWave < nb && lane + kWave > cur && par1 == cur && tok1 == want;
     const uint64_t b0 = __ballot(hit0);

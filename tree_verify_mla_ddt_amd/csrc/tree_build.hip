@@ -131,14 +131,14 @@ __global__ __launch_bounds__(kWave) void tree_build_kernel(
     // when several slots share it, the largest low word among them.  Live
     // candidates have distinct (parent, rank), so one slot remains.
     const uint32_t h0 = (uint32_t)(key0 >> 32), h1 = (uint32_t)(key1 >> 32);
-    const uint32_t hbest = wave_max_u32(h0 > h1 ? h0 : h1);
+    const uint32_t hbest = wave_max_u32(max(h0, h1));
     if (hbest == 0) break;  // nothing left on offer: underfull tree
     uint64_t m0 = __ballot(h0 == hbest);
     uint64_t m1 = __ballot(h1 == hbest);
     if (__popcll(m0) + __popcll(m1) > 1) {
       const uint32_t l0 = h0 == hbest ? (uint32_t)key0 : 0u;
       const uint32_t l1 = h1 == hbest ? (uint32_t)key1 : 0u;
-      const uint32_t lbest = wave_max_u32(l0 > l1 ? l0 : l1);
+      const uint32_t lbest = wave_max_u32(max(l0, l1));
       m0 = __ballot(h0 == hbest && (uint32_t)key0 == lbest);
       m1 = __ballot(h1 == hbest && (uint32_t)key1 == lbest);
     }
