@@ -107,14 +107,18 @@ def test_workload_trees(name):
     compare(g, o, T, max_skipped=wl.B // 16 + 1)
 
 
-@pytest.mark.parametrize("V,dtype", [(37, torch.float32), (1000, torch.bfloat16),
-                                     (70001, torch.float32)])
-def test_adversarial_values(V, dtype):
+@pytest.mark.parametrize("V,dtype,B", [(37, torch.float32, 24), (1000, torch.bfloat16, 24),
+                                       (70001, torch.float32, 24),
+                                       (300000, torch.bfloat16, 20)])
+def test_adversarial_values(V, dtype, B):
     """Random trees with duplicate and out-of-range tokens, bad parents, clamped
-    n_nodes, -inf/NaN/+inf logits, edge temperatures and coins."""
-    note(f"tree_accept_sampling adversarial V={V} {dtype}")
+    n_nodes, -inf/NaN/+inf logits, edge temperatures and coins.  With V = 300000 a
+    row spans more than 16 chunks and a request's nodes more than one staging
+    batch of chunk records (the per-wavefront combine); the other shapes take the
+    per-thread combine."""
+    note(f"tree_accept_sampling adversarial V={V} {dtype} B={B}")
     rng = np.random.default_rng(V)
-    B, Q = 24, 33
+    Q = 33
     tok = rng.integers(-2, V + 2, size=(B, Q)).astype(np.int32)
     par = np.zeros((B, Q), np.int32)
     for b in range(B):
@@ -136,7 +140,7 @@ def test_adversarial_values(V, dtype):
     x[3, 0, ::3] = float("nan")
     x[4, :, :] = 1.5                           # equal logits
     x = x.to(dtype)
-    T = np.array([0.0, 1.0, 1.0, 1.0, 1.0, -1.0, np.inf, np.nan, 1e-30, 1e30, 0.5, 2.0] * 2,
+    T = np.array(([0.0, 1.0, 1.0, 1.0, 1.0, -1.0, np.inf, np.nan, 1e-30, 1e30, 0.5, 2.0] * 2)[:B],
                  np.float32)
     coins = rng.random((B, Q), dtype=np.float32)
     coins[12] = 0.0
