@@ -125,27 +125,34 @@ __global__ __launch_bounds__(kWave) void tree_build_kernel(
     }
   }
 
+  // One pop.  With std::true_type (fewer than 64 nodes exist) every node,
+  // parent and frontier slot index is below 64, so only the first register of
+  // each pair is read or written (slots are handed out one per node at most);
+  // std::false_type is the general pop.
   int n = 1;
-  while (n < Q) {
+  auto pop = [&](auto low_tag) -> bool __attribute__((always_inline)) {
+    constexpr bool kLow = decltype(low_tag)::value;
     // The best key: the largest score word (one 32-bit DPP max), then, only
     // when several slots share it, the largest low word among them.  Live
     // candidates have distinct (parent, rank), so one slot remains.
-    const uint32_t h0 = (uint32_t)(key0 >> 32), h1 = (uint32_t)(key1 >> 32);
-    const uint32_t hbest = wave_max_u32(max(h0, h1));
-    if (hbest == 0) break;  // nothing left on offer: underfull tree
+    const uint32_t h0 = (uint32_t)(key0 >> 32), h1 = kLow ? 0u : (uint32_t)(key1 >> 32);
+    const uint32_t hbest = wave_max_u32(kLow ? h0 : max(h0, h1));
+    if (hbest == 0) return false;  // nothing left on offer: underfull tree
     uint64_t m0 = __ballot(h0 == hbest);
-    uint64_t m1 = __ballot(h1 == hbest);
+    uint64_t m1 = kLow ? 0ull : __ballot(h1 == hbest);
     if (__popcll(m0) + __popcll(m1) > 1) {
       const uint32_t l0 = h0 == hbest ? (uint32_t)key0 : 0u;
-      const uint32_t l1 = h1 == hbest ? (uint32_t)key1 : 0u;
-      const uint32_t lbest = wave_max_u32(max(l0, l1));
+      const uint32_t l1 = (!kLow && h1 == hbest) ? (uint32_t)key1 : 0u;
+      const uint32_t lbest = wave_max_u32(kLow ? l0 : max(l0, l1));
       m0 = __ballot(h0 == hbest && (uint32_t)key0 == lbest);
-      m1 = __ballot(h1 == hbest && (uint32_t)key1 == lbest);
+      m1 = kLow ? 0ull : __ballot(h1 == hbest && (uint32_t)key1 == lbest);
     }
     const int slot = m0 ? (__ffsll((unsigned long long)m0) - 1)
                         : (64 + __ffsll((unsigned long long)m1) - 1);
-    const uint32_t low = (uint32_t)read_i((int)(uint32_t)key0, (int)(uint32_t)key1, slot);
-    const int cdep = read_i(fd0, fd1, slot);
+    const uint32_t low =
+        kLow ? (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)key0, slot)
+             : (uint32_t)read_i((int)(uint32_t)key0, (int)(uint32_t)key1, slot);
+    const int cdep = kLow ? __builtin_amdgcn_readlane(fd0, slot) : read_i(fd0, fd1, slot);
     const float csc = unorder_bits(hbest);
     const int cpar = 0xFFFF - (int)(low >> 16);
     const int crank = 0xFFFF - (int)(low & 0xFFFFu);
@@ -158,16 +165,25 @@ __global__ __launch_bounds__(kWave) void tree_build_kernel(
     const int ctok = s_ids[row + crank];
     const float lp_child = s_logp[(cdep < D ? cdep : cdep - 1) * K];
     const float lp_sib = s_logp[row + (crank + 1 < K ? crank + 1 : crank)];
-    const float psc = read_f(sc0, sc1, cpar);
+    const float psc = kLow ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc0), cpar))
+                           : read_f(sc0, sc1, cpar);
 
     // The new node: fields into its owner lane, visibility = parent's + self.
-    const uint64_t pva = read_u64(va0, va1, cpar);
-    const uint64_t pvb = read_u64(vb0, vb1, cpar);
-    if (lane == (i & 63)) {
-      const uint64_t nva = pva | (i < 64 ? (1ull << i) : 0ull);
-      const uint64_t nvb = pvb | (i >= 64 ? (1ull << (i - 64)) : 0ull);
-      if (i < 64) { par0 = cpar; dep0 = cdep; tok0 = ctok; sc0 = csc; va0 = nva; vb0 = nvb; }
-      else        { par1 = cpar; dep1 = cdep; tok1 = ctok; sc1 = csc; va1 = nva; vb1 = nvb; }
+    if (kLow) {
+      const uint64_t pva = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)va0, cpar) |
+                           ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(va0 >> 32), cpar) << 32);
+      const uint64_t pvb = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)vb0, cpar) |
+                           ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(vb0 >> 32), cpar) << 32);
+      if (lane == i) { par0 = cpar; dep0 = cdep; tok0 = ctok; sc0 = csc; va0 = pva | (1ull << i); vb0 = pvb; }
+    } else {
+      const uint64_t pva = read_u64(va0, va1, cpar);
+      const uint64_t pvb = read_u64(vb0, vb1, cpar);
+      if (lane == (i & 63)) {
+        const uint64_t nva = pva | (i < 64 ? (1ull << i) : 0ull);
+        const uint64_t nvb = pvb | (i >= 64 ? (1ull << (i - 64)) : 0ull);
+        if (i < 64) { par0 = cpar; dep0 = cdep; tok0 = ctok; sc0 = csc; va0 = nva; vb0 = nvb; }
+        else        { par1 = cpar; dep1 = cdep; tok1 = ctok; sc1 = csc; va1 = nva; vb1 = nvb; }
+      }
     }
 
     // Offer the new node's rank-0 child and its next-ranked sibling.
@@ -189,12 +205,25 @@ __global__ __launch_bounds__(kWave) void tree_build_kernel(
       key_a = ks;
       dep_a = cdep;
     }
-    if (lane == (slot_a & 63)) {
-      if (slot_a < 64) { key0 = key_a; fd0 = dep_a; } else { key1 = key_a; fd1 = dep_a; }
+    if (kLow) {
+      if (lane == slot_a) { key0 = key_a; fd0 = dep_a; }
+      if (lane == slot_b) { key0 = key_b; fd0 = dep_b; }
+    } else {
+      if (lane == (slot_a & 63)) {
+        if (slot_a < 64) { key0 = key_a; fd0 = dep_a; } else { key1 = key_a; fd1 = dep_a; }
+      }
+      if (slot_b >= 0 && lane == (slot_b & 63)) {
+        if (slot_b < 64) { key0 = key_b; fd0 = dep_b; } else { key1 = key_b; fd1 = dep_b; }
+      }
     }
-    if (slot_b >= 0 && lane == (slot_b & 63)) {
-      if (slot_b < 64) { key0 = key_b; fd0 = dep_b; } else { key1 = key_b; fd1 = dep_b; }
-    }
+    return true;
+  };
+  // The first 64 nodes, then the rest; a frontier that runs empty ends the
+  // build in either phase (the second starts only once 64 nodes exist).
+  const int q_low = Q < kWave ? Q : kWave;
+  while (n < q_low && pop(std::true_type{})) {
+  }
+  while (n >= kWave && n < Q && pop(std::false_type{})) {
   }
 
   // Children bitsets, then the links: first child = lowest child index; next
