@@ -150,7 +150,11 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(si
         if (x == x) ts += __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -mk));
       }
   }
-  const float wm = wave_max(tm);
+  // Butterfly shuffles here rather than the DPP reductions: two per workgroup,
+  // and the DPP form's registers would push this kernel past 64 VGPRs.
+  float wm = tm;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) wm = fmaxf(wm, __shfl_xor(wm, o));
   if (lane == 0) s_max[wave] = wm;
 
   // Threshold: each wave sorts its threads' maxima (lane-exchange bitonic
@@ -182,7 +186,8 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(si
   }
   // The thread's share of the chunk's sum of exp(x - M) (M >= tm).
   float part = tm > -INFINITY ? ts * __builtin_amdgcn_exp2f((tm - M) * kLog2e) : 0.0f;
-  part = wave_sum(part);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o);
   if (lane == 0) s_sum[wave] = part;
 
   // Fast path (threshold above -inf): threads whose max reaches it gather their

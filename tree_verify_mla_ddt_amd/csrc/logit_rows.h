@@ -104,15 +104,37 @@ __device__ __forceinline__ void mark_rewritten(uint32_t (&w)[kW]) {
   for (int q = 0; q < kW; ++q) asm volatile("" : "+v"(w[q]));
 }
 
+// Wave-wide reductions with DPP row operations: quad swaps, half-row and row
+// mirrors give every lane its row's result, two row broadcasts carry it to lane
+// 63, whose value every lane then reads (the result is wave-uniform).  Rows a
+// broadcast leaves out take the identity.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t v, uint32_t identity, Op op) {
+  const int id = (int)identity;
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  return __uint_as_float(wave_reduce(__float_as_uint(v), __float_as_uint(-INFINITY),
+                                     [](uint32_t a, uint32_t b) {
+                                       return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+                                     }));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  return __uint_as_float(wave_reduce(__float_as_uint(v), 0u, [](uint32_t a, uint32_t b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  }));
+}
+__device__ __forceinline__ int wave_min(int v) {
+  return (int)wave_reduce((uint32_t)v, 0x7FFFFFFFu, [](uint32_t a, uint32_t b) {
+    return (uint32_t)min((int)a, (int)b);
+  });
 }
 
 }  // namespace ddt

@@ -167,8 +167,7 @@ void sampling_stats_kernel(
       for (int j = kN - 1; j >= 0; --j)
         if (val(u, j) == m) a = (tid + kRowThreads * u) * kN + j;
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) a = min(a, __shfl_xor(a, o));
+  a = wave_min(a);
   // The thread's share of the chunk's sum of exp((x - m) / T) (m >= tm).
   float part = 0.0f;
   if (sampled && m > -INFINITY && m < INFINITY && tm > -INFINITY)
@@ -289,8 +288,7 @@ __global__ __launch_bounds__(kRowThreads) void sampling_accept_kernel(
         const float z = M > -INFINITY ? Z * weight(M, Mw, k2) : 0.0f;
         const float Zw = wave_sum(z);
         int a = M == Mw ? am : 0x7FFFFFFF;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) a = min(a, __shfl_xor(a, o));
+        a = wave_min(a);
         if (lane == 0) {
           const int node = nb0 + k;
           const bool greedy = !sampled || !(Mw > -INFINITY && Mw < INFINITY);
