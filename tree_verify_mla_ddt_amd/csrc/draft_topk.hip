@@ -10,14 +10,15 @@
 // are cut into chunks of at most 12288 entries so that the grid fills the chip
 // even for a handful of rows:
 //  * draft_topk_partial_kernel (one 256-thread workgroup per chunk): 16-byte
-//    loads straight into registers as order-preserving 32-bit keys, the chunk
-//    max and sum of exp(x - max), then the chunk's K best (key, index) pairs.
-//    The K-th largest of the 256 threads' maxima is a lower bound of the
-//    chunk's K-th largest key, so the keys at or above it -- usually a few more
-//    than K -- are gathered into LDS and ranked (each candidate counts the
-//    larger ones); when wide ties make them too many, a radix selection (four
-//    8-bit digits, LDS histograms) finds the K-th key exactly and the
-//    lowest-index ties are taken in index order;
+//    loads kept in registers as loaded words; one pass gives each thread's max
+//    and its sum of exp(x - max), combined into the chunk's.  Each wave's K-th
+//    largest thread max has K entries at or above it, so the largest of the
+//    four bounds the chunk's K-th entry from below; the entries at or above it
+//    -- a few times K on ordinary rows -- are gathered into LDS as
+//    order-preserving (key, index) pairs and ranked (each candidate counts the
+//    larger ones).  When the bound is -inf or wide ties make the candidates too
+//    many, a radix selection (four 8-bit digits, LDS histograms) finds the K-th
+//    key exactly and the lowest-index ties are taken in index order;
 //  * draft_topk_merge_kernel (one workgroup per row): the chunks' log-sum-exps
 //    combined, their candidates ranked (or bitonic-sorted in LDS when there are
 //    more than 1024) and the first K written as log-probs and ids.

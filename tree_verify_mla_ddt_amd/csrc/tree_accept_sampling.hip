@@ -16,16 +16,18 @@
 //
 // Two kernels on one stream:
 //  * sampling_stats_kernel, one 256-thread workgroup per (node row, chunk)
-//    (rows along the grid's x, so any batch fits):
-//    16-byte loads of the chunk into registers, its max, the lowest index
-//    holding it, and the sum of exp((x - max) / T).  This pass reads every
-//    live node's logits once and bounds the path by HBM bandwidth.
+//    (rows along the grid's x, so any batch fits): 16-byte loads of the chunk
+//    kept in registers; one pass gives each thread's max and sum of
+//    exp((x - max) / T), combined into the chunk's, and the threads holding
+//    the chunk max find its lowest index.  This pass reads every live node's
+//    logits once and bounds the path by HBM bandwidth.
 //  * sampling_accept_kernel, one workgroup per request: combines the chunk
-//    statistics of every node, reads the one logit each child's acceptance
-//    needs, walks the tree on one wavefront (a prefix sum over the siblings
-//    gives each one's rejected mass, a ballot the first accepted), then draws
-//    the bonus token: the chunk holding the draw comes from the chunks'
-//    residual masses, and a block-wide scan of that chunk finds the entry.
+//    statistics of every node (staged in LDS), reads the one logit each
+//    child's acceptance needs, walks the tree on one wavefront (a DPP prefix
+//    sum over the siblings gives each one's rejected mass, a ballot the first
+//    accepted), then draws the bonus token: the chunk holding the draw comes
+//    from the chunks' residual masses, its residual weights are staged in LDS,
+//    and a block-wide scan over runs of entries finds the token.
 #include <float.h>
 
 #include "logit_rows.h"
