@@ -36,7 +36,7 @@ namespace ddt {
 namespace {
 
 constexpr int kMaxQ = 128;
-constexpr int kStatBatch = 512;  // chunk records staged in LDS at a time
+constexpr int kStatBatch = 1024;  // chunk records staged in LDS at a time
 constexpr int kSerialChunks = 16;  // up to this many chunks a thread combines a node alone
 static_assert(kRowChunksMax <= kStatBatch, "a batch holds at least one node");
 constexpr float kLog2e = 1.4426950408889634f;
@@ -239,7 +239,7 @@ __global__ __launch_bounds__(kRowThreads) void sampling_accept_kernel(
   for (int nb0 = 0; nb0 < n; nb0 += npb) {
     const int nn = min(npb, n - nb0);
     const ChunkStat* src = ws + ((long long)b * Q + nb0) * S;
-#pragma unroll 2
+#pragma unroll 4
     for (int i = tid; i < nn * S; i += kRowThreads) s_cs[i] = src[i];
     __syncthreads();
     if (S <= kSerialChunks) {
