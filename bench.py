@@ -73,7 +73,7 @@ def source_digest():
 
 
 COPY_BYTES = 256 << 20  # the --copy-calibration copy
-ATTN_KERNELS = ("verify_attn_kernel", "verify_merge_kernel")
+ATTN_KERNELS = ("verify_attn_kernel", "verify_merge_kernel", "verify_merge_wide_kernel")
 
 
 def _counter_rows(directory):

@@ -234,6 +234,34 @@ __device__ __forceinline__ long long range_owner(long long t, long long W, long 
   return ((t + 1) * G - 1) / W;
 }
 
+// Work split when every request has the same row-tile and key-tile counts and
+// there are at least as many row tiles with work (units) as workgroups: unit u
+// is b * vt + rt.  Workgroup g takes the q = U / G whole units [g*q, g*q + q),
+// written directly, then an equal share of the r = U - q*G units left over,
+// laid out as one stream of r * nkb key tiles cut into G contiguous ranges (a
+// range cuts at most two units: r < G).  Otherwise the whole work is one
+// stream over (request, row tile, key tile) cut into G ranges.  The attention
+// kernel records the mode in ws_pref[B + 1]: U in the first case, -1 in the
+// second.  For a row tile with work, its place in the stream that holds it:
+// S (first key tile) and W (stream length); false for a whole unit.
+__device__ __forceinline__ bool stream_place(long long mode, const long long* pref, int B, int b,
+                                             int rt, const ReqInfo& ri, long long G, long long& S,
+                                             long long& W) {
+  if (mode >= 0) {
+    const long long q = mode / G, r = mode - q * G;
+    const long long u = (long long)b * ri.vt + rt;
+    if (u < q * G) return false;
+    S = (u - q * G) * ri.nkb;
+    W = r * ri.nkb;
+    return true;
+  }
+  S = pref[b] + (long long)rt * ri.nkb;
+  W = pref[B];
+  return true;
+}
+
+
+
 template <typename T, int DL, int DR>
 struct Smem {
   using G = Geo<T, DL, DR>;
@@ -994,14 +1022,14 @@ __device__ __forceinline__ void run_unit(Smem<T, DL, DR>& sm, const Args& a, con
   }
 }
 
-template <typename T, int DL, int DR>
+template <typename T, int DL, int DR, bool kSplit2>
 __global__ __launch_bounds__(kThreads) void verify_attn_kernel(
     const T* __restrict__ q_lat, const T* __restrict__ q_pe, const T* __restrict__ c_kv,
     const T* __restrict__ k_pe, int64_t num_slots, const int32_t* __restrict__ req_to_slot,
     int max_kv, const int32_t* __restrict__ prefix_len, const int32_t* __restrict__ n_nodes,
     const uint64_t* __restrict__ vis, int B, int Q, int H, int RT, float sm_scale,
     float* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o,
-    float* __restrict__ ws_lse, long long* __restrict__ ws_pref) {
+    float* __restrict__ ws_lse, long long* __restrict__ ws_pref, int G) {
   __shared__ Smem<T, DL, DR> sm;
   const Args args{q_lat, q_pe, c_kv, k_pe, num_slots, req_to_slot, max_kv, vis, Q, H,
                   sm_scale * kLog2e, out, lse, ws_o, ws_lse};
@@ -1011,17 +1039,64 @@ __global__ __launch_bounds__(kThreads) void verify_attn_kernel(
   int seq = 0;  // this wave's pair-sync sequence (see pair_post)
   work_prefix<kThreads>(sm.pref, sm.wsum, sm.req, prefix_len, n_nodes, B, Q, H, max_kv, RT);
   const long long Wtot = uni(sm.pref[B]);
-  if (blockIdx.x == 0)  // for the merge kernel
-    for (int i = threadIdx.x; i <= B; i += kThreads) ws_pref[i] = sm.pref[i];
-  const long long Gn = gridDim.x;
-  // Logical id: workgroups are dealt to the XCDs round-robin (blockIdx % 8), so
-  // XCD x gets the consecutive logical ids [start_x, start_x + count_x).
-  const long long xcd = blockIdx.x % kXcds;
-  const long long gid = xcd * (Gn / kXcds) + (xcd < Gn % kXcds ? xcd : Gn % kXcds) +
-                        blockIdx.x / kXcds;
-  const long long start = range_start(gid, Wtot, Gn);
-  const long long end = range_start(gid + 1, Wtot, Gn);
-  if (start >= end) return;
+  const long long Gn = G;
+  long long start, end, gid;
+  if constexpr (!kSplit2) {
+    if (blockIdx.x == 0) {  // for the merge kernels: the stream split
+      for (int i = threadIdx.x; i <= B; i += kThreads) ws_pref[i] = sm.pref[i];
+      if (threadIdx.x == 0) ws_pref[B + 1] = -1;
+    }
+    // Logical id: workgroups are dealt to the XCDs round-robin (blockIdx % 8),
+    // so XCD x gets the consecutive logical ids [start_x, start_x + count_x).
+    const long long xcd = blockIdx.x % kXcds;
+    gid = xcd * (Gn / kXcds) + (xcd < Gn % kXcds ? xcd : Gn % kXcds) + blockIdx.x / kXcds;
+    start = range_start(gid, Wtot, Gn);
+    end = range_start(gid + 1, Wtot, Gn);
+    if (start >= end) return;
+  } else {
+    // Launched with 2G workgroups for the aligned split (see stream_place):
+    // uniform requests (the same row-tile and key-tile counts) with at least
+    // one row tile of work per workgroup.  Unit u then covers tiles
+    // [u*nkb, (u+1)*nkb) of the stream; the first G workgroups (dispatched
+    // first) take the whole units, the second G the ranges of the leftover
+    // units, so each workgroup still walks one range of the stream.  Other
+    // requests take the stream split on the first G.
+    const bool second = blockIdx.x >= Gn;
+    const ReqInfo ri0 = req_info_ln(sm.req[0].x, sm.req[0].y, H, RT);
+    int same = 1;
+    for (int bb = threadIdx.x; bb < B; bb += kThreads) {
+      const ReqInfo r = req_info_ln(sm.req[bb].x, sm.req[bb].y, H, RT);
+      if (r.nkb != ri0.nkb || r.vt != ri0.vt) same = 0;
+    }
+    same = __syncthreads_and(same);
+    const long long U = (long long)B * ri0.vt;
+    const long long mode = (same && ri0.vt > 0 && U >= Gn) ? U : -1;
+    if (blockIdx.x == 0) {  // for the merge kernels
+      for (int i = threadIdx.x; i <= B; i += kThreads) ws_pref[i] = sm.pref[i];
+      if (threadIdx.x == 0) ws_pref[B + 1] = mode;
+    }
+    if (mode < 0 && second) return;
+    // Logical id within its half, dealt to the XCDs as above.
+    const long long bl = blockIdx.x - (second ? Gn : 0);
+    const long long xcd = bl % kXcds;
+    gid = xcd * (Gn / kXcds) + (xcd < Gn % kXcds ? xcd : Gn % kXcds) + bl / kXcds;
+    if (mode < 0) {
+      start = range_start(gid, Wtot, Gn);
+      end = range_start(gid + 1, Wtot, Gn);
+    } else {
+      const long long nkb = ri0.nkb, q = mode / Gn, r = mode - q * Gn;
+      if (!second) {
+        start = gid * q * nkb;
+        end = start + q * nkb;
+      } else {
+        start = q * Gn * nkb + range_start(gid, r * nkb, Gn);
+        end = q * Gn * nkb + range_start(gid + 1, r * nkb, Gn);
+      }
+    }
+    start = uni(start);
+    end = uni(end);
+    if (start >= end) return;
+  }
 
   // Request holding `start`: the last b with pref[b] <= start (it has work).
   int b = 0;
@@ -1114,13 +1189,15 @@ __global__ __launch_bounds__(kMergeThreads) void verify_merge_kernel(
   const long long QH = (long long)Q * H;
   const int r0 = blockIdx.y * MG::kRows;                   // first row within the tile
   if ((long long)rt * kRowsPerWG + r0 >= QH) return;
-  // Work prefix over requests, as the attention kernel computed it.
-  const long long Wtot = ws_pref[B];
+  // Work prefix over requests and the split mode, as the attention kernel
+  // recorded them.
   const long long Gn = grid_attn;
+  const long long mode = ws_pref[B + 1];
 
   const bool has_work = rt < ri.vt;
   if (has_work) {
-    const long long S_u = ws_pref[b] + (long long)rt * ri.nkb;
+    long long S_u, Wtot;
+    if (!stream_place(mode, ws_pref, B, b, rt, ri, Gn, S_u, Wtot)) return;  // a whole unit
     const long long g_first = range_owner(S_u, Wtot, Gn);
     const long long g_last = range_owner(S_u + ri.nkb - 1, Wtot, Gn);
     if (g_first == g_last) return;  // written directly by the attention kernel
@@ -1276,7 +1353,8 @@ template <int DL>
 __global__ __launch_bounds__(kMergeThreads) void verify_merge_wide_kernel(
     const int32_t* __restrict__ prefix_len, const int32_t* __restrict__ n_nodes, int B, int Q,
     int H, int RT, int max_kv, int grid_attn, float* __restrict__ out, float* __restrict__ lse,
-    const float* __restrict__ ws_o, const float* __restrict__ ws_lse) {
+    const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
+    const long long* __restrict__ ws_pref) {
   using MG = MergeGeoW<DL>;
   __shared__ long long s_pref[kMaxBatch + 1];
   __shared__ long long s_wsum[kMergeThreads / kWave];
@@ -1292,12 +1370,13 @@ __global__ __launch_bounds__(kMergeThreads) void verify_merge_wide_kernel(
   const long long QH = (long long)Q * H;
   const int r0 = blockIdx.y * MG::kRows;                   // first row within the tile
   if ((long long)rt * kRowsPerWG + r0 >= QH) return;
-  const long long Wtot = s_pref[B];
   const long long Gn = grid_attn;
+  const long long mode = ws_pref[B + 1];  // the split mode the attention kernel recorded
 
   const bool has_work = rt < ri.vt;
   if (has_work) {
-    const long long S_u = s_pref[b] + (long long)rt * ri.nkb;
+    long long S_u, Wtot;
+    if (!stream_place(mode, s_pref, B, b, rt, ri, Gn, S_u, Wtot)) return;  // a whole unit
     const long long g_first = range_owner(S_u, Wtot, Gn);
     const long long g_last = range_owner(S_u + ri.nkb - 1, Wtot, Gn);
     if (g_first == g_last) return;  // written directly by the attention kernel
@@ -1421,11 +1500,16 @@ hipError_t launch_impl(const void* q_lat, const void* q_pe, const void* c_kv, co
   float* ws_o = static_cast<float*>(workspace);
   float* ws_lse = ws_o + (size_t)2 * plan.grid * kRowsPerWG * DL;
   long long* ws_pref = reinterpret_cast<long long*>(ws_lse + (size_t)2 * plan.grid * kRowsPerWG);
-  hipLaunchKernelGGL((verify_attn_kernel<T, DL, DR>), dim3(plan.grid), dim3(kThreads), 0,
+  // Twice the workgroups, and the kernel that can take the aligned split, when
+  // that split can apply (B * row tiles >= G); the kernel decides from the data
+  // whether it does.
+  const bool split2 = (long long)B * plan.row_tiles >= plan.grid;
+  auto kernel = split2 ? verify_attn_kernel<T, DL, DR, true> : verify_attn_kernel<T, DL, DR, false>;
+  hipLaunchKernelGGL(kernel, dim3(split2 ? 2 * plan.grid : plan.grid), dim3(kThreads), 0,
                      stream, static_cast<const T*>(q_lat), static_cast<const T*>(q_pe),
                      static_cast<const T*>(c_kv), static_cast<const T*>(k_pe), num_slots,
                      req_to_slot, max_kv, prefix_len, n_nodes, vis, B, Q, H, plan.row_tiles,
-                     sm_scale, out, lse, ws_o, ws_lse, ws_pref);
+                     sm_scale, out, lse, ws_o, ws_lse, ws_pref, plan.grid);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // Thin merge workgroups (2 rows of 512) when there are so few row tiles that
@@ -1440,7 +1524,7 @@ hipError_t launch_impl(const void* q_lat, const void* q_pe, const void* c_kv, co
     hipLaunchKernelGGL((verify_merge_wide_kernel<DL>),
                        dim3(units, kRowsPerWG / MergeGeoW<DL>::kRows), dim3(kMergeThreads), 0,
                        stream, prefix_len, n_nodes, B, Q, H, plan.row_tiles, max_kv, plan.grid,
-                       out, lse, ws_o, ws_lse);
+                       out, lse, ws_o, ws_lse, ws_pref);
   return hipGetLastError();
 }
 
@@ -1476,9 +1560,9 @@ AttnPlan plan_verify_attn(int B, int Q, int H, int max_kv, int d_lat, int num_cu
   p.grid = (int)g;
   p.num_cu = num_cu > 0 ? num_cu : 256;
   // Partial outputs and log-sum-exps (two slots per workgroup), then the work
-  // prefix over requests that the merge kernel reads.
+  // prefix over requests and the split mode that the merge kernels read.
   p.ws_bytes = (size_t)2 * p.grid * kRowsPerWG * ((size_t)d_lat + 1) * sizeof(float) +
-               ((size_t)B + 1) * sizeof(long long);
+               ((size_t)B + 2) * sizeof(long long);
   return p;
 }
 
