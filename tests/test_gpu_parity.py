@@ -232,6 +232,13 @@ def tree_for(wl):
     ("b4_l4k_q17", {"L": 700}, True),
     ("b4_l4k_q33", {"L": 600, "B": 3}, False),
     ("b64_l2k_q9", {"B": 6, "L": 300}, True),
+    # Uniform batches of at least one row tile per workgroup take the aligned
+    # split: whole row tiles, then leftover ranges of 0-1 key tiles (L 40) or
+    # ranges crossing row tiles (L 520); ragged prefixes on the doubled grid fall
+    # back to the linear split.
+    ("b64_l2k_q9", {"L": 40}, True),
+    ("b64_l2k_q9", {"L": 520}, False),
+    ("b64_l2k_q9", {"L": 300, "L_jitter": 0.25}, True),
     ("b8_l32k_q65", {"B": 2, "L": 600}, True),
 ])
 def test_verify_attn_full_oracle(name, overrides, shuffle):
