@@ -47,7 +47,10 @@
 //    normalised partial outputs plus their log-sum-exp to the workspace and a
 //    merge kernel combines them; uncut tiles write the output directly.
 //    Logical workgroup ids are remapped so that consecutive ranges (same
-//    request, same keys) land on the same XCD and share its L2.
+//    request, same keys) land on the same XCD and share its L2.  Uniform
+//    batches with at least one row tile per workgroup take an aligned split
+//    instead (twice the workgroups: whole row tiles first, then the leftover
+//    row tiles cut evenly), which leaves far fewer row tiles to merge.
 #include <type_traits>
 
 #include "ddt_internal.h"
