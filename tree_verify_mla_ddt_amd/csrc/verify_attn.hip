@@ -1186,7 +1186,9 @@ __global__ __launch_bounds__(kMergeThreads) void verify_merge_kernel(
   __shared__ float s_lv[MG::kBatch][MG::kRows];  // LSEs of the first batch's contributors
   __shared__ float s_w[MG::kBatch][MG::kRows];
   const int tid = threadIdx.x;
-  const int u = blockIdx.x;
+  // Units in reverse: under the aligned split the row tiles to merge are the
+  // last ones, and are dispatched first this way.
+  const int u = (int)gridDim.x - 1 - (int)blockIdx.x;
   const int b = u / RT, rt = u % RT;
   const ReqInfo ri = req_info(prefix_len, n_nodes, b, Q, H, max_kv, RT);
   const long long QH = (long long)Q * H;
@@ -1365,16 +1367,21 @@ __global__ __launch_bounds__(kMergeThreads) void verify_merge_wide_kernel(
   __shared__ int s_cnt;
   __shared__ float s_lse[MG::kRows];
   __shared__ float s_w[kMergeBatchW][MG::kRows];
-  work_prefix<kMergeThreads>(s_pref, s_wsum, nullptr, prefix_len, n_nodes, B, Q, H, max_kv, RT);
+  // The split mode the attention kernel recorded; the aligned split needs no
+  // work prefix.
+  const long long mode = ws_pref[B + 1];
+  if (mode < 0)
+    work_prefix<kMergeThreads>(s_pref, s_wsum, nullptr, prefix_len, n_nodes, B, Q, H, max_kv, RT);
   const int tid = threadIdx.x;
-  const int u = blockIdx.x;
+  // Units in reverse: under the aligned split the row tiles to merge are the
+  // last ones, and are dispatched first this way.
+  const int u = (int)gridDim.x - 1 - (int)blockIdx.x;
   const int b = u / RT, rt = u % RT;
   const ReqInfo ri = req_info(prefix_len, n_nodes, b, Q, H, max_kv, RT);
   const long long QH = (long long)Q * H;
   const int r0 = blockIdx.y * MG::kRows;                   // first row within the tile
   if ((long long)rt * kRowsPerWG + r0 >= QH) return;
   const long long Gn = grid_attn;
-  const long long mode = ws_pref[B + 1];  // the split mode the attention kernel recorded
 
   const bool has_work = rt < ri.vt;
   if (has_work) {
