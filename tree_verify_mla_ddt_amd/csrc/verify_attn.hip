@@ -1474,7 +1474,7 @@ __global__ __launch_bounds__(kMergeThreads) void verify_merge_wide_kernel(
     __syncthreads();
     // Rows that no contributor wrote (not live) read stale workspace here; their
     // sums are discarded below, and every address stays inside the workspace.
-#pragma unroll 4
+#pragma unroll 8
     for (int k = 0; k < nk; ++k) {
       const float* src = ws_o + ((long long)s_src[k0 + k] * kRowsPerWG + r0) * DL + chunk * 4;
 #pragma unroll
