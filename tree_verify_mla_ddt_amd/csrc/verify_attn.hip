@@ -1025,28 +1025,20 @@ __device__ __forceinline__ void run_unit(Smem<T, DL, DR>& sm, const Args& a, con
   }
 }
 
-template <typename T, int DL, int DR, bool kSplit2>
-__global__ __launch_bounds__(kThreads) void verify_attn_kernel(
-    const T* __restrict__ q_lat, const T* __restrict__ q_pe, const T* __restrict__ c_kv,
-    const T* __restrict__ k_pe, int64_t num_slots, const int32_t* __restrict__ req_to_slot,
-    int max_kv, const int32_t* __restrict__ prefix_len, const int32_t* __restrict__ n_nodes,
-    const uint64_t* __restrict__ vis, int B, int Q, int H, int RT, float sm_scale,
-    float* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o,
-    float* __restrict__ ws_lse, long long* __restrict__ ws_pref, int G) {
-  __shared__ Smem<T, DL, DR> sm;
-  const Args args{q_lat, q_pe, c_kv, k_pe, num_slots, req_to_slot, max_kv, vis, Q, H,
-                  sm_scale * kLog2e, out, lse, ws_o, ws_lse};
-  const int half = uni((int)((threadIdx.x >> 6) & 1));  // share of the pair: wave % 2
-
-  if ((threadIdx.x & 63) == 0) sm.xflag[threadIdx.x >> 6] = 0;
-  int seq = 0;  // this wave's pair-sync sequence (see pair_post)
-  work_prefix<kThreads>(sm.pref, sm.wsum, sm.req, prefix_len, n_nodes, B, Q, H, max_kv, RT);
+// The units of this workgroup's share of the work, handed to `run` one by one.
+// Called by all kThr threads of the workgroup; SM provides pref, wsum and req.
+template <int kThr, bool kSplit2, class SM, class Run>
+__device__ __forceinline__ void for_each_unit(SM& sm, const int32_t* __restrict__ prefix_len,
+                                              const int32_t* __restrict__ n_nodes, int B, int Q,
+                                              int H, int max_kv, int RT,
+                                              long long* __restrict__ ws_pref, int G, Run&& run) {
+  work_prefix<kThr>(sm.pref, sm.wsum, sm.req, prefix_len, n_nodes, B, Q, H, max_kv, RT);
   const long long Wtot = uni(sm.pref[B]);
   const long long Gn = G;
   long long start, end, gid;
   if constexpr (!kSplit2) {
     if (blockIdx.x == 0) {  // for the merge kernels: the stream split
-      for (int i = threadIdx.x; i <= B; i += kThreads) ws_pref[i] = sm.pref[i];
+      for (int i = threadIdx.x; i <= B; i += kThr) ws_pref[i] = sm.pref[i];
       if (threadIdx.x == 0) ws_pref[B + 1] = -1;
     }
     // Logical id: workgroups are dealt to the XCDs round-robin (blockIdx % 8),
@@ -1067,7 +1059,7 @@ __global__ __launch_bounds__(kThreads) void verify_attn_kernel(
     const bool second = blockIdx.x >= Gn;
     const ReqInfo ri0 = req_info_ln(sm.req[0].x, sm.req[0].y, H, RT);
     int same = 1;
-    for (int bb = threadIdx.x; bb < B; bb += kThreads) {
+    for (int bb = threadIdx.x; bb < B; bb += kThr) {
       const ReqInfo r = req_info_ln(sm.req[bb].x, sm.req[bb].y, H, RT);
       if (r.nkb != ri0.nkb || r.vt != ri0.vt) same = 0;
     }
@@ -1075,7 +1067,7 @@ __global__ __launch_bounds__(kThreads) void verify_attn_kernel(
     const long long U = (long long)B * ri0.vt;
     const long long mode = (same && ri0.vt > 0 && U >= Gn) ? U : -1;
     if (blockIdx.x == 0) {  // for the merge kernels
-      for (int i = threadIdx.x; i <= B; i += kThreads) ws_pref[i] = sm.pref[i];
+      for (int i = threadIdx.x; i <= B; i += kThr) ws_pref[i] = sm.pref[i];
       if (threadIdx.x == 0) ws_pref[B + 1] = mode;
     }
     if (mode < 0 && second) return;
@@ -1141,11 +1133,542 @@ __global__ __launch_bounds__(kThreads) void verify_attn_kernel(
     u.nkeys = u.ri.L + u.ri.nb;
     pos += u.kb1 - u.kb0;
     if (head != (pass == 1)) continue;
-    if (half == 0) run_unit<T, DL, DR, 0>(sm, args, u, seq);
-    else run_unit<T, DL, DR, 1>(sm, args, u, seq);
+    run(u, gid);
     if (pass == 1) break;
   }
   }
+}
+
+template <typename T, int DL, int DR, bool kSplit2>
+__global__ __launch_bounds__(kThreads) void verify_attn_kernel(
+    const T* __restrict__ q_lat, const T* __restrict__ q_pe, const T* __restrict__ c_kv,
+    const T* __restrict__ k_pe, int64_t num_slots, const int32_t* __restrict__ req_to_slot,
+    int max_kv, const int32_t* __restrict__ prefix_len, const int32_t* __restrict__ n_nodes,
+    const uint64_t* __restrict__ vis, int B, int Q, int H, int RT, float sm_scale,
+    float* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o,
+    float* __restrict__ ws_lse, long long* __restrict__ ws_pref, int G) {
+  __shared__ Smem<T, DL, DR> sm;
+  const Args args{q_lat, q_pe, c_kv, k_pe, num_slots, req_to_slot, max_kv, vis, Q, H,
+                  sm_scale * kLog2e, out, lse, ws_o, ws_lse};
+  const int half = uni((int)((threadIdx.x >> 6) & 1));  // share of the pair: wave % 2
+  if ((threadIdx.x & 63) == 0) sm.xflag[threadIdx.x >> 6] = 0;
+  int seq = 0;  // this wave's pair-sync sequence (see pair_post)
+  for_each_unit<kThreads, kSplit2>(sm, prefix_len, n_nodes, B, Q, H, max_kv, RT, ws_pref, G,
+                                   [&](const Unit& u, long long) __attribute__((always_inline)) {
+                                     if (half == 0) run_unit<T, DL, DR, 0>(sm, args, u, seq);
+                                     else run_unit<T, DL, DR, 1>(sm, args, u, seq);
+                                   });
+}
+
+// ----------------------------------------------------------------------------
+// Wide form (bf16, 512 + 64): one wavefront per 32 rows, four per workgroup,
+// one per SIMD.  Each wave holds its rows' whole query (36 operand registers)
+// and whole output (16 accumulator blocks of 32 columns, the 256 accumulator
+// registers), so both contractions of a tile run inside one wave and the
+// softmax needs no exchange: a row's 32 scores sit in two lanes (l, l ^ 32).
+// Per tile a wave issues 36 QK^T and 32 PV MFMAs; the softmax of tile t is
+// computed while the value product of tile t-1 runs, so the matrix core of
+// the SIMD keeps a queue of independent MFMAs while the VALU works.
+constexpr int kWavesW = 4;
+constexpr int kThreadsW = kWavesW * kWave;
+
+template <int DL, int DR>
+struct SmemW {
+  using G = Geo<uint16_t, DL, DR>;
+  alignas(1024) unsigned char stage[kStages][G::kStageBytes];
+  alignas(16) int32_t slot[kRing][kTileKeys];  // pool slot of each key of a tile (0 when invalid)
+  uint32_t valid[kRing];            // bit m: key m of the tile is in range with a valid slot
+  uint64_t visrow[kRowsPerWG][2];   // visibility bitset of each row's tree node
+  alignas(128) unsigned char qpe[kRowsPerWG][DR * 2];  // rope part of the query tile
+  long long pref[kMaxBatch + 1];
+  int2 req[kMaxBatch];  // per request: clamped prefix length, tree size
+  long long wsum[kWavesW];
+};
+
+// Direct loads of one key tile by the four waves: wave w fills the latent rows
+// of keys 8w..8w+7 (one 1 KiB row per instruction, the slot read as a scalar)
+// and the rope rows of the same keys (one instruction of 8 keys x 8 chunks).
+// Measured on gfx950: issuing the nine loads together at the top of the tile
+// costs less than spreading them between the MFMAs.
+template <int DL, int DR>
+__device__ __forceinline__ void issue_tile_w(unsigned char* stage, const int32_t* ring_slots,
+                                             const uint16_t* __restrict__ c_kv,
+                                             const uint16_t* __restrict__ k_pe, int wave,
+                                             int lane) {
+  using G = Geo<uint16_t, DL, DR>;
+  static_assert(G::kLatChunks == kWave && G::kPeChunks == 8 && G::kLatInstr == 8 * kWavesW &&
+                    G::kPeInstr == kWavesW,
+                "wide tile loads");
+  const int4 s0 = *reinterpret_cast<const int4*>(ring_slots + wave * 8);
+  const int4 s1 = *reinterpret_cast<const int4*>(ring_slots + wave * 8 + 4);
+  const int pe_row = ring_slots[wave * 8 + (lane >> 3)];
+  const int rows[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int key = wave * 8 + it;
+    const long long row = uni(rows[it]);
+    dma16(static_cast<const void*>(c_kv + row * DL + (lane ^ swz(key)) * G::kPerChunk),
+          lds_addr(stage + key * G::kLatPitchB));
+  }
+  // 8 keys x 8 chunks; key & 7 == lane / 8, so the swizzled chunk depends on
+  // the lane only.
+  const uint16_t* src = k_pe + (long long)pe_row * DR + (((lane & 7) ^ (lane >> 3)) * G::kPerChunk);
+  dma16(static_cast<const void*>(src), lds_addr(stage + G::kLatBytes + wave * kWave * 16));
+}
+
+// Reference max of the wide form, in log2 units: a row's reference is the max
+// of its first tile with a visible key and does not move afterwards, so the
+// accumulators are never rescaled inside the tile loop.  A later score more
+// than kOverflowLog2 above it (probabilities up to 2^kOverflowLog2 keep every
+// sum far from fp32 overflow) makes the unit run again from its first tile
+// with each row's reference at the largest score of the whole range.
+constexpr float kOverflowLog2 = 64.0f;
+
+// One step of the score chain S^T += K Q^T with the accumulator in VGPRs, for
+// builds whose MFMAs default to AGPR accumulators (all 256 of them hold the
+// output).  The hazards the compiler cannot see through the asm are covered
+// here: two wait states before each MFMA (a VALU write of an operand just
+// before it), back-to-back steps accumulate into the same registers (no wait
+// needed), and after the last step the MFMA's result latency is waited out
+// before anything may read the scores.
+template <bool kFirst, bool kLast>
+__device__ __forceinline__ void mfma_qk(f32x16_t& s, bf16x8_t a, bf16x8_t b) {
+  if constexpr (kFirst)
+    __asm__ __volatile__("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
+                         : "=&v"(s) : "v"(a), "v"(b));
+  else if constexpr (kLast)
+    __asm__ __volatile__("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\t"
+                         "s_nop 7\n\ts_nop 7\n\ts_nop 5"
+                         : "+v"(s) : "v"(a), "v"(b));
+  else
+    __asm__ __volatile__("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                         : "+v"(s) : "v"(a), "v"(b));
+}
+
+template <int DL, int DR>
+__device__ __forceinline__ void run_unit_w(SmemW<DL, DR>& sm, const Args& a, const Unit& u) {
+  using G = Geo<uint16_t, DL, DR>;
+  using T = uint16_t;
+  constexpr int kNK = G::kNK;               // QK^T MFMAs per tile (576 / 16)
+  constexpr int kLatSteps = DL / G::kKStep;  // ... of them over the latent part
+  constexpr int kNCB = G::kNCB;             // 32-column output blocks
+  static_assert(G::kSwz && DR == 64 && kNK == 36 && kNCB == 16 && kLatSteps == 32,
+                "wide form shape");
+  const int tid = threadIdx.x;
+  const int wave = uni(tid >> 6);
+  int lane = tid;
+  __asm__ __volatile__("" : "+v"(lane));
+  lane &= 63;
+  const int n = lane & 31;
+  const int g = lane >> 5;
+  const int W = (a.Q + 63) >> 6;
+  const long long QH = (long long)a.Q * a.H;
+  const T* q_lat = static_cast<const T*>(a.q_lat);
+  const T* q_pe = static_cast<const T*>(a.q_pe);
+  const T* c_kv = static_cast<const T*>(a.c_kv);
+  const T* k_pe = static_cast<const T*>(a.k_pe);
+  const int32_t* slots_b = a.req_to_slot + (long long)u.b * a.max_kv;
+
+  const int rloc = wave * 32 + n;  // row within the tile
+  const long long r_loc = (long long)u.rt * kRowsPerWG + rloc;
+  int heads = a.H;
+  __asm__ __volatile__("" : "+s"(heads));
+  const int node = (int)(r_loc / heads);
+  const bool row_exists = r_loc < QH;
+  const bool row_live = row_exists && node < u.ri.nb;
+  const bool wave_live = __ballot(row_live) != 0;
+
+  // Slot ids of the unit's first two tiles, published to the ring, then the
+  // first tile's loads (done again when the unit restarts).
+  auto start_tiles = [&]() __attribute__((always_inline)) {
+    int32_t raw0 = -1, raw1 = -1;
+    if (tid < kTileKeys) {
+      raw0 = fetch_slot(slots_b, u.kb0 * kTileKeys + tid, u.nkeys);
+      if (u.kb0 + 1 < u.kb1) raw1 = fetch_slot(slots_b, (u.kb0 + 1) * kTileKeys + tid, u.nkeys);
+      publish_slots(sm.slot[u.kb0 % kRing], &sm.valid[u.kb0 % kRing], raw0, a.num_slots, tid);
+      if (u.kb0 + 1 < u.kb1)
+        publish_slots(sm.slot[(u.kb0 + 1) % kRing], &sm.valid[(u.kb0 + 1) % kRing], raw1,
+                      a.num_slots, tid);
+    }
+  };
+
+  uint64_t vis0 = 0, vis1 = 0;
+  if (g == 0 && row_live) {
+    const uint64_t* vr = a.vis + ((long long)u.b * a.Q + node) * W;
+    vis0 = vr[0];
+    if (W > 1) vis1 = vr[1];
+  }
+  start_tiles();
+  if (g == 0) {
+    sm.visrow[rloc][0] = vis0;
+    sm.visrow[rloc][1] = vis1;
+  }
+  __syncthreads();
+  issue_tile_w<DL, DR>(sm.stage[u.kb0 % kStages], sm.slot[u.kb0 % kRing], c_kv, k_pe, wave, lane);
+
+  // The latent query tile goes through LDS in two passes (dims 0..287, then
+  // 288..511) of 128 rows, parked in the two stages the first key tile does
+  // not use, and is read into registers; each load instruction reads 1 KiB of
+  // consecutive bytes.  The rope part stays in LDS (qpe), where the score
+  // MFMAs read it like the keys' rope rows.
+  bf16x8_t q[kLatSteps];
+  {
+    unsigned char* qst[2] = {sm.stage[(u.kb0 + 1) % kStages], sm.stage[(u.kb0 + 2) % kStages]};
+    const long long row0 = (long long)u.b * QH + (long long)u.rt * kRowsPerWG;
+    const long long rlast = (long long)u.b * QH + QH - 1;  // rows past it are clamped, unused
+    {
+      // Rope rows: 8 rows x 8 chunks per instruction, chunk c of row r stored
+      // at chunk c ^ (r & 7); rows 8i..8i+7 by instruction i.
+      constexpr int kPerWave = kRowsPerWG / 8 / kWavesW;
+#pragma unroll
+      for (int i = 0; i < kPerWave; ++i) {
+        const int r = (wave * kPerWave + i) * 8 + (lane >> 3);
+        long long gr = row0 + r;
+        gr = gr < rlast ? gr : rlast;
+        const T* src = q_pe + gr * DR + (((lane & 7) ^ (lane >> 3)) * G::kPerChunk);
+        dma16(static_cast<const void*>(src), lds_addr(&sm.qpe[(wave * kPerWave + i) * 8][0]));
+      }
+    }
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const int kQC = pass == 0 ? 36 : 28;                      // 16-byte chunks per row
+      const int kQPerWave = kRowsPerWG * kQC / kWave / kWavesW;  // instructions per wave
+      const int kQStageChunks = kRowsPerWG / 2 * kQC;             // 64 rows per stage
+#pragma unroll
+      for (int i = 0; i < kQPerWave; ++i) {
+        const int c0 = (wave * kQPerWave + i) * kWave;  // first chunk of this instruction
+        const int c = c0 + lane;
+        const int r = c / kQC, j = c - r * kQC;
+        long long gr = row0 + r;
+        gr = gr < rlast ? gr : rlast;
+        // Chunk j of pass p holds dims 288 p + 8 j .. +8.
+        const T* src = q_lat + gr * DL + 288 * pass + 8 * j;
+        const int h = c0 >= kQStageChunks ? 1 : 0;
+        dma16(static_cast<const void*>(src), lds_addr(qst[h] + 16 * (c0 - h * kQStageChunks)));
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      const uint32_t qrow = lds_addr(qst[rloc >> 6]) + (rloc & 63) * (kQC * 16);
+#pragma unroll
+      for (int kk = 0; kk < kQC / 2; ++kk) {
+        q[18 * pass + kk] = bf16x8_t{};
+        if (row_live)
+          q[18 * pass + kk] = *(const DDT_LDS bf16x8_t*)(uintptr_t)(qrow + 16 * (2 * kk + g));
+      }
+      __syncthreads();  // the stages are reused by the next pass and the loop
+    }
+  }
+
+  constexpr int kAhead = 4;    // score operand reads in flight ahead of the MFMAs
+  constexpr int kAheadPV = 6;  // value operand reads in flight ahead of the MFMAs
+
+  // m_ref: the row's reference max (log2 units), the same in both lanes of the
+  // row; m_seen: the largest scaled score so far; l_run: this lane's share of
+  // the row sum (its 16 keys of each tile).
+  float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.0f;
+  bool overflow = false;
+
+  // The softmax of a tile runs one tile late, in parts placed between the
+  // MFMAs of the next tile's QK^T (part A: row maxima, reference,
+  // probabilities) and of its own value product (part B: row sum and
+  // residual test), so the VALU work issues while the matrix core runs.  sv
+  // holds the tile's scores until the next tile's replace them; the fences
+  // keep each part where it is placed.
+  float sv[16];
+  float p[16];
+  float mh0 = 0.0f, mh1 = 0.0f, mref = 0.0f, psum = 0.0f;
+  bf16x8_t p0 = bf16x8_t{}, p1 = bf16x8_t{};
+  bool h0 = false, h1 = false;
+  auto part_a = [&](int j) __attribute__((always_inline)) {
+    if (j == 0) {
+      mh0 = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                  fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+      mh1 = fmaxf(fmaxf(fmaxf(sv[8], sv[9]), fmaxf(sv[10], sv[11])),
+                  fmaxf(fmaxf(sv[12], sv[13]), fmaxf(sv[14], sv[15])));
+    } else if (j == 1) {
+      // Maxima of the row over keys 0..15 and 16..31 (unscaled).
+      mh0 = xor32_max(mh0);
+      mh1 = xor32_max(mh1);
+      const float mt = fmaxf(mh0, mh1) * a.sl2;  // row max over the tile, log2 units
+      m_seen = fmaxf(m_seen, mt);
+      if (m_ref == -INFINITY) m_ref = mt;  // first visible key of the row (o is still 0)
+      overflow = overflow || mt > m_ref + kOverflowLog2;
+      mref = m_ref == -INFINITY ? 0.0f : m_ref;
+    } else if (j < 10) {
+      const int k = 2 * (j - 2);
+      p[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[k], a.sl2, -mref));
+      p[k + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[k + 1], a.sl2, -mref));
+    } else if (j == 10) {
+      p0 = pack_p<false>(p);
+    } else if (j == 11) {
+      p1 = pack_p<false>(p + 8);
+    } else if (j == 12) {
+      psum = (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]))) +
+             (((p[8] + p[9]) + (p[10] + p[11])) + ((p[12] + p[13]) + (p[14] + p[15])));
+    }
+  };
+  constexpr int kPartsA = 13;
+  auto part_b = [&](int j) __attribute__((always_inline)) {
+    if (j == 0) {
+      // Residual pass when some key's probability is a sizeable share of its
+      // row's running sum (a lower bound of the final sum, so the test errs
+      // towards the residual).
+      l_run += psum;
+      const float lrow = xor32_sum(l_run);
+      const float pm0 = __builtin_amdgcn_exp2f(__builtin_fmaf(mh0, a.sl2, -mref));
+      const float pm1 = __builtin_amdgcn_exp2f(__builtin_fmaf(mh1, a.sl2, -mref));
+      h0 = __ballot(pm0 > kHeavyShare * lrow) != 0;
+      h1 = __ballot(pm1 > kHeavyShare * lrow) != 0;
+    }
+  };
+  constexpr int kPartsB = 1;
+
+  // Invisible keys of tile kb get -inf in sv (prefix keys are always visible;
+  // a tree key when its bit is set in the row's node bitset; keys past the
+  // request or with an invalid slot never).  The scale (> 0) is applied
+  // inside the exponent.  Register i of sv is key 8*(i/4) + 4*g + (i%4).
+  auto mask = [&](int kb, int lane_it) __attribute__((always_inline)) {
+    const int key0 = kb * kTileKeys;
+    const uint32_t valid = (uint32_t)uni((int)sm.valid[kb % kRing]);
+    const bool tree_tile = key0 + kTileKeys > u.ri.L;
+    if (tree_tile || valid != 0xFFFFFFFFu) {
+      const int n = lane_it & 31;
+      const int g = lane_it >> 5;
+      uint32_t okm = valid;
+      if (tree_tile) {
+        const uint64_t* vr = sm.visrow[wave * 32 + n];
+        okm &= tree_window(vr[0], vr[1], key0 - u.ri.L);
+      }
+      okm >>= 4 * g;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        sv[i] = ((okm >> (8 * (i >> 2) + (i & 3))) & 1u) ? sv[i] : -INFINITY;
+    }
+  };
+
+  // S^T = K Q^T of tile kb over all 576 dims, into sv; part A of the previous
+  // tile's softmax runs between its MFMAs when `soft` (whose scores sv holds
+  // until the chain's result replaces them).  Operand reads run kAhead MFMAs
+  // ahead; the fences keep that order (the register budget would otherwise
+  // make the scheduler wait for every read).
+  auto do_qk = [&](int kb, int lane_it, auto kSoft) __attribute__((always_inline)) {
+    constexpr bool soft = decltype(kSoft)::value;
+    const int n = lane_it & 31;
+    const int g = lane_it >> 5;
+    const uint32_t kt = lds_addr(sm.stage[kb % kStages]);
+    // Permuted latent rows: logical chunk 2*step + g of key n is at byte
+    // n*1024 + 16*((2*step + g) ^ swz(n)) = (base ^ 32*(step % 8)) + 256*(step / 8).
+    const uint32_t qk_base = kt + n * G::kLatPitchB + 16 * (g ^ swz(n));
+    // Rope rows (keys and queries alike): logical chunk c of row n at
+    // physical chunk c ^ (n & 7); query row wave*32 + n has the same n & 7.
+    // Rope step k: logical chunk 2k + g at byte 16 * ((2k) ^ xswz) = base ^ 32k.
+    const int xswz = g ^ (n & 7);
+    const uint32_t pe_base = kt + G::kLatBytes + n * (DR * 2) + 16 * xswz;
+    const uint32_t qpe_base = lds_addr(&sm.qpe[wave * 32 + n][0]) + 16 * xswz;
+    auto kread = [&](int step) __attribute__((always_inline)) -> bf16x8_t {
+      if (step < kLatSteps)
+        return *(const DDT_LDS bf16x8_t*)(uintptr_t)((qk_base ^ ((step & 7) << 5)) +
+                                                     256 * (step >> 3));
+      return *(const DDT_LDS bf16x8_t*)(uintptr_t)(pe_base ^ (32 * (step - kLatSteps)));
+    };
+    auto qread = [&](int step) __attribute__((always_inline)) -> bf16x8_t {
+      if (step < kLatSteps) return q[step];
+      return *(const DDT_LDS bf16x8_t*)(uintptr_t)(qpe_base ^ (32 * (step - kLatSteps)));
+    };
+    bf16x8_t kop[kNK], qop[kNK];
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) {
+      kop[i] = kread(i);
+      qop[i] = qread(i);
+    }
+    f32x16_t s;
+#pragma unroll
+    for (int step = 0; step < kNK; ++step) {
+      if (step + kAhead < kNK) {
+        kop[step + kAhead] = kread(step + kAhead);
+        qop[step + kAhead] = qread(step + kAhead);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (step == 0) mfma_qk<true, false>(s, kop[step], qop[step]);
+      else if (step == kNK - 1) mfma_qk<false, true>(s, kop[step], qop[step]);
+      else mfma_qk<false, false>(s, kop[step], qop[step]);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (soft) {
+        if (step >= 2 && step % 2 == 0 && (step - 2) / 2 < kPartsA) part_a((step - 2) / 2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sv[i] = s[i];
+  };
+
+  f32x16_t o[kNCB];
+  // O^T += V^T P^T of tile kb over all 512 columns, part B of its softmax
+  // between the MFMAs.  MFMA i: column block i % 16, keys 16 * (i / 16) .. +15
+  // (probabilities p0, then p1), so consecutive MFMAs accumulate into
+  // different blocks.
+  auto do_pv = [&](int kb, int lane_it) __attribute__((always_inline)) {
+    const VtAddr va(lds_addr(sm.stage[kb % kStages]), lane_it);
+    bf16x8_t vop[2 * kNCB];
+#pragma unroll
+    for (int i = 0; i < kAheadPV; ++i) vop[i] = va.read(i % kNCB, i / kNCB);
+#pragma unroll
+    for (int i = 0; i < 2 * kNCB; ++i) {
+      if (i + kAheadPV < 2 * kNCB)
+        vop[i + kAheadPV] = va.read((i + kAheadPV) % kNCB, (i + kAheadPV) / kNCB);
+      __builtin_amdgcn_sched_barrier(0);
+      o[i % kNCB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[i], (i / kNCB) ? p1 : p0,
+                                                           o[i % kNCB], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i % 4 == 3 && i / 4 < kPartsB) part_b(i / 4);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Residual pass: (p - bf16(p)) of the key halves that hold a heavy key,
+    // through the same V^T operands.
+    if (h0) {
+      const bf16x8_t r = pack_p<true>(p);
+#pragma unroll
+      for (int cb = 0; cb < kNCB; ++cb)
+        o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va.read(cb, 0), r, o[cb], 0, 0, 0);
+    }
+    if (h1) {
+      const bf16x8_t r = pack_p<true>(p + 8);
+#pragma unroll
+      for (int cb = 0; cb < kNCB; ++cb)
+        o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va.read(cb, 1), r, o[cb], 0, 0, 0);
+    }
+  };
+
+  // Step kb: QK^T of tile kb (with part A of tile kb-1's softmax), then the
+  // value product of tile kb-1 (with part B); the unit's first step has no
+  // previous tile.
+  auto step = [&](int kb, auto kFirst) __attribute__((always_inline)) {
+    constexpr bool first = decltype(kFirst)::value;
+    // Lane-derived offsets are recomputed every tile from an opaque copy of the
+    // lane id: a handful of VALU ops instead of registers held across the loop.
+    int lane_it = lane;
+    __asm__ __volatile__("" : "+v"(lane_it));
+    int32_t ahead = -1;
+    if (tid < kTileKeys && kb + 2 < u.kb1)
+      ahead = fetch_slot(slots_b, (kb + 2) * kTileKeys + tid, u.nkeys);
+    // Tile kb+1 goes to the stage tile kb-2 used (every wave finished it
+    // before the previous iteration's closing barrier).
+    if (kb + 1 < u.kb1)
+      issue_tile_w<DL, DR>(sm.stage[(kb + 1) % kStages], sm.slot[(kb + 1) % kRing], c_kv, k_pe,
+                           wave, lane_it);
+    if (wave_live) {
+      if constexpr (first) {
+        do_qk(kb, lane_it, std::false_type{});
+      } else {
+        mask(kb - 1, lane_it);
+        do_qk(kb, lane_it, std::true_type{});  // tile kb's scores replace sv at its end
+        do_pv(kb - 1, lane_it);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile kb+1 have landed in LDS
+    if (tid < kTileKeys && kb + 2 < u.kb1)
+      publish_slots(sm.slot[(kb + 2) % kRing], &sm.valid[(kb + 2) % kRing], ahead, a.num_slots,
+                    tid);
+    __syncthreads();
+  };
+
+  for (int attempt = 0;; ++attempt) {
+#pragma unroll
+    for (int cb = 0; cb < kNCB; ++cb) o[cb] = f32x16_t{};
+    l_run = 0.0f;
+    if (attempt > 0) {
+      // The rerun: references at each row's largest score, which no tile of
+      // the range exceeds.
+      m_ref = m_seen;
+      start_tiles();
+      __syncthreads();
+      issue_tile_w<DL, DR>(sm.stage[u.kb0 % kStages], sm.slot[u.kb0 % kRing], c_kv, k_pe, wave,
+                           lane);
+    }
+    step(u.kb0, std::true_type{});
+    for (int kb = u.kb0 + 1; kb < u.kb1; ++kb) step(kb, std::false_type{});
+    // Drain: the last tile's softmax and value product.
+    if (wave_live) {
+      int lane_it = lane;
+      __asm__ __volatile__("" : "+v"(lane_it));
+      mask(u.kb1 - 1, lane_it);
+#pragma unroll
+      for (int j = 0; j < kPartsA; ++j) part_a(j);
+      do_pv(u.kb1 - 1, lane_it);
+    }
+    // Every wave's last value product has read the key stages before the
+    // epilogue (or a rerun) writes them.
+    if (!__syncthreads_or(attempt == 0 && overflow)) break;
+    overflow = false;
+  }
+
+  // Row sum over the two lanes of the row.
+  const float l = xor32_sum(l_run);
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  const float lse_v = l > 0.0f ? (m_ref + log2f(l)) * kLn2 : -INFINITY;
+  float* dst_lse = nullptr;
+  if (u.complete) {
+    if (row_exists && a.lse) dst_lse = a.lse + (long long)u.b * QH + r_loc;
+  } else if (row_live) {
+    dst_lse = a.ws_lse + u.slot * kRowsPerWG + rloc;
+  }
+  // Rows go out through LDS (the key stages are free now): each pass parks 64
+  // columns of this wave's 32 rows, then every store instruction writes four
+  // 256-byte row segments.
+  constexpr int kPCb = 2, kPCols = 32 * kPCb, kPitch = kPCols + 4;  // floats
+  static_assert(kWavesW * 32 * kPitch * 4 <= kStages * G::kStageBytes, "epilogue staging");
+  float* buf = reinterpret_cast<float*>(sm.stage[0]) + wave * (32 * kPitch);
+  const uint32_t live_m = (uint32_t)__ballot(row_live);  // bit r: row r of this wave
+  const uint32_t exist_m = (uint32_t)__ballot(row_exists);
+  const uint32_t write_m = u.complete ? exist_m : live_m;
+  float* base = u.complete
+                    ? a.out + ((long long)u.b * QH + (long long)u.rt * kRowsPerWG + wave * 32) * DL
+                    : a.ws_o + ((long long)u.slot * kRowsPerWG + wave * 32) * DL;
+  const int c4 = lane & 15;
+#pragma unroll
+  for (int pass = 0; pass < kNCB / kPCb; ++pass) {
+#pragma unroll
+    for (int c = 0; c < kPCb; ++c) {
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4) {
+        const int cb = pass * kPCb + c;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (row_live)
+          v = make_float4(o[cb][4 * t4] * inv, o[cb][4 * t4 + 1] * inv, o[cb][4 * t4 + 2] * inv,
+                          o[cb][4 * t4 + 3] * inv);
+        *reinterpret_cast<float4*>(buf + n * kPitch + c * 32 + 8 * t4 + 4 * g) = v;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's parked rows are in LDS
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 4 * i + (lane >> 4);
+      const float4 v = *reinterpret_cast<const float4*>(buf + r * kPitch + 4 * c4);
+      float* d = base + (long long)r * DL + pass * kPCols + 4 * c4;
+      if ((write_m >> r) & 1u) *reinterpret_cast<float4*>(d) = v;
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next pass overwrites
+  }
+  if (dst_lse && g == 0) *dst_lse = row_live ? lse_v : -INFINITY;
+}
+
+template <int DL, int DR, bool kSplit2>
+__global__ __launch_bounds__(kThreadsW, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void verify_attn_wide_kernel(
+    const uint16_t* __restrict__ q_lat, const uint16_t* __restrict__ q_pe,
+    const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ k_pe, int64_t num_slots,
+    const int32_t* __restrict__ req_to_slot, int max_kv, const int32_t* __restrict__ prefix_len,
+    const int32_t* __restrict__ n_nodes, const uint64_t* __restrict__ vis, int B, int Q, int H,
+    int RT, float sm_scale, float* __restrict__ out, float* __restrict__ lse,
+    float* __restrict__ ws_o, float* __restrict__ ws_lse, long long* __restrict__ ws_pref,
+    int G) {
+  __shared__ SmemW<DL, DR> sm;
+  const Args args{q_lat, q_pe, c_kv, k_pe, num_slots, req_to_slot, max_kv, vis, Q, H,
+                  sm_scale * kLog2e, out, lse, ws_o, ws_lse};
+  for_each_unit<kThreadsW, kSplit2>(sm, prefix_len, n_nodes, B, Q, H, max_kv, RT, ws_pref, G,
+                                    [&](const Unit& u, long long) __attribute__((always_inline)) {
+                                      run_unit_w<DL, DR>(sm, args, u);
+                                    });
 }
 
 // Combines the partial results of row tiles whose key range was cut, and writes
@@ -1514,12 +2037,23 @@ hipError_t launch_impl(const void* q_lat, const void* q_pe, const void* c_kv, co
   // that split can apply (B * row tiles >= G); the kernel decides from the data
   // whether it does.
   const bool split2 = (long long)B * plan.row_tiles >= plan.grid;
-  auto kernel = split2 ? verify_attn_kernel<T, DL, DR, true> : verify_attn_kernel<T, DL, DR, false>;
-  hipLaunchKernelGGL(kernel, dim3(split2 ? 2 * plan.grid : plan.grid), dim3(kThreads), 0,
-                     stream, static_cast<const T*>(q_lat), static_cast<const T*>(q_pe),
-                     static_cast<const T*>(c_kv), static_cast<const T*>(k_pe), num_slots,
-                     req_to_slot, max_kv, prefix_len, n_nodes, vis, B, Q, H, plan.row_tiles,
-                     sm_scale, out, lse, ws_o, ws_lse, ws_pref, plan.grid);
+  if constexpr (Geo<T, DL, DR>::kBF16 && DL == 512 && DR == 64) {
+    auto kernel = split2 ? verify_attn_wide_kernel<DL, DR, true>
+                         : verify_attn_wide_kernel<DL, DR, false>;
+    hipLaunchKernelGGL(kernel, dim3(split2 ? 2 * plan.grid : plan.grid), dim3(kThreadsW), 0,
+                       stream, static_cast<const T*>(q_lat), static_cast<const T*>(q_pe),
+                       static_cast<const T*>(c_kv), static_cast<const T*>(k_pe), num_slots,
+                       req_to_slot, max_kv, prefix_len, n_nodes, vis, B, Q, H, plan.row_tiles,
+                       sm_scale, out, lse, ws_o, ws_lse, ws_pref, plan.grid);
+  } else {
+    auto kernel =
+        split2 ? verify_attn_kernel<T, DL, DR, true> : verify_attn_kernel<T, DL, DR, false>;
+    hipLaunchKernelGGL(kernel, dim3(split2 ? 2 * plan.grid : plan.grid), dim3(kThreads), 0,
+                       stream, static_cast<const T*>(q_lat), static_cast<const T*>(q_pe),
+                       static_cast<const T*>(c_kv), static_cast<const T*>(k_pe), num_slots,
+                       req_to_slot, max_kv, prefix_len, n_nodes, vis, B, Q, H, plan.row_tiles,
+                       sm_scale, out, lse, ws_o, ws_lse, ws_pref, plan.grid);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // Thin merge workgroups (2 rows of 512) when there are so few row tiles that
