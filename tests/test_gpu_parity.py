@@ -9,9 +9,9 @@
   host round-trip equals the oracle chain.
 
 Workloads are the seeded generators of tree_verify_mla_ddt_amd.workloads, at the
-benchmark's full sizes (attention sampled row by row where the oracle would be
-slow) and at reduced sizes that still span several row tiles, key tiles and a
-ragged tail.
+benchmark's full sizes (every row; at the max shape every row of the request
+whose row tiles take the most merged ranges, sampled rows elsewhere) and at
+reduced sizes that still span several row tiles, key tiles and a ragged tail.
 """
 import math
 import sys
@@ -240,6 +240,15 @@ def tree_for(wl):
     ("b64_l2k_q9", {"L": 520}, False),
     ("b64_l2k_q9", {"L": 300, "L_jitter": 0.25}, True),
     ("b8_l32k_q65", {"B": 2, "L": 600}, True),
+    # Q=65 with eight uniform requests: 264 row tiles, at least one per
+    # workgroup, so the aligned split runs (eight leftover row tiles, each
+    # merged from about 32 contributors).
+    ("b8_l32k_q65", {"L": 600}, True),
+    # The bf16 64+16 instantiation: one row tile, and several with ragged
+    # prefixes and two-word bitsets.
+    ("tiny_fp32", {"dtype": "bf16"}, True),
+    ("tiny_fp32", {"dtype": "bf16", "B": 3, "H": 16, "L": 300, "L_jitter": 0.3,
+                   "budget": 70, "D": 9, "K": 4}, True),
 ])
 def test_verify_attn_full_oracle(name, overrides, shuffle):
     """Every row against the oracle at sizes it evaluates in seconds."""
@@ -251,34 +260,40 @@ def test_verify_attn_full_oracle(name, overrides, shuffle):
     check_attn(g_out, g_lse, o_out, o_lse, TOL[wl.dtype], name)
 
 
-def sample_rows(rng, wl, n_nodes, per_req):
-    rows = []
-    for b in range(wl.B):
-        nodes = rng.integers(0, wl.Q, size=per_req)
-        nodes[: min(4, per_req)] = [0, wl.Q - 1, int(n_nodes[b]) - 1, min(1, wl.Q - 1)][: min(4, per_req)]
-        heads = rng.integers(0, wl.H, size=per_req)
-        rows += [(b, int(i), int(h)) for i, h in zip(nodes, heads)]
-    return np.array(rows, np.int32)
-
-
-@pytest.mark.parametrize("name,per_req", [("b1_l2k_q9", 96), ("b4_l4k_q17", 48),
-                                          ("b4_l4k_q33", 48), ("b64_l2k_q9", 6),
-                                          ("b8_l32k_q65", 12)])
-def test_verify_attn_full_size_sampled(name, per_req):
-    """The benchmark's full workloads, in the benchmark's launch configuration;
-    sampled rows (including node 0, the last slot and the last live node of
-    every request) against the oracle, plus finiteness of every output."""
-    note(f"verify_attn full-size {name}")
+@pytest.mark.parametrize("name", ["b1_l2k_q9", "b4_l4k_q17", "b4_l4k_q33", "b64_l2k_q9"])
+def test_verify_attn_full_size_every_row(name):
+    """The benchmark's full workloads, in the benchmark's launch configuration,
+    every row against the oracle."""
+    note(f"verify_attn full-size every row {name}")
     wl = workloads.make_workload(name)
     t = tree_for(wl)
     g_out, g_lse = gpu_attn(wl, wl.req_to_slot, wl.prefix_len, t["n_nodes"], t["vis"])
-    rng = np.random.default_rng(5)
-    rows = sample_rows(rng, wl, t["n_nodes"], per_req)
-    o_out, o_lse = oracle_attn(wl, wl.req_to_slot, wl.prefix_len, t["n_nodes"], t["vis"], rows=rows)
-    gsel = g_out[rows[:, 0], rows[:, 1], rows[:, 2]]
-    lsel = g_lse[rows[:, 0], rows[:, 1], rows[:, 2]]
+    o_out, o_lse = oracle_attn(wl, wl.req_to_slot, wl.prefix_len, t["n_nodes"], t["vis"])
+    check_attn(g_out, g_lse, o_out, o_lse, TOL[wl.dtype], name)
+
+
+def test_verify_attn_max_shape():
+    """The max shape (batch 8, prefix 32768, q_len 65) in the benchmark's launch
+    configuration: every row of the last request (its row tiles hold the
+    aligned split's leftover ranges, merged from about 32 contributors each)
+    and 12 sampled rows of every other request against the oracle, and every
+    output finite."""
+    note("verify_attn max shape")
+    wl = workloads.make_workload("b8_l32k_q65")
+    t = tree_for(wl)
+    g_out, g_lse = gpu_attn(wl, wl.req_to_slot, wl.prefix_len, t["n_nodes"], t["vis"])
     assert np.isfinite(g_out).all()
-    check_attn(gsel, lsel, o_out, o_lse, TOL[wl.dtype], name)
+    rng = np.random.default_rng(5)
+    last = wl.B - 1
+    rows = [(last, i, h) for i in range(wl.Q) for h in range(wl.H)]
+    for b in range(last):
+        nodes = rng.integers(0, int(t["n_nodes"][b]), size=12)
+        nodes[:2] = [0, int(t["n_nodes"][b]) - 1]
+        rows += [(b, int(i), int(h)) for i, h in zip(nodes, rng.integers(0, wl.H, size=12))]
+    rows = np.array(rows, np.int32)
+    o_out, o_lse = oracle_attn(wl, wl.req_to_slot, wl.prefix_len, t["n_nodes"], t["vis"], rows=rows)
+    check_attn(g_out[rows[:, 0], rows[:, 1], rows[:, 2]], g_lse[rows[:, 0], rows[:, 1], rows[:, 2]],
+               o_out, o_lse, TOL[wl.dtype], "b8_l32k_q65")
 
 
 def test_verify_attn_edge_cases():

@@ -216,3 +216,57 @@ def test_band_and_margin_diagnostics():
     o0 = run(x.numpy(), T, t["node_token"], t["parent"], t["n_nodes"], coins, cfin, eps=0.0)
     np.testing.assert_array_equal(o0["bonus_lo"], o0["next_root"])
     np.testing.assert_array_equal(o0["bonus_hi"], o0["next_root"])
+
+
+def _numpy_band(x, T, rejected, coin_final, eps):
+    """The bonus band written out with NumPy: the residual distribution
+    (softmax(x / T) in float64 without the rejected tokens), its CDF by
+    cumulative sum, and every entry with mass whose CDF interval
+    [cdf - p, cdf] comes within eps * Zr of the draw coin_final * Zr."""
+    p = scipy.special.softmax(x.astype(np.float64) / T)
+    keep = np.ones_like(p, dtype=bool)
+    keep[list(rejected)] = False
+    keep &= p > 0
+    r = np.where(keep, p, 0.0)
+    Zr = r.sum()
+    target = float(coin_final) * Zr
+    hi = np.cumsum(r)
+    lo = hi - r
+    inband = keep & (hi >= target - eps * Zr) & (lo <= target + eps * Zr)
+    drawn = int(np.flatnonzero(keep & (hi > target))[0])
+    idx = np.flatnonzero(inband)
+    return drawn, int(idx.min()), int(idx.max())
+
+
+@pytest.mark.parametrize("eps", [1e-5, 1e-3, 3e-2])
+def test_bonus_band_width_against_numpy_cdf(eps):
+    """The band the oracle reports at eps > 0 (the set of bonus tokens a
+    sampler within eps of the draw may return) equals the band computed
+    independently from a NumPy cumulative sum, on a root-only tree (residual =
+    target) and on a root whose two children are both rejected (residual
+    without their tokens)."""
+    rng = np.random.default_rng(17)
+    V = 4000
+    for case in range(40):
+        T = float(rng.choice([0.5, 1.0, 1.7]))
+        x = (rng.normal(0, 2, size=V)).astype(np.float32)
+        cf = np.float32(rng.random())
+        if case % 2 == 0:
+            tok = np.array([[0, -1, -1]], np.int32)
+            par = np.array([[-1, -1, -1]], np.int32)
+            nn, rejected = 1, set()
+            coins = np.zeros((1, 3), np.float32)
+        else:
+            t1, t2 = (int(v) for v in rng.choice(V, size=2, replace=False))
+            tok = np.array([[0, t1, t2]], np.int32)
+            par = np.array([[-1, 0, 0]], np.int32)
+            nn, rejected = 3, {t1, t2}
+            coins = np.array([[0.0, 0.999999, 0.999999]], np.float32)
+            x[t1] = x[t2] = -3.0  # small enough that both are rejected
+        z = np.zeros((1, 3, V), np.float32)
+        z[0, 0] = x
+        o = run(z, [T], tok, par, [nn], coins, [cf], eps=eps)
+        assert o["accept_len"][0] == 1
+        drawn, lo, hi = _numpy_band(x, T, rejected, cf, eps)
+        assert o["next_root"][0] == drawn
+        assert (o["bonus_lo"][0], o["bonus_hi"][0]) == (lo, hi), (case, eps)

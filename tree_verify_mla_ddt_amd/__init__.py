@@ -95,18 +95,47 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def _dev(t: torch.Tensor, name: str, dtype, ndim: int | None = None):
+def _dev(t: torch.Tensor, name: str, dtype, ndim: int | None = None, shape=None, device=None):
+    """A contiguous GPU tensor of `dtype`; with `shape`, exactly that shape, and
+    with `device`, on that device (every array of a call is on one GPU)."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the other arrays on {device}")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     return t
+
+
+def _workspace(ws: torch.Tensor | None, need: int, device) -> torch.Tensor:
+    """The caller's workspace (a contiguous uint8 GPU tensor on `device`, at least
+    `need` bytes), or a new one."""
+    if ws is None:
+        return torch.empty((max(1, need),), dtype=torch.uint8, device=device)
+    _dev(ws, "workspace", torch.uint8, 1, device=device)
+    if ws.numel() < need:
+        raise ValueError(f"workspace of {ws.numel()} bytes given, {need} needed")
+    return ws
+
+
+def _out_dict(out: dict | None, spec: dict, device) -> dict:
+    """Output arrays: the caller's (each checked against its dtype and shape)
+    or new ones.  spec: name -> (dtype, shape)."""
+    if out is None:
+        return {k: torch.empty(shp, dtype=dt, device=device) for k, (dt, shp) in spec.items()}
+    for k, (dt, shp) in spec.items():
+        if k not in out:
+            raise KeyError(f"out is missing {k!r}")
+        _dev(out[k], k, dt, shape=shp, device=device)
+    return out
 
 
 def tree_build(topk_logp: torch.Tensor, topk_ids: torch.Tensor, root_token: torch.Tensor,
@@ -118,21 +147,19 @@ def tree_build(topk_logp: torch.Tensor, topk_ids: torch.Tensor, root_token: torc
     score [B,Q] f32, vis [B,Q,W] int64 (bit pattern of the u64 bitsets), n_nodes [B] i32.
     """
     _dev(topk_logp, "topk_logp", torch.float32, 3)
-    _dev(topk_ids, "topk_ids", torch.int32, 3)
-    _dev(root_token, "root_token", torch.int32, 1)
-    _dev(prefix_len, "prefix_len", torch.int32, 1)
+    dev = topk_logp.device
     B, D, K = topk_logp.shape
-    if tuple(topk_ids.shape) != (B, D, K) or root_token.numel() != B or prefix_len.numel() != B:
-        raise ValueError("inconsistent shapes")
+    _dev(topk_ids, "topk_ids", torch.int32, shape=(B, D, K), device=dev)
+    _dev(root_token, "root_token", torch.int32, shape=(B,), device=dev)
+    _dev(prefix_len, "prefix_len", torch.int32, shape=(B,), device=dev)
     Q = budget + 1
     W = (Q + 63) // 64
-    dev = topk_logp.device
-    if out is None:
-        out = {k: torch.empty((B, Q), dtype=torch.int32, device=dev) for k in
-               ("node_token", "parent", "depth", "position", "first_child", "next_sibling")}
-        out["score"] = torch.empty((B, Q), dtype=torch.float32, device=dev)
-        out["vis"] = torch.empty((B, Q, W), dtype=torch.int64, device=dev)
-        out["n_nodes"] = torch.empty((B,), dtype=torch.int32, device=dev)
+    spec = {k: (torch.int32, (B, Q)) for k in
+            ("node_token", "parent", "depth", "position", "first_child", "next_sibling")}
+    spec["score"] = (torch.float32, (B, Q))
+    spec["vis"] = (torch.int64, (B, Q, W))
+    spec["n_nodes"] = (torch.int32, (B,))
+    out = _out_dict(out, spec, dev)
     rc = load_library().ddt_tree_build(
         _ptr(topk_logp), _ptr(topk_ids), _ptr(root_token), _ptr(prefix_len), B, D, K, budget,
         _ptr(out["node_token"]), _ptr(out["parent"]), _ptr(out["depth"]), _ptr(out["position"]),
@@ -160,34 +187,36 @@ def verify_attn(q_lat: torch.Tensor, q_pe: torch.Tensor, c_kv: torch.Tensor, k_p
     if dt not in (torch.bfloat16, torch.float32):
         raise TypeError("q_lat must be bf16 or f32")
     _dev(q_lat, "q_lat", dt, 4)
-    _dev(q_pe, "q_pe", dt, 4)
-    _dev(c_kv, "c_kv", dt, 2)
-    _dev(k_pe, "k_pe", dt, 2)
-    _dev(req_to_slot, "req_to_slot", torch.int32, 2)
-    _dev(prefix_len, "prefix_len", torch.int32, 1)
-    _dev(n_nodes, "n_nodes", torch.int32, 1)
-    _dev(vis, "vis", torch.int64, 3)
-    B, Q, H, d_lat = q_lat.shape
-    d_rope = q_pe.shape[-1]
-    max_kv = req_to_slot.shape[1]
-    if (tuple(q_pe.shape[:3]) != (B, Q, H) or c_kv.shape[1] != d_lat or k_pe.shape[1] != d_rope
-            or k_pe.shape[0] != c_kv.shape[0] or req_to_slot.shape[0] != B
-            or tuple(vis.shape) != (B, Q, (Q + 63) // 64)):
-        raise ValueError("inconsistent shapes")
     dev = q_lat.device
+    B, Q, H, d_lat = q_lat.shape
+    _dev(q_pe, "q_pe", dt, 4, device=dev)
+    d_rope = q_pe.shape[-1]
+    _dev(q_pe, "q_pe", dt, shape=(B, Q, H, d_rope))
+    _dev(c_kv, "c_kv", dt, 2, device=dev)
+    S = c_kv.shape[0]
+    _dev(c_kv, "c_kv", dt, shape=(S, d_lat))
+    _dev(k_pe, "k_pe", dt, shape=(S, d_rope), device=dev)
+    _dev(req_to_slot, "req_to_slot", torch.int32, 2, device=dev)
+    max_kv = req_to_slot.shape[1]
+    _dev(req_to_slot, "req_to_slot", torch.int32, shape=(B, max_kv))
+    _dev(prefix_len, "prefix_len", torch.int32, shape=(B,), device=dev)
+    _dev(n_nodes, "n_nodes", torch.int32, shape=(B,), device=dev)
+    _dev(vis, "vis", torch.int64, shape=(B, Q, (Q + 63) // 64), device=dev)
     if out is None:
         out = torch.empty((B, Q, H, d_lat), dtype=torch.float32, device=dev)
+    _dev(out, "out", torch.float32, shape=(B, Q, H, d_lat), device=dev)
     if lse is None and want_lse:
         lse = torch.empty((B, Q, H), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32, shape=(B, Q, H), device=dev)
     lib = load_library()
     need = int(lib.ddt_verify_attn_workspace_size(B, Q, H, max_kv, d_lat))
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, need, dev)
     rc = lib.ddt_verify_attn(
         _ptr(q_lat), _ptr(q_pe), _ptr(c_kv), _ptr(k_pe), c_kv.shape[0], _ptr(req_to_slot), max_kv,
         _ptr(prefix_len), _ptr(n_nodes), _ptr(vis), B, Q, H, d_lat, d_rope,
         DDT_BF16 if dt == torch.bfloat16 else DDT_F32, float(sm_scale), _ptr(out), _ptr(lse),
-        _ptr(workspace), workspace.numel(), _stream())
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream())
     _check(rc)
     return out, lse
 
@@ -196,16 +225,15 @@ def tree_accept(node_token: torch.Tensor, parent: torch.Tensor, n_nodes: torch.T
                 target_argmax: torch.Tensor, out: dict | None = None) -> dict:
     """Greedy follow-the-verified-tree acceptance (ddt_tree_accept)."""
     _dev(node_token, "node_token", torch.int32, 2)
-    _dev(parent, "parent", torch.int32, 2)
-    _dev(n_nodes, "n_nodes", torch.int32, 1)
-    _dev(target_argmax, "target_argmax", torch.int32, 2)
-    B, Q = node_token.shape
     dev = node_token.device
-    if out is None:
-        out = {"accept_len": torch.empty((B,), dtype=torch.int32, device=dev),
-               "accept_nodes": torch.empty((B, Q), dtype=torch.int32, device=dev),
-               "out_tokens": torch.empty((B, Q), dtype=torch.int32, device=dev),
-               "next_root": torch.empty((B,), dtype=torch.int32, device=dev)}
+    B, Q = node_token.shape
+    _dev(parent, "parent", torch.int32, shape=(B, Q), device=dev)
+    _dev(n_nodes, "n_nodes", torch.int32, shape=(B,), device=dev)
+    _dev(target_argmax, "target_argmax", torch.int32, shape=(B, Q), device=dev)
+    out = _out_dict(out, {"accept_len": (torch.int32, (B,)),
+                          "accept_nodes": (torch.int32, (B, Q)),
+                          "out_tokens": (torch.int32, (B, Q)),
+                          "next_root": (torch.int32, (B,))}, dev)
     rc = load_library().ddt_tree_accept(
         _ptr(node_token), _ptr(parent), _ptr(n_nodes), _ptr(target_argmax), B, Q,
         _ptr(out["accept_len"]), _ptr(out["accept_nodes"]), _ptr(out["out_tokens"]),
@@ -226,26 +254,21 @@ def tree_accept_sampling(target_logits: torch.Tensor, temperature: torch.Tensor,
     if dt not in (torch.bfloat16, torch.float32):
         raise TypeError("target_logits must be bf16 or f32")
     _dev(target_logits, "target_logits", dt, 3)
-    _dev(temperature, "temperature", torch.float32, 1)
-    _dev(node_token, "node_token", torch.int32, 2)
-    _dev(parent, "parent", torch.int32, 2)
-    _dev(n_nodes, "n_nodes", torch.int32, 1)
-    _dev(coins, "coins", torch.float32, 2)
-    _dev(coin_final, "coin_final", torch.float32, 1)
-    B, Q, V = target_logits.shape
-    if (node_token.shape != (B, Q) or parent.shape != (B, Q) or coins.shape != (B, Q)
-            or n_nodes.shape != (B,) or temperature.shape != (B,) or coin_final.shape != (B,)):
-        raise ValueError("shapes of the tree, temperature and coins must match target_logits")
-    lib = load_library()
     dev = target_logits.device
-    if out is None:
-        out = {"accept_len": torch.empty((B,), dtype=torch.int32, device=dev),
-               "accept_nodes": torch.empty((B, Q), dtype=torch.int32, device=dev),
-               "out_tokens": torch.empty((B, Q), dtype=torch.int32, device=dev),
-               "next_root": torch.empty((B,), dtype=torch.int32, device=dev)}
+    B, Q, V = target_logits.shape
+    _dev(temperature, "temperature", torch.float32, shape=(B,), device=dev)
+    _dev(node_token, "node_token", torch.int32, shape=(B, Q), device=dev)
+    _dev(parent, "parent", torch.int32, shape=(B, Q), device=dev)
+    _dev(n_nodes, "n_nodes", torch.int32, shape=(B,), device=dev)
+    _dev(coins, "coins", torch.float32, shape=(B, Q), device=dev)
+    _dev(coin_final, "coin_final", torch.float32, shape=(B,), device=dev)
+    lib = load_library()
+    out = _out_dict(out, {"accept_len": (torch.int32, (B,)),
+                          "accept_nodes": (torch.int32, (B, Q)),
+                          "out_tokens": (torch.int32, (B, Q)),
+                          "next_root": (torch.int32, (B,))}, dev)
     need = int(lib.ddt_tree_accept_sampling_workspace_size(B, Q, V))
-    if workspace is None:
-        workspace = torch.empty((max(1, need),), dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, need, dev)
     rc = lib.ddt_tree_accept_sampling(
         _ptr(target_logits), DDT_BF16 if dt == torch.bfloat16 else DDT_F32, V, _ptr(temperature),
         _ptr(node_token), _ptr(parent), _ptr(n_nodes), _ptr(coins), _ptr(coin_final), B, Q,
@@ -264,15 +287,13 @@ def draft_topk(logits: torch.Tensor, K: int, out: dict | None = None,
     if dt not in (torch.bfloat16, torch.float32):
         raise TypeError("logits must be bf16 or f32")
     _dev(logits, "logits", dt, 3)
+    dev = logits.device
     B, D, V = logits.shape
     lib = load_library()
-    dev = logits.device
-    if out is None:
-        out = {"topk_logp": torch.empty((B, D, K), dtype=torch.float32, device=dev),
-               "topk_ids": torch.empty((B, D, K), dtype=torch.int32, device=dev)}
+    out = _out_dict(out, {"topk_logp": (torch.float32, (B, D, K)),
+                          "topk_ids": (torch.int32, (B, D, K))}, dev)
     need = int(lib.ddt_draft_topk_workspace_size(B, D, V, K))
-    if workspace is None:
-        workspace = torch.empty((max(1, need),), dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, need, dev)
     rc = lib.ddt_draft_topk(_ptr(logits), DDT_BF16 if dt == torch.bfloat16 else DDT_F32, B, D, V,
                             K, _ptr(out["topk_logp"]), _ptr(out["topk_ids"]), _ptr(workspace),
                             workspace.numel() * workspace.element_size(), _stream())
@@ -288,16 +309,16 @@ def kv_commit(req_to_slot: torch.Tensor, prefix_len: torch.Tensor, n_nodes: torc
     Rewrites `req_to_slot` and `prefix_len` in place; returns the released
     slots ("freed_slots" [B][Q], -1 padded) and their count ("n_freed" [B])."""
     _dev(req_to_slot, "req_to_slot", torch.int32, 2)
-    _dev(prefix_len, "prefix_len", torch.int32, 1)
-    _dev(n_nodes, "n_nodes", torch.int32, 1)
-    _dev(accept_len, "accept_len", torch.int32, 1)
-    _dev(accept_nodes, "accept_nodes", torch.int32, 2)
-    B, max_kv = req_to_slot.shape
-    Q = accept_nodes.shape[1]
     dev = req_to_slot.device
-    if out is None:
-        out = {"freed_slots": torch.empty((B, Q), dtype=torch.int32, device=dev),
-               "n_freed": torch.empty((B,), dtype=torch.int32, device=dev)}
+    B, max_kv = req_to_slot.shape
+    _dev(accept_nodes, "accept_nodes", torch.int32, 2, device=dev)
+    Q = accept_nodes.shape[1]
+    _dev(accept_nodes, "accept_nodes", torch.int32, shape=(B, Q))
+    _dev(prefix_len, "prefix_len", torch.int32, shape=(B,), device=dev)
+    _dev(n_nodes, "n_nodes", torch.int32, shape=(B,), device=dev)
+    _dev(accept_len, "accept_len", torch.int32, shape=(B,), device=dev)
+    out = _out_dict(out, {"freed_slots": (torch.int32, (B, Q)),
+                          "n_freed": (torch.int32, (B,))}, dev)
     rc = load_library().ddt_kv_commit(
         _ptr(req_to_slot), max_kv, _ptr(prefix_len), _ptr(n_nodes), _ptr(accept_len),
         _ptr(accept_nodes), B, Q, _ptr(out["freed_slots"]), _ptr(out["n_freed"]), _stream())

@@ -51,6 +51,8 @@
 //    batches with at least one row tile per workgroup take an aligned split
 //    instead (twice the workgroups: whole row tiles first, then the leftover
 //    row tiles cut evenly), which leaves far fewer row tiles to merge.
+#include <stdlib.h>
+
 #include <type_traits>
 
 #include "ddt_internal.h"
@@ -487,6 +489,7 @@ struct Args {
   float* lse;
   float* ws_o;
   float* ws_lse;
+  int spin_limit;  // polls of a pair wait before it gives up (pair kernel)
 };
 
 // Sums / maxima of a value over lanes l and l ^ 32 (the two lanes of one row),
@@ -505,7 +508,9 @@ __device__ __forceinline__ float xor32_sum(float v) {
 // Pair synchronisation through LDS.  A wave posts an increasing sequence number
 // once its LDS writes have completed; its partner waits until it sees that
 // number.  Both waves of a pair take the same path, so they post the same
-// sequence.  The wait is bounded so that it always ends.
+// sequence.  The wait is bounded so that it always ends; a wait that gives up
+// marks the wave as stalled, and a stalled wave writes NaN for its rows (and
+// their log-sum-exp), so the give-up can never pass as a result.
 constexpr int kSpinLimit = 1 << 16;  // polls of ~100 cycles: milliseconds, far beyond a tile
 
 __device__ __forceinline__ void pair_post(int* flag, int seq) {
@@ -514,11 +519,16 @@ __device__ __forceinline__ void pair_post(int* flag, int seq) {
   __hip_atomic_store(flag, seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-__device__ __forceinline__ void pair_wait(int* flag, int seq) {
-  for (int i = 0; i < kSpinLimit; ++i) {
-    if (uni(__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) >= seq) break;
+__device__ __forceinline__ void pair_wait(int* flag, int seq, int limit, bool& stalled) {
+  bool seen = false;
+  for (int i = 0; i < limit; ++i) {
+    if (uni(__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) >= seq) {
+      seen = true;
+      break;
+    }
     __builtin_amdgcn_s_sleep(1);
   }
+  stalled = stalled || !seen;
   __asm__ __volatile__("" ::: "memory");
 }
 
@@ -600,6 +610,7 @@ __device__ __forceinline__ void run_unit(Smem<T, DL, DR>& sm, const Args& a, con
   // m_run: the row's reference max (log2 units), identical in both waves of the
   // pair; l_run: this lane's share of the row sum (own keys, its 8 of them).
   float m_run = -INFINITY, l_run = 0.0f;
+  bool stalled = false;  // a pair wait of this wave gave up
 
   // Prologue: publish the slot ids and visibility rows, then issue the first
   // tile's loads and after them the query loads (both land together).
@@ -741,7 +752,7 @@ __device__ __forceinline__ void run_unit(Smem<T, DL, DR>& sm, const Args& a, con
     sm.xs[wave][0][lane_it] = make_float4(s[kMate], s[kMate + 1], s[kMate + 2], s[kMate + 3]);
     sm.xs[wave][1][lane_it] = make_float4(s[kMate + 4], s[kMate + 5], s[kMate + 6], s[kMate + 7]);
     pair_post(&sm.xflag[wave], ++seq);
-    pair_wait(&sm.xflag[mate], seq);
+    pair_wait(&sm.xflag[mate], seq, a.spin_limit, stalled);
     float sv[8];
     {
       const float4 h0 = sm.xs[mate][0][lane_it];
@@ -812,7 +823,7 @@ __device__ __forceinline__ void run_unit(Smem<T, DL, DR>& sm, const Args& a, con
     sm.xm[wave][lane_it] = mo;
     if constexpr (G::kBF16) sm.xl[wave][lane_it] = xor32_sum(l_run);
     pair_post(&sm.xflag[wave], ++seq);
-    pair_wait(&sm.xflag[mate], seq);
+    pair_wait(&sm.xflag[mate], seq, a.spin_limit, stalled);
     if constexpr (G::kBF16) l_mate = sm.xl[mate][lane_it];
     // Lazy rescaling: the reference moves on a row's first visible key or
     // when the pair's tile max exceeds it by more than kRescaleLog2, so
@@ -831,7 +842,7 @@ __device__ __forceinline__ void run_unit(Smem<T, DL, DR>& sm, const Args& a, con
       for (int cb = 0; cb < G::kNCBh; ++cb) o[cb] *= alpha;
       post_p(m_run == -INFINITY ? 0.0f : m_run);
       pair_post(&sm.xflag[wave], ++seq);
-      pair_wait(&sm.xflag[mate], seq);
+      pair_wait(&sm.xflag[mate], seq, a.spin_limit, stalled);
     }
     l_run += psum;
     if constexpr (G::kBF16) {
@@ -956,8 +967,9 @@ __device__ __forceinline__ void run_unit(Smem<T, DL, DR>& sm, const Args& a, con
   const float l = l_own + sm.xl[mate][lane];
   // Normalise and write: this lane holds row n, columns
   // (kCb0 + cb)*32 + 8*t + 4*g + {0..3} in o[cb][4t..4t+3].
-  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-  const float lse_v = l > 0.0f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+  const float inv = stalled ? __builtin_nanf("") : (l > 0.0f ? 1.0f / l : 0.0f);
+  const float lse_v =
+      stalled ? __builtin_nanf("") : (l > 0.0f ? (m_run + log2f(l)) * kLn2 : -INFINITY);
   float* dst = nullptr;
   float* dst_lse = nullptr;
   if (u.complete) {
@@ -1146,10 +1158,10 @@ __global__ __launch_bounds__(kThreads) void verify_attn_kernel(
     int max_kv, const int32_t* __restrict__ prefix_len, const int32_t* __restrict__ n_nodes,
     const uint64_t* __restrict__ vis, int B, int Q, int H, int RT, float sm_scale,
     float* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o,
-    float* __restrict__ ws_lse, long long* __restrict__ ws_pref, int G) {
+    float* __restrict__ ws_lse, long long* __restrict__ ws_pref, int G, int spin_limit) {
   __shared__ Smem<T, DL, DR> sm;
   const Args args{q_lat, q_pe, c_kv, k_pe, num_slots, req_to_slot, max_kv, vis, Q, H,
-                  sm_scale * kLog2e, out, lse, ws_o, ws_lse};
+                  sm_scale * kLog2e, out, lse, ws_o, ws_lse, spin_limit};
   const int half = uni((int)((threadIdx.x >> 6) & 1));  // share of the pair: wave % 2
   if ((threadIdx.x & 63) == 0) sm.xflag[threadIdx.x >> 6] = 0;
   int seq = 0;  // this wave's pair-sync sequence (see pair_post)
@@ -1664,7 +1676,7 @@ void verify_attn_wide_kernel(
     int G) {
   __shared__ SmemW<DL, DR> sm;
   const Args args{q_lat, q_pe, c_kv, k_pe, num_slots, req_to_slot, max_kv, vis, Q, H,
-                  sm_scale * kLog2e, out, lse, ws_o, ws_lse};
+                  sm_scale * kLog2e, out, lse, ws_o, ws_lse, 0};
   for_each_unit<kThreadsW, kSplit2>(sm, prefix_len, n_nodes, B, Q, H, max_kv, RT, ws_pref, G,
                                     [&](const Unit& u, long long) __attribute__((always_inline)) {
                                       run_unit_w<DL, DR>(sm, args, u);
@@ -2024,6 +2036,19 @@ __global__ __launch_bounds__(kMergeThreads) void verify_merge_wide_kernel(
   }
 }
 
+// Polls of a pair wait before it gives up.  DDT_PAIR_SPIN_LIMIT (read once)
+// lowers it, so that a test can make every wait give up at once and check
+// that the rows come out as NaN; every wait still ends.
+int pair_spin_limit() {
+  static const int v = [] {
+    const char* e = getenv("DDT_PAIR_SPIN_LIMIT");
+    if (!e || !*e) return kSpinLimit;
+    const long x = strtol(e, nullptr, 10);
+    return x < 0 ? 0 : (x > kSpinLimit ? kSpinLimit : (int)x);
+  }();
+  return v;
+}
+
 template <typename T, int DL, int DR>
 hipError_t launch_impl(const void* q_lat, const void* q_pe, const void* c_kv, const void* k_pe,
                        int64_t num_slots, const int32_t* req_to_slot, int max_kv,
@@ -2052,7 +2077,7 @@ hipError_t launch_impl(const void* q_lat, const void* q_pe, const void* c_kv, co
                        stream, static_cast<const T*>(q_lat), static_cast<const T*>(q_pe),
                        static_cast<const T*>(c_kv), static_cast<const T*>(k_pe), num_slots,
                        req_to_slot, max_kv, prefix_len, n_nodes, vis, B, Q, H, plan.row_tiles,
-                       sm_scale, out, lse, ws_o, ws_lse, ws_pref, plan.grid);
+                       sm_scale, out, lse, ws_o, ws_lse, ws_pref, plan.grid, pair_spin_limit());
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
