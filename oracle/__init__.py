@@ -18,6 +18,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ddt_oracle.c")
 LIB_PATH = os.path.join(_HERE, "libddt_oracle.so")
+# AddressSanitizer + UndefinedBehaviorSanitizer build (host code only), loaded
+# instead of LIB_PATH when DDT_ORACLE_LIB names it.
+SAN_PATH = os.path.join(_HERE, "libddt_oracle_san.so")
 
 _lib = None
 
@@ -34,12 +37,24 @@ def build(force: bool = True) -> str:
     return LIB_PATH
 
 
+def build_sanitized() -> str:
+    """ddt_oracle.c with -fsanitize=address,undefined (any finding aborts)."""
+    tmp = SAN_PATH + ".tmp"
+    cmd = ["gcc", "-O1", "-g", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math",
+           "-ffp-contract=off", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, SAN_PATH)
+    return SAN_PATH
+
+
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
+        path = os.environ.get("DDT_ORACLE_LIB") or LIB_PATH
+        if path == LIB_PATH and not os.path.exists(LIB_PATH):
             build(force=False)
-        lib = ctypes.CDLL(LIB_PATH)
+        lib = ctypes.CDLL(path)
         p = ctypes.c_void_p
         i32, i64, f32 = ctypes.c_int, ctypes.c_int64, ctypes.c_float
         lib.ddt_oracle_tree_build.argtypes = [p, p, p, p, i32, i32, i32, i32] + [p] * 9

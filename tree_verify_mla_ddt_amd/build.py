@@ -11,6 +11,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "libddt.so")
+# Host-side checker of the attention work split (CPU tests only).
+CHECK_PATH = os.path.join(HERE, "libddt_split_check.so")
 SOURCES = ["api.hip", "draft_topk.hip", "tree_build.hip", "tree_accept.hip",
            "tree_accept_sampling.hip", "kv_commit.hip", "verify_attn.hip"]
 ARCH = os.environ.get("DDT_OFFLOAD_ARCH", "gfx950")
@@ -28,6 +30,19 @@ def hipcc_command(out_path: str, resource_report: bool = False) -> list[str]:
     return cmd
 
 
+def build_split_check() -> str:
+    """The host-only split checker (csrc/split_check.hip) as its own library."""
+    tmp = CHECK_PATH + ".tmp"
+    cmd = ["hipcc", f"--offload-arch={ARCH}", "-O2", "-std=c++17", "-fPIC", "-shared",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           os.path.join(CSRC, "split_check.hip"), "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}{res.stderr}")
+    os.replace(tmp, CHECK_PATH)
+    return CHECK_PATH
+
+
 def build(verbose: bool = False, resource_report: bool = False) -> str:
     tmp = LIB_PATH + ".tmp"
     res = subprocess.run(hipcc_command(tmp, resource_report), capture_output=True, text=True)
@@ -38,6 +53,7 @@ def build(verbose: bool = False, resource_report: bool = False) -> str:
     if verbose and log.strip():
         print(log)
     os.replace(tmp, LIB_PATH)
+    build_split_check()
     return LIB_PATH
 
 

@@ -1,0 +1,210 @@
+// attn_split.h -- the work split of the verify-attention kernels, as plain
+// integer arithmetic usable on the host and the device.
+//
+// The attention kernels cut the (request, 128-row tile, 32-key tile) work into
+// contiguous ranges, one per workgroup; row tiles whose key range is cut are
+// written as partial results to workspace slots and combined by the merge
+// kernels.  Everything that decides which workgroup takes which tiles, which
+// slot a partial result lands in and which slots the merge reads is here, so
+// that a host program (the split checker) runs exactly the code the kernels
+// run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ddt {
+
+constexpr int kTileKeys = 32;     // keys per tile
+constexpr int kRowsPerWG = 128;   // rows per tile
+constexpr int kMaxBatch = 512;    // requests the attention kernels take
+constexpr int kXcds = 8;          // XCDs the workgroups are dealt to
+constexpr int kMaxGrid = 1024;    // upper bound of the attention grid
+
+#define DDT_HD __host__ __device__ __forceinline__
+
+DDT_HD int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+// Per-request quantities shared by the attention and merge kernels.
+struct ReqInfo {
+  int L;      // prefix length
+  int nb;     // tree entries
+  int nkb;    // key tiles
+  int vt;     // row tiles holding at least one live row
+};
+
+// From the clamped prefix length and tree size.
+DDT_HD ReqInfo req_info_ln(int L, int nb, int H, int RT) {
+  ReqInfo r;
+  r.L = L;
+  r.nb = nb;
+  r.nkb = (r.L + r.nb + kTileKeys - 1) / kTileKeys;
+  const long long live_rows = (long long)r.nb * H;
+  long long vt = (live_rows + kRowsPerWG - 1) / kRowsPerWG;
+  r.vt = (int)(vt > RT ? RT : vt);
+  return r;
+}
+
+// Prefix length clamped to [0, max_kv], tree size to [0, min(Q, max_kv - L)].
+DDT_HD void clamp_request(int prefix_len, int n_nodes, int Q, int max_kv, int& L, int& nb) {
+  L = clampi(prefix_len, 0, max_kv);
+  const int cap = Q < max_kv - L ? Q : max_kv - L;
+  nb = clampi(n_nodes, 0, cap);
+}
+
+DDT_HD ReqInfo req_info(const int32_t* prefix_len, const int32_t* n_nodes, int b, int Q, int H,
+                        int max_kv, int RT) {
+  int L, nb;
+  clamp_request(prefix_len[b], n_nodes[b], Q, max_kv, L, nb);
+  return req_info_ln(L, nb, H, RT);
+}
+
+// Start of range g when W tiles are cut into G contiguous ranges.
+DDT_HD long long range_start(long long g, long long W, long long G) { return (g * W) / G; }
+// The range holding tile t (0 <= t < W).
+DDT_HD long long range_owner(long long t, long long W, long long G) { return ((t + 1) * G - 1) / W; }
+
+// Logical id of workgroup bl (0 <= bl < G): workgroups are dealt to the XCDs
+// round-robin (bl % 8), so XCD x gets the consecutive logical ids
+// [start_x, start_x + count_x) and consecutive ranges share an L2.
+DDT_HD long long logical_gid(long long bl, long long G) {
+  const long long xcd = bl % kXcds;
+  return xcd * (G / kXcds) + (xcd < G % kXcds ? xcd : G % kXcds) + bl / kXcds;
+}
+
+// The split mode: U = B * vt row tiles with work when every request has the
+// same row-tile and key-tile counts (`same`) and U >= G (the aligned split,
+// launched with 2G workgroups), else -1 (one stream over all work, cut into G
+// ranges).
+DDT_HD long long split_mode(bool same, int vt0, int B, long long G) {
+  const long long U = (long long)B * vt0;
+  return (same && vt0 > 0 && U >= G) ? U : -1;
+}
+
+// Range [start, end) of the stream taken by the workgroup with logical id gid
+// in the first (second = false) or second half of an aligned-split launch.
+// Under the aligned split unit u covers tiles [u*nkb, (u+1)*nkb): the first G
+// workgroups take q = U / G whole units each, the second G the r = U - q*G
+// leftover units as one stream cut into G ranges.  Otherwise the whole work
+// Wtot is cut into G ranges (first half only).
+DDT_HD void workgroup_range(long long mode, bool second, long long gid, long long Wtot, int nkb0,
+                            long long G, long long& start, long long& end) {
+  if (mode < 0) {
+    start = range_start(gid, Wtot, G);
+    end = range_start(gid + 1, Wtot, G);
+    if (second) end = start;
+    return;
+  }
+  const long long nkb = nkb0, q = mode / G, r = mode - q * G;
+  if (!second) {
+    start = gid * q * nkb;
+    end = start + q * nkb;
+  } else {
+    start = q * G * nkb + range_start(gid, r * nkb, G);
+    end = q * G * nkb + range_start(gid + 1, r * nkb, G);
+  }
+}
+
+// For a row tile with work, its place in the stream that holds it: S (first
+// key tile) and W (stream length); false for a whole unit of the aligned
+// split (written directly).  pref: exclusive work prefix over requests, with
+// pref[B] the total.
+DDT_HD bool stream_place(long long mode, const long long* pref, int B, int b, int rt,
+                         const ReqInfo& ri, long long G, long long& S, long long& W) {
+  if (mode >= 0) {
+    const long long q = mode / G, r = mode - q * G;
+    const long long u = (long long)b * ri.vt + rt;
+    if (u < q * G) return false;
+    S = (u - q * G) * ri.nkb;
+    W = r * ri.nkb;
+    return true;
+  }
+  S = pref[b] + (long long)rt * ri.nkb;
+  W = pref[B];
+  return true;
+}
+
+// Workspace slot a workgroup writes a partial result of a cut row tile to:
+// 2g for the tile holding the start of its range (its head), 2g + 1 for the
+// one holding its end (a range cuts at most two row tiles).
+DDT_HD long long partial_slot(long long gid, bool head) { return 2 * gid + (head ? 0 : 1); }
+
+// The merge's rule: contributor gg (g_first <= gg <= g_last, the ranges
+// overlapping a row tile whose stream place starts at S_u) wrote slot
+// 2gg (its range starts inside the tile) or 2gg + 1, or nothing (empty range).
+DDT_HD long long contributor_slot(long long gg, long long S_u, long long W, long long G) {
+  const long long s0 = range_start(gg, W, G);
+  const long long s1 = range_start(gg + 1, W, G);
+  if (s0 == s1) return -1;
+  return partial_slot(gg, s0 >= S_u);
+}
+
+// One unit (a row tile over a key range) of a workgroup's range: the unit
+// starting at stream position pos, inside request b (pref[b] <= pos <
+// pref[b + 1]).
+struct UnitPos {
+  int rt, kb0, kb1;
+  bool complete;
+};
+DDT_HD UnitPos unit_at(long long pos, long long end, long long pref_b, const ReqInfo& ri) {
+  UnitPos u;
+  const long long off = pos - pref_b;
+  u.rt = (int)(off / ri.nkb);
+  u.kb0 = (int)(off % ri.nkb);
+  const long long left = end - pos;
+  u.kb1 = (long long)(ri.nkb - u.kb0) < left ? ri.nkb : u.kb0 + (int)left;
+  u.complete = u.kb0 == 0 && u.kb1 == ri.nkb;
+  return u;
+}
+
+#undef DDT_HD
+
+// The attention launch: grid (workgroups per half), row tiles per request and
+// the workspace it needs.
+struct AttnPlan {
+  int grid;          // attention workgroups (at most one per CU)
+  int row_tiles;     // ceil(Q*H / 128)
+  int num_cu;        // compute units the plan was made for
+  size_t ws_bytes;   // workspace bytes needed
+};
+
+constexpr int kMinTilesPerWG = 3;  // key tiles per workgroup before splitting further
+
+inline AttnPlan plan_verify_attn(int B, int Q, int H, int max_kv, int d_lat, int num_cu) {
+  AttnPlan p;
+  const long long rows = (long long)Q * H;
+  p.row_tiles = (int)((rows + kRowsPerWG - 1) / kRowsPerWG);
+  const long long nkb = ((long long)max_kv + kTileKeys - 1) / kTileKeys;
+  const long long work = (long long)B * p.row_tiles * nkb;
+  // One resident workgroup per CU (register-bound), but at least kMinTilesPerWG
+  // key tiles each so that query loads and partial outputs stay a small share.
+  long long cap = num_cu > 0 ? num_cu : 256;
+  if (cap > kMaxGrid) cap = kMaxGrid;
+  const long long units = (long long)B * p.row_tiles;
+  const long long per_unit = (nkb + kMinTilesPerWG - 1) / kMinTilesPerWG;
+  long long g;
+  if (units * per_unit <= cap) {
+    // Few row tiles: cut each into ranges of at most kMinTilesPerWG tiles, so
+    // that every workgroup's range lies inside one row tile (one query load,
+    // one partial output) and none is longer than that.
+    g = units * per_unit;
+  } else {
+    g = cap;
+    const long long by_work = (work + kMinTilesPerWG - 1) / kMinTilesPerWG;
+    if (by_work < g) g = by_work;
+    // When a multiple of the row-tile count comes within 10% of that, take it
+    // (requests of equal length then give ranges inside one row tile).
+    if (units <= g && units * (g / units) * 10 >= g * 9) g = units * (g / units);
+  }
+  if (g < 1) g = 1;
+  p.grid = (int)g;
+  p.num_cu = num_cu > 0 ? num_cu : 256;
+  // Partial outputs and log-sum-exps (two slots per workgroup), then the work
+  // prefix over requests and the split mode that the merge kernels read.
+  p.ws_bytes = (size_t)2 * p.grid * kRowsPerWG * ((size_t)d_lat + 1) * sizeof(float) +
+               ((size_t)B + 2) * sizeof(long long);
+  return p;
+}
+
+}  // namespace ddt

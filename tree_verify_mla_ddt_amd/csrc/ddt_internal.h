@@ -9,6 +9,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "attn_split.h"
+
 namespace ddt {
 
 constexpr int kWave = 64;
@@ -66,16 +68,8 @@ hipError_t launch_tree_accept_sampling(int dtype, const void* logits, int V,
 
 // Verify attention: rows of a request are (node, head) pairs, row = i*H + h.
 // The key range of every 128-row tile is split across a fixed grid of
-// workgroups (see verify_attn.hip); partial results go to the workspace and a
-// merge kernel combines them.
-struct AttnPlan {
-  int grid;          // attention workgroups (at most one per CU)
-  int row_tiles;     // ceil(Q*H / 128)
-  int num_cu;        // compute units the plan was made for
-  size_t ws_bytes;   // workspace bytes needed
-};
-AttnPlan plan_verify_attn(int B, int Q, int H, int max_kv, int d_lat, int num_cu);
-
+// workgroups (see attn_split.h, which holds the plan); partial results go to
+// the workspace and a merge kernel combines them.
 hipError_t launch_verify_attn(int dtype, int d_lat, int d_rope, const void* q_lat,
                               const void* q_pe, const void* c_kv, const void* k_pe,
                               int64_t num_slots, const int32_t* req_to_slot,

@@ -65,21 +65,12 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x4_lds_t __attribute__((__vector_size__(4 * sizeof(__bf16))));
 #define DDT_LDS __attribute__((address_space(3)))
 
-constexpr int kTileKeys = 32;
 constexpr int kSplit = 2;                // waves sharing one 32-row block
 constexpr int kWaves = 4 * kSplit;
 constexpr int kThreads = kWaves * kWave;
-constexpr int kRowsPerWG = 128;
-constexpr int kMaxBatch = 512;
-constexpr int kXcds = 8;
 constexpr int kRing = 3;                 // slot-id ring (tiles kb .. kb+2)
 constexpr int kStages = 3;               // key-tile stages in LDS (tiles kb-1 .. kb+1)
 constexpr int kMergeThreads = 256;
-constexpr int kMaxGrid = 1024;           // upper bound of the attention grid
-#ifndef DDT_MIN_TILES
-#define DDT_MIN_TILES 3
-#endif
-constexpr int kMinTilesPerWG = DDT_MIN_TILES;  // key tiles per workgroup before splitting further
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // A tile takes the residual pass when some key's probability exceeds this share
@@ -144,9 +135,6 @@ __device__ __forceinline__ bf16x8_t pack_p(const float* p) {
   return __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
 }
 
-__device__ __forceinline__ int clampi(int v, int lo, int hi) {
-  return v < lo ? lo : (v > hi ? hi : v);
-}
 
 // Wave-uniform values read from LDS or derived from them are moved to scalar
 // registers so they do not occupy vector registers.
@@ -155,33 +143,6 @@ __device__ __forceinline__ long long uni(long long v) {
   const int lo = __builtin_amdgcn_readfirstlane((int)(v & 0xFFFFFFFFll));
   const int hi = __builtin_amdgcn_readfirstlane((int)(v >> 32));
   return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
-}
-
-// Per-request quantities shared by the attention and merge kernels.
-struct ReqInfo {
-  int L;      // prefix length
-  int nb;     // tree entries
-  int nkb;    // key tiles
-  int vt;     // row tiles holding at least one live row
-};
-
-// From the clamped prefix length and tree size.
-__device__ __forceinline__ ReqInfo req_info_ln(int L, int nb, int H, int RT) {
-  ReqInfo r;
-  r.L = L;
-  r.nb = nb;
-  r.nkb = (r.L + r.nb + kTileKeys - 1) / kTileKeys;
-  const long long live_rows = (long long)r.nb * H;
-  long long vt = (live_rows + kRowsPerWG - 1) / kRowsPerWG;
-  r.vt = (int)(vt > RT ? RT : vt);
-  return r;
-}
-
-__device__ __forceinline__ ReqInfo req_info(const int32_t* prefix_len, const int32_t* n_nodes,
-                                            int b, int Q, int H, int max_kv, int RT) {
-  const int L = clampi(prefix_len[b], 0, max_kv);
-  const int cap = Q < max_kv - L ? Q : max_kv - L;
-  return req_info_ln(L, clampi(n_nodes[b], 0, cap), H, RT);
 }
 
 // Exclusive prefix of work (key tiles) over requests into s_pref[0..B], and
@@ -230,42 +191,6 @@ __device__ void work_prefix(long long* s_pref, long long* s_wsum, int2* s_req,
   }
   __syncthreads();
 }
-
-__device__ __forceinline__ long long range_start(long long g, long long W, long long G) {
-  return (g * W) / G;
-}
-// The workgroup whose range holds key tile t (0 <= t < W).
-__device__ __forceinline__ long long range_owner(long long t, long long W, long long G) {
-  return ((t + 1) * G - 1) / W;
-}
-
-// Work split when every request has the same row-tile and key-tile counts and
-// there are at least as many row tiles with work (units) as workgroups: unit u
-// is b * vt + rt.  Workgroup g takes the q = U / G whole units [g*q, g*q + q),
-// written directly, then an equal share of the r = U - q*G units left over,
-// laid out as one stream of r * nkb key tiles cut into G contiguous ranges (a
-// range cuts at most two units: r < G).  Otherwise the whole work is one
-// stream over (request, row tile, key tile) cut into G ranges.  The attention
-// kernel records the mode in ws_pref[B + 1]: U in the first case, -1 in the
-// second.  For a row tile with work, its place in the stream that holds it:
-// S (first key tile) and W (stream length); false for a whole unit.
-__device__ __forceinline__ bool stream_place(long long mode, const long long* pref, int B, int b,
-                                             int rt, const ReqInfo& ri, long long G, long long& S,
-                                             long long& W) {
-  if (mode >= 0) {
-    const long long q = mode / G, r = mode - q * G;
-    const long long u = (long long)b * ri.vt + rt;
-    if (u < q * G) return false;
-    S = (u - q * G) * ri.nkb;
-    W = r * ri.nkb;
-    return true;
-  }
-  S = pref[b] + (long long)rt * ri.nkb;
-  W = pref[B];
-  return true;
-}
-
-
 
 template <typename T, int DL, int DR>
 struct Smem {
@@ -1047,28 +972,12 @@ __device__ __forceinline__ void for_each_unit(SM& sm, const int32_t* __restrict_
   work_prefix<kThr>(sm.pref, sm.wsum, sm.req, prefix_len, n_nodes, B, Q, H, max_kv, RT);
   const long long Wtot = uni(sm.pref[B]);
   const long long Gn = G;
-  long long start, end, gid;
-  if constexpr (!kSplit2) {
-    if (blockIdx.x == 0) {  // for the merge kernels: the stream split
-      for (int i = threadIdx.x; i <= B; i += kThr) ws_pref[i] = sm.pref[i];
-      if (threadIdx.x == 0) ws_pref[B + 1] = -1;
-    }
-    // Logical id: workgroups are dealt to the XCDs round-robin (blockIdx % 8),
-    // so XCD x gets the consecutive logical ids [start_x, start_x + count_x).
-    const long long xcd = blockIdx.x % kXcds;
-    gid = xcd * (Gn / kXcds) + (xcd < Gn % kXcds ? xcd : Gn % kXcds) + blockIdx.x / kXcds;
-    start = range_start(gid, Wtot, Gn);
-    end = range_start(gid + 1, Wtot, Gn);
-    if (start >= end) return;
-  } else {
-    // Launched with 2G workgroups for the aligned split (see stream_place):
-    // uniform requests (the same row-tile and key-tile counts) with at least
-    // one row tile of work per workgroup.  Unit u then covers tiles
-    // [u*nkb, (u+1)*nkb) of the stream; the first G workgroups (dispatched
-    // first) take the whole units, the second G the ranges of the leftover
-    // units, so each workgroup still walks one range of the stream.  Other
-    // requests take the stream split on the first G.
-    const bool second = blockIdx.x >= Gn;
+  long long mode = -1;
+  bool second = false;
+  if constexpr (kSplit2) {
+    // Launched with 2G workgroups for the aligned split (see workgroup_range);
+    // the kernel decides from the clamped request sizes whether it applies.
+    second = blockIdx.x >= Gn;
     const ReqInfo ri0 = req_info_ln(sm.req[0].x, sm.req[0].y, H, RT);
     int same = 1;
     for (int bb = threadIdx.x; bb < B; bb += kThr) {
@@ -1076,34 +985,19 @@ __device__ __forceinline__ void for_each_unit(SM& sm, const int32_t* __restrict_
       if (r.nkb != ri0.nkb || r.vt != ri0.vt) same = 0;
     }
     same = __syncthreads_and(same);
-    const long long U = (long long)B * ri0.vt;
-    const long long mode = (same && ri0.vt > 0 && U >= Gn) ? U : -1;
-    if (blockIdx.x == 0) {  // for the merge kernels
-      for (int i = threadIdx.x; i <= B; i += kThr) ws_pref[i] = sm.pref[i];
-      if (threadIdx.x == 0) ws_pref[B + 1] = mode;
-    }
-    if (mode < 0 && second) return;
-    // Logical id within its half, dealt to the XCDs as above.
-    const long long bl = blockIdx.x - (second ? Gn : 0);
-    const long long xcd = bl % kXcds;
-    gid = xcd * (Gn / kXcds) + (xcd < Gn % kXcds ? xcd : Gn % kXcds) + bl / kXcds;
-    if (mode < 0) {
-      start = range_start(gid, Wtot, Gn);
-      end = range_start(gid + 1, Wtot, Gn);
-    } else {
-      const long long nkb = ri0.nkb, q = mode / Gn, r = mode - q * Gn;
-      if (!second) {
-        start = gid * q * nkb;
-        end = start + q * nkb;
-      } else {
-        start = q * Gn * nkb + range_start(gid, r * nkb, Gn);
-        end = q * Gn * nkb + range_start(gid + 1, r * nkb, Gn);
-      }
-    }
-    start = uni(start);
-    end = uni(end);
-    if (start >= end) return;
+    mode = split_mode(same != 0, ri0.vt, B, Gn);
   }
+  if (blockIdx.x == 0) {  // for the merge kernels: the work prefix and the split mode
+    for (int i = threadIdx.x; i <= B; i += kThr) ws_pref[i] = sm.pref[i];
+    if (threadIdx.x == 0) ws_pref[B + 1] = mode;
+  }
+  const long long gid = logical_gid(blockIdx.x - (second ? Gn : 0), Gn);
+  long long start, end;
+  const ReqInfo ri0 = req_info_ln(sm.req[0].x, sm.req[0].y, H, RT);
+  workgroup_range(mode, second, gid, Wtot, ri0.nkb, Gn, start, end);
+  start = uni(start);
+  end = uni(end);
+  if (start >= end) return;
 
   // Request holding `start`: the last b with pref[b] <= start (it has work).
   int b = 0;
@@ -1135,13 +1029,12 @@ __device__ __forceinline__ void for_each_unit(SM& sm, const int32_t* __restrict_
       const int2 ln = sm.req[b];
       u.ri = req_info_ln(uni(ln.x), uni(ln.y), H, RT);
     }
-    const long long off = pos - uni(sm.pref[b]);
-    u.rt = (int)(off / u.ri.nkb);
-    u.kb0 = (int)(off % u.ri.nkb);
-    const long long left = end - pos;
-    u.kb1 = (long long)(u.ri.nkb - u.kb0) < left ? u.ri.nkb : u.kb0 + (int)left;
-    u.complete = u.kb0 == 0 && u.kb1 == u.ri.nkb;
-    u.slot = 2 * gid + (head ? 0 : 1);
+    const UnitPos up = unit_at(pos, end, uni(sm.pref[b]), u.ri);
+    u.rt = up.rt;
+    u.kb0 = up.kb0;
+    u.kb1 = up.kb1;
+    u.complete = up.complete;
+    u.slot = partial_slot(gid, head);
     u.nkeys = u.ri.L + u.ri.nb;
     pos += u.kb1 - u.kb0;
     if (head != (pass == 1)) continue;
@@ -1749,11 +1642,7 @@ __global__ __launch_bounds__(kMergeThreads) void verify_merge_kernel(
       for (int k0 = 0; k0 < cnt; k0 += kWave) {
         const long long gg = g_first + k0 + tid;
         int src = -1;
-        if (k0 + tid < cnt) {
-          const long long s0 = range_start(gg, Wtot, Gn);
-          const long long s1 = range_start(gg + 1, Wtot, Gn);
-          if (s0 != s1) src = (int)(2 * gg + (s0 >= S_u ? 0 : 1));
-        }
+        if (k0 + tid < cnt) src = (int)contributor_slot(gg, S_u, Wtot, Gn);
         const uint64_t m = __ballot(src >= 0);
         const int at = base + (int)__builtin_amdgcn_mbcnt_hi(
                                   (unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
@@ -1933,11 +1822,7 @@ __global__ __launch_bounds__(kMergeThreads) void verify_merge_wide_kernel(
       for (int k0 = 0; k0 < cnt; k0 += kWave) {
         const long long gg = g_first + k0 + tid;
         int src = -1;
-        if (k0 + tid < cnt) {
-          const long long s0 = range_start(gg, Wtot, Gn);
-          const long long s1 = range_start(gg + 1, Wtot, Gn);
-          if (s0 != s1) src = (int)(2 * gg + (s0 >= S_u ? 0 : 1));
-        }
+        if (k0 + tid < cnt) src = (int)contributor_slot(gg, S_u, Wtot, Gn);
         const uint64_t m = __ballot(src >= 0);
         const int at = base + (int)__builtin_amdgcn_mbcnt_hi(
                                   (unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
@@ -2098,42 +1983,6 @@ hipError_t launch_impl(const void* q_lat, const void* q_pe, const void* c_kv, co
 }
 
 }  // namespace
-
-AttnPlan plan_verify_attn(int B, int Q, int H, int max_kv, int d_lat, int num_cu) {
-  AttnPlan p;
-  const long long rows = (long long)Q * H;
-  p.row_tiles = (int)((rows + kRowsPerWG - 1) / kRowsPerWG);
-  const long long nkb = ((long long)max_kv + kTileKeys - 1) / kTileKeys;
-  const long long work = (long long)B * p.row_tiles * nkb;
-  // One resident workgroup per CU (register-bound), but at least kMinTilesPerWG
-  // key tiles each so that query loads and partial outputs stay a small share.
-  long long cap = num_cu > 0 ? num_cu : 256;
-  if (cap > kMaxGrid) cap = kMaxGrid;
-  const long long units = (long long)B * p.row_tiles;
-  const long long per_unit = (nkb + kMinTilesPerWG - 1) / kMinTilesPerWG;
-  long long g;
-  if (units * per_unit <= cap) {
-    // Few row tiles: cut each into ranges of at most kMinTilesPerWG tiles, so
-    // that every workgroup's range lies inside one row tile (one query load,
-    // one partial output) and none is longer than that.
-    g = units * per_unit;
-  } else {
-    g = cap;
-    const long long by_work = (work + kMinTilesPerWG - 1) / kMinTilesPerWG;
-    if (by_work < g) g = by_work;
-    // When a multiple of the row-tile count comes within 10% of that, take it
-    // (requests of equal length then give ranges inside one row tile).
-    if (units <= g && units * (g / units) * 10 >= g * 9) g = units * (g / units);
-  }
-  if (g < 1) g = 1;
-  p.grid = (int)g;
-  p.num_cu = num_cu > 0 ? num_cu : 256;
-  // Partial outputs and log-sum-exps (two slots per workgroup), then the work
-  // prefix over requests and the split mode that the merge kernels read.
-  p.ws_bytes = (size_t)2 * p.grid * kRowsPerWG * ((size_t)d_lat + 1) * sizeof(float) +
-               ((size_t)B + 2) * sizeof(long long);
-  return p;
-}
 
 hipError_t launch_verify_attn(int dtype, int d_lat, int d_rope, const void* q_lat,
                               const void* q_pe, const void* c_kv, const void* k_pe,
