@@ -8,6 +8,12 @@ prefix 2048, drafter depth 8 x top-8, budget 8.  The same JSON line also carries
 the attention roofline of that workload, the other benchmark workloads as extra
 measurements, and the CPU oracle timed on the host cores.
 
+Every GPU figure is the median of 5 repeats of back-to-back graph replays (the
+headline step: --steps replays per repeat; everything else: at least 100), with
+the repeats' minimum and maximum beside it.  The attention roofline is given
+for the attention kernel alone (HIP events around back-to-back launches of that
+kernel) and for the whole call (attention kernel + split merge).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only-primary]
 Prints exactly one JSON line on stdout (progress goes to stderr).
 """
@@ -28,7 +34,10 @@ sys.path.insert(0, ROOT)
 METRIC = ("verify-attn TFLOP/s + HBM GB/s (% roofline); "
           "tree-verify steps/s at batch 1/64")
 PRIMARY = "b1_l2k_q9"
-EXTRA = ["tiny_fp32", "b4_l4k_q17", "b4_l4k_q33", "b64_l2k_q9", "b8_l32k_q65"]
+EXTRA = ["tiny_fp32", "b4_l4k_q17", "b4_l4k_q33", "b64_l2k_q9", "b8_l32k_q65",
+         "b64_l2k_q9_h8", "b8_l32k_q65_h8"]
+REPEATS = 5        # timed repeats per figure; the median is reported
+MIN_REPLAYS = 100  # replays per repeat for every figure but the headline step
 # MI355X published peaks.
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_F32_TFLOPS = 157.3
@@ -73,7 +82,8 @@ def source_digest():
 
 
 COPY_BYTES = 256 << 20  # the --copy-calibration copy
-ATTN_KERNELS = ("verify_attn_kernel", "verify_merge_kernel", "verify_merge_wide_kernel")
+ATTN_KERNELS = ("verify_attn_kernel", "verify_attn_wide_kernel", "verify_merge_kernel",
+                "verify_merge_wide_kernel")
 
 
 def _counter_rows(directory):
@@ -101,7 +111,7 @@ def _per_launch_kib(rows, counter):
                 per_kernel.setdefault(k, []).append(v)
         if "copyBuffer" in name and int(r["Grid_Size"]) * 2048 == COPY_BYTES:
             copy.append(v)  # the calibration copy moves 2 KiB per work-item
-    if "verify_attn_kernel" not in per_kernel or not copy:
+    if not ({"verify_attn_kernel", "verify_attn_wide_kernel"} & set(per_kernel)) or not copy:
         raise SystemExit(f"{counter}: attention kernel or calibration copy missing")
     att = sum(sum(v) / len(v) for v in per_kernel.values())
     return att, sum(copy) / len(copy)
@@ -143,6 +153,20 @@ def measured_traffic(workload):
         return None
     w = rec.get("workloads", {}).get(workload)
     return None if w is None else float(w["bytes_per_launch"])
+
+
+class Timing:
+    """Per-launch milliseconds of each timed repeat; `ms` is their median."""
+
+    def __init__(self, per_repeat, n):
+        self.per = sorted(float(x) for x in per_repeat)
+        self.n = n
+        self.ms = float(np.median(self.per))
+
+    def summary(self, scale=1e3, unit="us"):
+        return {"median": round(self.ms * scale, 3), "min": round(self.per[0] * scale, 3),
+                "max": round(self.per[-1] * scale, 3), "unit": unit,
+                "replays_per_repeat": self.n, "repeats": len(self.per)}
 
 
 class StepRunner:
@@ -206,35 +230,50 @@ class StepRunner:
         torch.cuda.synchronize()
         return g
 
-    def time_graph(self, g, steps, warmup):
+    def _time(self, launch, n, warmup, repeats=REPEATS):
+        """`repeats` timed runs of n back-to-back launches, each bracketed by a
+        device synchronization and HIP events on the current stream (where the
+        graphs are replayed and the library enqueues its kernels).  Returns the
+        per-launch milliseconds of every repeat and their median."""
         torch = self.torch
         for _ in range(warmup):
-            g.replay()
+            launch()
         torch.cuda.synchronize()
-        start = torch.cuda.Event(enable_timing=True)
-        stop = torch.cuda.Event(enable_timing=True)
-        start.record()
-        for _ in range(steps):
-            g.replay()
-        stop.record()
-        torch.cuda.synchronize()
-        return start.elapsed_time(stop) / steps  # ms
+        per = []
+        for _ in range(repeats):
+            start = torch.cuda.Event(enable_timing=True)
+            stop = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            start.record()
+            for _ in range(n):
+                launch()
+            stop.record()
+            torch.cuda.synchronize()
+            per.append(start.elapsed_time(stop) / n)
+        return Timing(per, n)
 
-    def time_eager(self, fn, steps, warmup):
-        torch = self.torch
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
-        start = torch.cuda.Event(enable_timing=True)
-        stop = torch.cuda.Event(enable_timing=True)
-        start.record()
-        for _ in range(steps):
-            fn()
-        stop.record()
-        torch.cuda.synchronize()
-        return start.elapsed_time(stop) / steps
+    def time_graph(self, g, n, warmup, repeats=REPEATS):
+        return self._time(g.replay, n, warmup, repeats)
 
-    def commit_ms(self, steps=200):
+    def time_eager(self, fn, n, warmup, repeats=REPEATS):
+        return self._time(fn, n, warmup, repeats)
+
+    def kernel_times(self, reps=MIN_REPLAYS, repeats=REPEATS):
+        """Per-launch milliseconds of the attention kernel and of the merge kernel,
+        each launched `reps` times back to back between HIP events on the current
+        stream; `repeats` runs, medians."""
+        a = self.wl
+        att, mrg = [], []
+        for _ in range(repeats):
+            ms_a, ms_m, _, _ = self.ddt.verify_attn_kernel_times(
+                self.q_lat, self.q_pe, self.c_kv, self.k_pe, self.r2s, self.plen,
+                self.tree["n_nodes"], self.tree["vis"], a.sm_scale, reps, out=self.out,
+                lse=self.lse, workspace=self.ws)
+            att.append(ms_a)
+            mrg.append(ms_m)
+        return Timing(att, reps), Timing(mrg, reps)
+
+    def commit_ms(self, steps=MIN_REPLAYS):
         """What ddt_kv_commit adds to a step: graph replays of (step, restore
         prefix_len, commit) minus replays of (step, restore).  The commit rewrites
         the table in place, so prefix_len is reset every time and each replay
@@ -255,12 +294,12 @@ class StepRunner:
                           self.acc["accept_nodes"], out=fo)
 
         g_w, g_c = self.capture(without), self.capture(with_commit)
-        t_w = self.time_graph(g_w, steps, 10)
-        t_c = self.time_graph(g_c, steps, 10)
-        t_w2 = self.time_graph(g_w, steps, 10)
+        t_w = self.time_graph(g_w, steps, 10).ms
+        t_c = self.time_graph(g_c, steps, 10).ms
+        t_w2 = self.time_graph(g_w, steps, 10).ms
         return max(t_c - 0.5 * (t_w + t_w2), 0.0)
 
-    def topk_stats(self, steps=200):
+    def topk_stats(self, steps=MIN_REPLAYS):
         """ddt_draft_topk on this workload's drafter shape: D depths of logits over
         the workload's vocabulary (bf16, or fp32 for the fp32 workload), timed by
         graph replays; HBM-bound, so the roofline is bytes read and written."""
@@ -273,14 +312,14 @@ class StepRunner:
         ws = torch.empty((int(ddt.load_library().ddt_draft_topk_workspace_size(
             wl.B, wl.D, wl.vocab, wl.K)),), dtype=torch.uint8, device="cuda")
         gr = self.capture(lambda: ddt.draft_topk(logits, wl.K, out=out, workspace=ws))
-        ms = self.time_graph(gr, steps, 10)
+        ms = self.time_graph(gr, steps, 10).ms
         nbytes = logits.numel() * logits.element_size() + wl.B * wl.D * wl.K * 8
         gbs = nbytes / (ms * 1e-3) / 1e9
         return {"ms": round(ms, 5), "bytes": nbytes, "gbs": round(gbs, 1),
                 "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "vocab": wl.vocab, "K": wl.K,
                 "D": wl.D}
 
-    def sampling_stats(self, steps=200):
+    def sampling_stats(self, steps=MIN_REPLAYS):
         """ddt_tree_accept_sampling on this workload's drafted tree at temperature 1:
         target logits N(0, 2) over the workload's vocabulary at every tree node (bf16,
         or fp32 for the fp32 workload), with each node's lowest-index child's token set
@@ -311,7 +350,7 @@ class StepRunner:
         fn = lambda: ddt.tree_accept_sampling(logits, temp, tr["node_token"], tr["parent"],
                                               tr["n_nodes"], coins, cfin, out=out, workspace=ws)
         gr = self.capture(fn)
-        ms = self.time_graph(gr, steps, 10)
+        ms = self.time_graph(gr, steps, 10).ms
         live = int(ht["n_nodes"][:B].sum())
         nbytes = live * V * logits.element_size() + B * Q * 4 * 4
         gbs = nbytes / (ms * 1e-3) / 1e9
@@ -320,29 +359,73 @@ class StepRunner:
                 "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "vocab": V,
                 "mean_accept_len": round(mean_len, 3)}
 
-    def roofline(self, attn_ms, name):
+    def roofline(self, kernel_ms, merge_ms, call_ms, name):
+        """Roofline of one verify_attn call's algorithmic work (flops and bytes as
+        attn_work counts them), over the attention kernel's mean launch time
+        (the dominant kernel: `frac`) and over the whole call (`call_frac`).  The
+        bound is the one the algorithmic intensity falls under: MFMA when
+        flops / bytes is at least the peak ratio, else HBM."""
         wl = self.wl
-        peak = PEAK_F32_TFLOPS if wl.dtype == "f32" else PEAK_BF16_TFLOPS
-        achieved = self.flops / (attn_ms * 1e-3) / 1e12
-        gbs = self.nbytes / (attn_ms * 1e-3) / 1e9
-        return {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+        peak_f = PEAK_F32_TFLOPS if wl.dtype == "f32" else PEAK_BF16_TFLOPS
+        ridge = peak_f * 1e12 / (PEAK_HBM_GBS * 1e9)
+        mfma = self.flops / self.nbytes >= ridge
+        tf = lambda ms: self.flops / (ms * 1e-3) / 1e12
+        gb = lambda ms: self.nbytes / (ms * 1e-3) / 1e9
+        if mfma:
+            ach, peak, unit, call_ach = tf(kernel_ms), peak_f, "TFLOP/s", tf(call_ms)
+        else:
+            ach, peak, unit, call_ach = gb(kernel_ms), PEAK_HBM_GBS, "GB/s", gb(call_ms)
+        return {"bound": "mfma" if mfma else "hbm", "achieved": round(ach, 3), "peak": peak,
+                "unit": unit, "frac": round(ach / peak, 4),
                 "traffic": measured_traffic(name),
-                "kernel": "verify_attn (attention + split-merge kernels)",
+                "kernel": ("verify_attn_wide_kernel" if wl.dtype == "bf16" and wl.d_lat == 512
+                           else "verify_attn_kernel"),
+                "kernel_us": round(kernel_ms * 1e3, 3), "merge_kernel_us": round(merge_ms * 1e3, 3),
+                "call_us": round(call_ms * 1e3, 3), "call_achieved": round(call_ach, 3),
+                "call_frac": round(call_ach / peak, 4),
                 "flops_per_launch": self.flops, "bytes_per_launch": self.nbytes,
-                "hbm_gbs_algorithmic": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
-                "launch_ms": round(attn_ms, 5)}
+                "kernel_tflops": round(tf(kernel_ms), 3),
+                "kernel_mfma_frac": round(tf(kernel_ms) / peak_f, 4),
+                "kernel_hbm_gbs": round(gb(kernel_ms), 1),
+                "kernel_hbm_frac": round(gb(kernel_ms) / PEAK_HBM_GBS, 4)}
+
+    def measure(self, steps, warmup, kernel_reps=MIN_REPLAYS):
+        """Step and attention-call graph replays plus kernel times; returns the
+        timings and the roofline."""
+        g_step, g_attn = self.capture(self.step), self.capture(self.attn)
+        self.torch.cuda.synchronize()
+        t_step = self.time_graph(g_step, steps, warmup)
+        t_call = self.time_graph(g_attn, max(steps, MIN_REPLAYS), warmup)
+        t_kern, t_merge = self.kernel_times(kernel_reps)
+        roof = self.roofline(t_kern.ms, t_merge.ms, t_call.ms, self.wl.name)
+        del g_step, g_attn
+        return t_step, t_call, t_kern, t_merge, roof
 
 
-def cpu_baseline(name, wl, host_tree, tgt_host, budget_s=12.0):
-    """The oracle on the host cores: one full step of the workload (tree build,
-    attention over every row, accept), repeated until about `budget_s` of work."""
-    import oracle
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_inputs(wl):
     f = lambda t: t.float().numpy()
-    q_lat, q_pe, c_kv, k_pe = f(wl.q_lat), f(wl.q_pe), f(wl.c_kv), f(wl.k_pe)
+    return f(wl.q_lat), f(wl.q_pe), f(wl.c_kv), f(wl.k_pe)
+
+
+def cpu_full_steps(wl, tgt_host, budget_s, max_reps=1000):
+    """The oracle running whole steps of the workload (tree build, attention over
+    every row in fp64, accept) until about `budget_s` of work; at least one."""
+    import oracle
+    q_lat, q_pe, c_kv, k_pe = _oracle_inputs(wl)
     reps, t_total = 0, 0.0
     t_build = t_attn = t_acc = 0.0
-    while t_total < budget_s and reps < 1000:
+    while (t_total < budget_s or reps == 0) and reps < max_reps:
         t0 = time.perf_counter()
         t = oracle.tree_build(wl.topk_logp, wl.topk_ids, wl.root_token, wl.prefix_len, wl.budget)
         t1 = time.perf_counter()
@@ -356,19 +439,86 @@ def cpu_baseline(name, wl, host_tree, tgt_host, budget_s=12.0):
         t_acc += t3 - t2
         t_total += t3 - t0
         reps += 1
-    per_step = t_total / reps
-    return {"value": round(1.0 / per_step, 3), "unit": "steps/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": (f"{reps} full steps of {name} (tree build, attention over all "
-                       f"{wl.B * wl.Q * wl.H} rows in fp64, accept), {t_total:.1f}s total; "
-                       f"per step build {t_build / reps * 1e3:.2f} ms, attention "
-                       f"{t_attn / reps * 1e3:.1f} ms, accept {t_acc / reps * 1e3:.3f} ms")}
+    return {"steps_per_s": round(reps / t_total, 4), "steps": reps, "seconds": round(t_total, 2),
+            "build_ms": round(t_build / reps * 1e3, 3), "attn_ms": round(t_attn / reps * 1e3, 2),
+            "accept_ms": round(t_acc / reps * 1e3, 4)}
+
+
+def cpu_sampled_step(wl, tgt_host, budget_s, seed=0):
+    """A whole oracle step of the workload estimated from a bounded sample: the
+    tree build and the accept run in full; the attention is timed on rows drawn
+    uniformly from all B*Q*H rows (doubling the sample until it takes about
+    `budget_s`) and scaled to every row."""
+    import oracle
+    q_lat, q_pe, c_kv, k_pe = _oracle_inputs(wl)
+    t0 = time.perf_counter()
+    t = oracle.tree_build(wl.topk_logp, wl.topk_ids, wl.root_token, wl.prefix_len, wl.budget)
+    t1 = time.perf_counter()
+    oracle.tree_accept(t["node_token"], t["parent"], t["n_nodes"], tgt_host)
+    t2 = time.perf_counter()
+    total_rows = wl.B * wl.Q * wl.H
+    rng = np.random.default_rng(seed)
+    n, t_rows, done = min(16, total_rows), 0.0, 0
+    while True:
+        idx = (np.arange(total_rows) if n == total_rows
+               else rng.integers(0, total_rows, size=n))
+        rows = np.stack([idx // (wl.Q * wl.H), (idx // wl.H) % wl.Q, idx % wl.H], axis=1)
+        ta = time.perf_counter()
+        oracle.verify_attn(q_lat, q_pe, c_kv, k_pe, wl.req_to_slot, wl.prefix_len, t["n_nodes"],
+                           t["vis"], wl.sm_scale, rows=rows)
+        t_rows += time.perf_counter() - ta
+        done += n
+        if t_rows >= budget_s or n == total_rows:
+            break
+        n = min(2 * n, total_rows)
+    per_step = (t1 - t0) + (t2 - t1) + t_rows / done * total_rows
+    return {"steps_per_s": round(1.0 / per_step, 4), "rows_evaluated": done,
+            "rows_per_step": total_rows, "seconds": round(t_rows + t2 - t0, 2)}
+
+
+def cpu_baseline(name, wl, tgt_host, budget_s=12.0, single_budget_s=6.0):
+    """The oracle on the host cores at the headline workload: whole steps on all
+    the threads the oracle runs with, then on one thread."""
+    import oracle
+    threads = oracle.num_threads()
+    full = cpu_full_steps(wl, tgt_host, budget_s)
+    oracle.set_num_threads(1)
+    try:
+        single = cpu_full_steps(wl, tgt_host, single_budget_s)
+    finally:
+        oracle.set_num_threads(threads)
+    return {"value": full["steps_per_s"], "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": (f"{full['steps']} full steps of {name} (tree build, attention over all "
+                       f"{wl.B * wl.Q * wl.H} rows in fp64, accept) in {full['seconds']} s on "
+                       f"{threads} threads; per step build {full['build_ms']} ms, attention "
+                       f"{full['attn_ms']} ms, accept {full['accept_ms']} ms"),
+            "cpu_model": cpu_model(),
+            "single_core": {"value": single["steps_per_s"], "unit": "steps/s", "cores": 1,
+                            "sample": f"{single['steps']} full steps in {single['seconds']} s"}}
+
+
+def cpu_config_estimate(wl, tgt_host, budget_s=2.0):
+    """Oracle steps/s of a workload on all threads and on one, each from a
+    bounded row sample (cpu_sampled_step)."""
+    import oracle
+    threads = oracle.num_threads()
+    allc = cpu_sampled_step(wl, tgt_host, budget_s)
+    oracle.set_num_threads(1)
+    try:
+        one = cpu_sampled_step(wl, tgt_host, budget_s, seed=1)
+    finally:
+        oracle.set_num_threads(threads)
+    return {"steps_per_s": allc["steps_per_s"], "cores": threads,
+            "rows_evaluated": allc["rows_evaluated"], "rows_per_step": allc["rows_per_step"],
+            "single_core_steps_per_s": one["steps_per_s"],
+            "single_core_rows_evaluated": one["rows_evaluated"]}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=200,
+                    help="headline step replays per timed repeat (5 repeats)")
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only-primary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
@@ -389,6 +539,8 @@ def main():
         print(f"bench.py: the verify step runs on one GPU; --gpus {args.gpus} is not "
               f"supported (no sharding or collectives across GPUs).", file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        raise SystemExit("bench.py: --steps must be >= 1 and --warmup >= 0")
 
     import torch
     import tree_verify_mla_ddt_amd as ddt
@@ -407,64 +559,81 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     if args.eager:
-        ms_step = runner.time_eager(runner.step, args.steps, args.warmup)
-        ms_attn = runner.time_eager(runner.attn, args.steps, args.warmup)
+        # Eager launches only (profilers see every kernel of every step).
+        t_step = runner.time_eager(runner.step, args.steps, args.warmup, repeats=1)
+        t_call = runner.time_eager(runner.attn, args.steps, args.warmup, repeats=1)
+        t_kern, t_merge = runner.kernel_times(args.steps, repeats=1)
+        roof = runner.roofline(t_kern.ms, t_merge.ms, t_call.ms, primary)
     else:
-        g_step = runner.capture(runner.step)
-        g_attn = runner.capture(runner.attn)
-        torch.cuda.synchronize()
-        ms_step = runner.time_graph(g_step, args.steps, args.warmup)
-        ms_attn = runner.time_graph(g_attn, args.steps, args.warmup)
-    ms_eager = runner.time_eager(runner.step, min(args.steps, 100), 5)
-    log(f"[bench] {primary}: step {ms_step * 1e3:.1f} us (graph), {ms_eager * 1e3:.1f} us "
-        f"(eager), attention {ms_attn * 1e3:.1f} us")
-    roof = runner.roofline(ms_attn, primary)
+        t_step, t_call, t_kern, t_merge, roof = runner.measure(args.steps, args.warmup)
+    t_eager = runner.time_eager(runner.step, min(args.steps, MIN_REPLAYS), 5)
+    log(f"[bench] {primary}: step {t_step.ms * 1e3:.1f} us (graph; repeats "
+        f"{t_step.per[0] * 1e3:.1f}-{t_step.per[-1] * 1e3:.1f}), {t_eager.ms * 1e3:.1f} us "
+        f"(eager), attention call {t_call.ms * 1e3:.1f} us, kernel {t_kern.ms * 1e3:.1f} us "
+        f"+ merge {t_merge.ms * 1e3:.1f} us")
     wl = runner.wl
     result = {
-        "metric": METRIC, "value": round(1000.0 / ms_step, 2), "unit": "steps/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "metric": METRIC, "value": round(1000.0 / t_step.ms, 2), "unit": "steps/s",
+        "n_gpus": 1, "steps": args.steps, "repeats": len(t_step.per), "warmup": args.warmup,
+        "ms_per_step": round(t_step.ms, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
-        "config": {"workload": primary, "batch": wl.B, "heads": wl.H, "prefix": int(wl.prefix_len[0]),
-                   "q_len": wl.Q, "drafter": f"{wl.D}x{wl.K}",
+        "config": {"workload": primary, "batch": wl.B, "heads": wl.H,
+                   "prefix": int(wl.prefix_len[0]), "q_len": wl.Q, "drafter": f"{wl.D}x{wl.K}",
                    "kv": f"{wl.dtype} {wl.d_lat}+{wl.d_rope}",
                    "step": "tree_build -> verify_attn -> tree_accept, HIP graph replay"},
         "roofline": roof,
-        "step_eager_ms": round(ms_eager, 5),
+        "step_us": t_step.summary(),
+        "attn_call_us": t_call.summary(),
+        "attn_kernel_us": t_kern.summary(),
+        "merge_kernel_us": t_merge.summary(),
+        "step_eager_us": t_eager.summary(),
         "kv_commit_step_ms": round(runner.commit_ms(), 5),
         "draft_topk": runner.topk_stats(),
         "accept_sampling": runner.sampling_stats(),
     }
 
+    cpu_cfg = {}
+    do_cpu = not args.no_cpu
+    if do_cpu:
+        log("[bench] timing the CPU oracle on the headline workload ...")
+        tgt_host = runner.tgt.cpu().numpy()
+        result["cpu_baseline"] = cpu_baseline(primary, wl, tgt_host)
+        cpu_cfg[primary] = cpu_config_estimate(wl, tgt_host)
+        log(f"[bench] oracle: {result['cpu_baseline']['value']} steps/s on "
+            f"{result['cpu_baseline']['cores']} threads, "
+            f"{result['cpu_baseline']['single_core']['value']} on one")
+
     extras = {}
     if not args.only_primary:
+        del runner
+        torch.cuda.empty_cache()
         for name in [n for n in [PRIMARY] + EXTRA if n != primary]:
             r = StepRunner(name, torch, ddt, workloads)
-            gs, ga = r.capture(r.step), r.capture(r.attn)
-            k = max(10, min(args.steps, 200))
-            ms_s = r.time_graph(gs, k, 5)
-            ms_a = r.time_graph(ga, k, 5)
-            rf = r.roofline(ms_a, name)
-            extras[name] = {"steps_per_s": round(1000.0 / ms_s, 2), "ms_per_step": round(ms_s, 5),
-                            "requests_per_s": round(r.wl.B * 1000.0 / ms_s, 1),
-                            "attn_ms": round(ms_a, 5), "attn_tflops": rf["achieved"],
-                            "attn_frac_peak": rf["frac"], "attn_hbm_gbs": rf["hbm_gbs_algorithmic"],
-                            "traffic": rf["traffic"], "dtype": r.wl.dtype,
+            t_s, t_c, t_k, t_m, rf = r.measure(MIN_REPLAYS, 5)
+            extras[name] = {"steps_per_s": round(1000.0 / t_s.ms, 2),
+                            "ms_per_step": round(t_s.ms, 5),
+                            "requests_per_s": round(r.wl.B * 1000.0 / t_s.ms, 1),
+                            "heads": r.wl.H, "dtype": r.wl.dtype,
+                            "step_us": t_s.summary(), "attn_call_us": t_c.summary(),
+                            "attn_kernel_us": t_k.summary(), "merge_kernel_us": t_m.summary(),
+                            "roofline": rf,
                             "kv_commit_step_ms": round(r.commit_ms(), 5),
                             "draft_topk": r.topk_stats(),
                             "accept_sampling": r.sampling_stats()}
-            log(f"[bench] {name}: step {ms_s * 1e3:.1f} us, attention {ms_a * 1e3:.1f} us = "
-                f"{rf['achieved']:.1f} TFLOP/s ({100 * rf['frac']:.1f}% of {rf['peak']})")
-            del r, gs, ga
+            log(f"[bench] {name}: step {t_s.ms * 1e3:.1f} us, attention kernel "
+                f"{t_k.ms * 1e3:.1f} us = {rf['achieved']:.1f} {rf['unit']} "
+                f"({100 * rf['frac']:.1f}% of {rf['peak']}), call {t_c.ms * 1e3:.1f} us "
+                f"({100 * rf['call_frac']:.1f}%)")
+            if do_cpu:
+                cpu_cfg[name] = cpu_config_estimate(r.wl, r.tgt.cpu().numpy())
+                log(f"[bench] oracle {name}: {cpu_cfg[name]['steps_per_s']} steps/s "
+                    f"(estimated from {cpu_cfg[name]['rows_evaluated']} of "
+                    f"{cpu_cfg[name]['rows_per_step']} rows)")
+            del r
             torch.cuda.empty_cache()
         result["extra_workloads"] = extras
-
-    if not args.no_cpu:
-        log("[bench] timing the CPU oracle ...")
-        result["cpu_baseline"] = cpu_baseline(primary, wl, runner.host_tree,
-                                              runner.tgt.cpu().numpy())
-        log(f"[bench] oracle: {result['cpu_baseline']['value']} steps/s on "
-            f"{result['cpu_baseline']['cores']} threads")
+    if do_cpu:
+        result["cpu_baseline"]["per_config"] = cpu_cfg
     print(json.dumps(result), flush=True)
 
 

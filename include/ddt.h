@@ -36,7 +36,9 @@
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  A call
  *    only validates its scalar arguments on the host and enqueues kernels on
  *    `stream`: it never synchronizes, never reads device memory on the host and
- *    never allocates, so it may be recorded into a HIP graph.
+ *    never allocates, so it may be recorded into a HIP graph.  The one
+ *    exception is the measurement aid ddt_verify_attn_kernel_times, which
+ *    waits for its own timing events.
  *  - Return value: DDT_OK, or a negative DDT_E* code with nothing enqueued (a
  *    launch failure, DDT_ELAUNCH, may leave earlier kernels of the same call
  *    enqueued).  ddt_last_error() then describes the failure.
@@ -172,6 +174,11 @@ int ddt_tree_build(const float* topk_logp, const int32_t* topk_ids,
  *   [0, min(Q, max_kv - L_b)]; an entry whose slot id is outside
  *   [0, num_slots) is not visible.
  * Accuracy: fp32 accumulation; bf16 probabilities feed the value product.
+ * Failure signal: the (DDT_BF16, 64, 16) and (DDT_F32, 64, 16) kernels pair
+ *   two wavefronts of a workgroup through a bounded wait; if a wait ever gave
+ *   up, the live rows of the wavefront that waited get out = NaN and
+ *   lse = NaN (also after the split merge), so a give-up can never pass as a
+ *   result.
  * ------------------------------------------------------------------------- */
 size_t ddt_verify_attn_workspace_size(int B, int Q, int H, int max_kv, int d_lat);
 
@@ -183,6 +190,28 @@ int ddt_verify_attn(const void* q_lat, const void* q_pe, const void* c_kv,
                     int d_rope, int dtype, float sm_scale, float* out,
                     float* lse, void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/* ---------------------------------------------------------------------------
+ * ddt_verify_attn_kernel_times -- measurement aid for ddt_verify_attn.
+ *
+ * Takes ddt_verify_attn's arguments, with the same checks and error codes,
+ * plus reps (1 <= reps <= 100000) and kernel_ms, a HOST array of 2 floats.
+ * Enqueues the call's attention kernel reps times back to back, then its
+ * merge kernel reps times, with HIP events on `stream` around each run of
+ * launches; waits for the last event and stores the mean time per launch in
+ * milliseconds: kernel_ms[0] attention kernel, kernel_ms[1] merge kernel
+ * (each includes the short gap between back-to-back launches).  out and lse
+ * then hold the result of ddt_verify_attn.  Unlike every other entry point it
+ * synchronizes (on its own events only) and so cannot be graph-captured.
+ * ------------------------------------------------------------------------- */
+int ddt_verify_attn_kernel_times(const void* q_lat, const void* q_pe, const void* c_kv,
+                                 const void* k_pe, int64_t num_slots,
+                                 const int32_t* req_to_slot, int max_kv,
+                                 const int32_t* prefix_len, const int32_t* n_nodes,
+                                 const uint64_t* vis, int B, int Q, int H, int d_lat,
+                                 int d_rope, int dtype, float sm_scale, float* out, float* lse,
+                                 void* workspace, size_t workspace_bytes, void* stream,
+                                 int reps, float* kernel_ms);
 
 /* ---------------------------------------------------------------------------
  * ddt_tree_accept -- greedy follow-the-verified-tree acceptance ([P2]
@@ -202,6 +231,10 @@ int ddt_verify_attn(const void* q_lat, const void* q_pe, const void* c_kv,
  * Semantics: from the root, move to the lowest-index child c (parent[c] == cur,
  * c > cur, c < n_b) whose node_token equals target_argmax[cur]; stop when there
  * is none.  n_b is clamped to [1, Q].  Bit-exact deterministic.
+ * Precondition of a consistent step: L_b + n_b <= max_kv for the slot table
+ *   that ddt_verify_attn and ddt_kv_commit use.  Those two clamp n_b to
+ *   max_kv - L_b; this call does not see max_kv, so a tree that overran the
+ *   table could accept a node that the commit then cuts off.
  * ------------------------------------------------------------------------- */
 int ddt_tree_accept(const int32_t* node_token, const int32_t* parent,
                     const int32_t* n_nodes, const int32_t* target_argmax,

@@ -66,10 +66,11 @@ def _load():
         lib.ddt_oracle_tree_accept_sampling.argtypes = (
             [p, i32, p, p, p, p, p, p, i32, i32, ctypes.c_double] + [p] * 7)
         lib.ddt_oracle_num_threads.argtypes = []
+        lib.ddt_oracle_set_num_threads.argtypes = [i32]
         for f in (lib.ddt_oracle_tree_build, lib.ddt_oracle_verify_attn_rows,
                   lib.ddt_oracle_tree_accept, lib.ddt_oracle_kv_commit,
                   lib.ddt_oracle_draft_topk, lib.ddt_oracle_tree_accept_sampling,
-                  lib.ddt_oracle_num_threads):
+                  lib.ddt_oracle_num_threads, lib.ddt_oracle_set_num_threads):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -82,6 +83,11 @@ def _c(a, dtype):
 
 def num_threads() -> int:
     return int(_load().ddt_oracle_num_threads())
+
+
+def set_num_threads(n: int) -> int:
+    """Threads the oracle's parallel loops use from now on; returns the count."""
+    return int(_load().ddt_oracle_set_num_threads(int(n)))
 
 
 def tree_build(topk_logp, topk_ids, root_token, prefix_len, budget: int) -> dict:

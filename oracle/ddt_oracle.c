@@ -49,6 +49,16 @@ int ddt_oracle_num_threads(void) {
 #endif
 }
 
+int ddt_oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+  return omp_get_max_threads();
+#else
+  (void)n;
+  return 1;
+#endif
+}
+
 /* ------------------------------------------------------------------------ */
 /* Tree build: best-first expansion ([P1] "What to Build New" item 3; [P2]    */
 /* tree_build row, which replaces the per-request CPU heap queue).            */

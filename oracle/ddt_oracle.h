@@ -139,6 +139,8 @@ int ddt_oracle_tree_accept_sampling(const float* logits, int V, const float* tem
 
 /* Number of OpenMP threads the oracle runs with (1 if built without OpenMP). */
 int ddt_oracle_num_threads(void);
+/* Threads of the later parallel regions (n >= 1); returns the new count. */
+int ddt_oracle_set_num_threads(int n);
 
 #ifdef __cplusplus
 }

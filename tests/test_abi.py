@@ -99,6 +99,27 @@ def test_verify_attn_rejects(lib, kw, code, needle):
     assert needle in ddt.last_error()
 
 
+def call_attn_times(lib, reps=10, null_ms=False, **kw):
+    p = ctypes.c_void_p(16)
+    ms = (ctypes.c_float * 2)()
+    B, Q = kw.get("B", 1), kw.get("Q", 9)
+    return lib.ddt_verify_attn_kernel_times(p, p, p, p, 100, p, 100, p, p, p, B, Q, 64, 512, 64,
+                                            ddt.DDT_BF16, ctypes.c_float(0.07), p, p, p, 1 << 40,
+                                            NULL, reps, NULL if null_ms else ms)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(reps=0), ddt.DDT_EINVAL, "reps=0"),
+    (dict(reps=100001), ddt.DDT_EINVAL, "reps=100001"),
+    (dict(null_ms=True), ddt.DDT_EINVAL, "NULL kernel_ms"),
+    (dict(B=0), ddt.DDT_EINVAL, "ddt_verify_attn_kernel_times: B=0"),
+    (dict(Q=129), ddt.DDT_EINVAL, "ddt_verify_attn_kernel_times: Q=129"),
+])
+def test_verify_attn_kernel_times_rejects(lib, kw, code, needle):
+    assert call_attn_times(lib, **kw) == code
+    assert needle in ddt.last_error()
+
+
 def test_workspace_size_query(lib):
     n = lib.ddt_verify_attn_workspace_size(8, 65, 64, 32833, 512)
     assert n > 0

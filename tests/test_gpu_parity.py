@@ -260,7 +260,8 @@ def test_verify_attn_full_oracle(name, overrides, shuffle):
     check_attn(g_out, g_lse, o_out, o_lse, TOL[wl.dtype], name)
 
 
-@pytest.mark.parametrize("name", ["b1_l2k_q9", "b4_l4k_q17", "b4_l4k_q33", "b64_l2k_q9"])
+@pytest.mark.parametrize("name", ["b1_l2k_q9", "b4_l4k_q17", "b4_l4k_q33", "b64_l2k_q9",
+                                  "b64_l2k_q9_h8", "b8_l32k_q65_h8"])
 def test_verify_attn_full_size_every_row(name):
     """The benchmark's full workloads, in the benchmark's launch configuration,
     every row against the oracle."""
@@ -351,6 +352,24 @@ def test_verify_attn_determinism():
     a2, l2 = gpu_attn(wl, wl.req_to_slot, wl.prefix_len, t["n_nodes"], t["vis"])
     np.testing.assert_array_equal(a1.view(np.uint32), a2.view(np.uint32))
     np.testing.assert_array_equal(l1.view(np.uint32), l2.view(np.uint32))
+
+
+@pytest.mark.parametrize("name,overrides", [("b4_l4k_q17", {"L": 900}),
+                                            ("b64_l2k_q9", {"L": 300})])
+def test_verify_attn_kernel_times_matches_call(name, overrides):
+    """The kernel-time measurement leaves the call's exact result in out / lse
+    and reports positive per-launch times."""
+    note(f"verify_attn kernel times {name} {overrides}")
+    wl = workloads.make_workload(name, **overrides)
+    t = tree_for(wl)
+    a1, l1 = gpu_attn(wl, wl.req_to_slot, wl.prefix_len, t["n_nodes"], t["vis"])
+    args = (dev(wl.q_lat), dev(wl.q_pe), dev(wl.c_kv), dev(wl.k_pe), dev(wl.req_to_slot),
+            dev(wl.prefix_len), dev(t["n_nodes"]), dev(t["vis"].view(np.int64)), wl.sm_scale)
+    ms_a, ms_m, out, lse = ddt.verify_attn_kernel_times(*args, reps=5)
+    torch.cuda.synchronize()
+    assert ms_a > 0.0 and ms_m > 0.0
+    np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), a1.view(np.uint32))
+    np.testing.assert_array_equal(lse.cpu().numpy().view(np.uint32), l1.view(np.uint32))
 
 
 # ----------------------------------------------------------------------------- composition

@@ -23,7 +23,8 @@ DDT_F32, DDT_BF16 = 0, 1
 MAX_Q = 128
 
 EXPORTED = ("ddt_version", "ddt_last_error", "ddt_tree_build",
-            "ddt_verify_attn_workspace_size", "ddt_verify_attn", "ddt_tree_accept",
+            "ddt_verify_attn_workspace_size", "ddt_verify_attn", "ddt_verify_attn_kernel_times",
+            "ddt_tree_accept",
             "ddt_kv_commit", "ddt_draft_topk_workspace_size", "ddt_draft_topk",
             "ddt_tree_accept_sampling_workspace_size", "ddt_tree_accept_sampling")
 
@@ -56,6 +57,8 @@ def load_library(path: str | None = None):
     lib.ddt_verify_attn.argtypes = ([vp, vp, vp, vp, i64, vp, i32, vp, vp, vp, i32, i32, i32, i32,
                                      i32, i32, f32, vp, vp, vp, sz, vp])
     lib.ddt_verify_attn.restype = i32
+    lib.ddt_verify_attn_kernel_times.argtypes = list(lib.ddt_verify_attn.argtypes) + [i32, vp]
+    lib.ddt_verify_attn_kernel_times.restype = i32
     lib.ddt_tree_accept.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp]
     lib.ddt_tree_accept.restype = i32
     lib.ddt_kv_commit.argtypes = [vp, i32, vp, vp, vp, vp, i32, i32, vp, vp, vp]
@@ -173,16 +176,10 @@ def workspace_size(B: int, Q: int, H: int, max_kv: int, d_lat: int) -> int:
     return int(load_library().ddt_verify_attn_workspace_size(B, Q, H, max_kv, d_lat))
 
 
-def verify_attn(q_lat: torch.Tensor, q_pe: torch.Tensor, c_kv: torch.Tensor, k_pe: torch.Tensor,
-                req_to_slot: torch.Tensor, prefix_len: torch.Tensor, n_nodes: torch.Tensor,
-                vis: torch.Tensor, sm_scale: float, out: torch.Tensor | None = None,
-                lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-                want_lse: bool = True):
-    """Tree-verify MLA-absorb attention (ddt_verify_attn).
-
-    q_lat [B,Q,H,d_lat], q_pe [B,Q,H,d_rope], c_kv [S,d_lat], k_pe [S,d_rope] (all bf16 or
-    all f32), req_to_slot [B,max_kv] i32, prefix_len [B] i32, n_nodes [B] i32,
-    vis [B,Q,W] int64.  Returns (out [B,Q,H,d_lat] f32, lse [B,Q,H] f32 or None)."""
+def _attn_args(q_lat, q_pe, c_kv, k_pe, req_to_slot, prefix_len, n_nodes, vis, sm_scale,
+               out, lse, workspace, want_lse):
+    """Checked C arguments of ddt_verify_attn (everything but the stream) and the
+    output tensors."""
     dt = q_lat.dtype
     if dt not in (torch.bfloat16, torch.float32):
         raise TypeError("q_lat must be bf16 or f32")
@@ -212,13 +209,41 @@ def verify_attn(q_lat: torch.Tensor, q_pe: torch.Tensor, c_kv: torch.Tensor, k_p
     lib = load_library()
     need = int(lib.ddt_verify_attn_workspace_size(B, Q, H, max_kv, d_lat))
     workspace = _workspace(workspace, need, dev)
-    rc = lib.ddt_verify_attn(
-        _ptr(q_lat), _ptr(q_pe), _ptr(c_kv), _ptr(k_pe), c_kv.shape[0], _ptr(req_to_slot), max_kv,
-        _ptr(prefix_len), _ptr(n_nodes), _ptr(vis), B, Q, H, d_lat, d_rope,
-        DDT_BF16 if dt == torch.bfloat16 else DDT_F32, float(sm_scale), _ptr(out), _ptr(lse),
-        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream())
-    _check(rc)
+    args = (_ptr(q_lat), _ptr(q_pe), _ptr(c_kv), _ptr(k_pe), S, _ptr(req_to_slot), max_kv,
+            _ptr(prefix_len), _ptr(n_nodes), _ptr(vis), B, Q, H, d_lat, d_rope,
+            DDT_BF16 if dt == torch.bfloat16 else DDT_F32, float(sm_scale), _ptr(out),
+            _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size())
+    return lib, args, out, lse
+
+
+def verify_attn(q_lat: torch.Tensor, q_pe: torch.Tensor, c_kv: torch.Tensor, k_pe: torch.Tensor,
+                req_to_slot: torch.Tensor, prefix_len: torch.Tensor, n_nodes: torch.Tensor,
+                vis: torch.Tensor, sm_scale: float, out: torch.Tensor | None = None,
+                lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                want_lse: bool = True):
+    """Tree-verify MLA-absorb attention (ddt_verify_attn).
+
+    q_lat [B,Q,H,d_lat], q_pe [B,Q,H,d_rope], c_kv [S,d_lat], k_pe [S,d_rope] (all bf16 or
+    all f32), req_to_slot [B,max_kv] i32, prefix_len [B] i32, n_nodes [B] i32,
+    vis [B,Q,W] int64.  Returns (out [B,Q,H,d_lat] f32, lse [B,Q,H] f32 or None)."""
+    lib, args, out, lse = _attn_args(q_lat, q_pe, c_kv, k_pe, req_to_slot, prefix_len, n_nodes,
+                                     vis, sm_scale, out, lse, workspace, want_lse)
+    _check(lib.ddt_verify_attn(*args, _stream()))
     return out, lse
+
+
+def verify_attn_kernel_times(q_lat, q_pe, c_kv, k_pe, req_to_slot, prefix_len, n_nodes, vis,
+                             sm_scale: float, reps: int, out=None, lse=None, workspace=None,
+                             want_lse: bool = True):
+    """Mean per-launch milliseconds of the attention kernel and of the merge kernel
+    of one ddt_verify_attn call, each launched `reps` times back to back between
+    HIP events on the current stream (ddt_verify_attn_kernel_times; synchronizes).
+    Returns (attention_ms, merge_ms, out, lse)."""
+    lib, args, out, lse = _attn_args(q_lat, q_pe, c_kv, k_pe, req_to_slot, prefix_len, n_nodes,
+                                     vis, sm_scale, out, lse, workspace, want_lse)
+    ms = (ctypes.c_float * 2)()
+    _check(lib.ddt_verify_attn_kernel_times(*args, _stream(), int(reps), ms))
+    return float(ms[0]), float(ms[1]), out, lse
 
 
 def tree_accept(node_token: torch.Tensor, parent: torch.Tensor, n_nodes: torch.Tensor,

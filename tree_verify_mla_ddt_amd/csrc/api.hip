@@ -1,9 +1,10 @@
 // api.hip -- the exported C entry points of libddt.so (declared in ddt.h).
 //
 // Each entry point validates its scalar arguments and pointers on the host,
-// then enqueues its kernels on the caller's stream.  No entry point
-// synchronizes, reads device memory on the host or allocates, so all of them
-// may be captured into a HIP graph.
+// then enqueues its kernels on the caller's stream.  No entry point reads
+// device memory on the host or allocates, and all but one never synchronize,
+// so they may be captured into a HIP graph.  The exception is the measurement
+// aid ddt_verify_attn_kernel_times, which waits for its own timing events.
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -83,40 +84,102 @@ size_t ddt_verify_attn_workspace_size(int B, int Q, int H, int max_kv, int d_lat
   return ddt::plan_verify_attn(B, Q, H, max_kv, d_lat, device_cu_count()).ws_bytes;
 }
 
+namespace {
+
+// Argument checks shared by ddt_verify_attn and its kernel-time measurement;
+// `who` names the entry point in the error text.  On success fills `plan`.
+int check_verify_attn(const char* who, const void* q_lat, const void* q_pe, const void* c_kv,
+                      const void* k_pe, int64_t num_slots, const int32_t* req_to_slot,
+                      int max_kv, const int32_t* prefix_len, const int32_t* n_nodes,
+                      const uint64_t* vis, int B, int Q, int H, int d_lat, int d_rope,
+                      int dtype, float sm_scale, const float* out, const void* workspace,
+                      size_t workspace_bytes, ddt::AttnPlan& plan) {
+  if (B < 1 || B > DDT_MAX_BATCH_ATTN)
+    return fail(DDT_EINVAL, "%s: B=%d outside [1, %d]", who, B, DDT_MAX_BATCH_ATTN);
+  if (Q < 1 || Q > DDT_MAX_Q)
+    return fail(DDT_EINVAL, "%s: Q=%d outside [1, %d]", who, Q, DDT_MAX_Q);
+  if (H < 1) return fail(DDT_EINVAL, "%s: H=%d must be >= 1", who, H);
+  if (max_kv < 1) return fail(DDT_EINVAL, "%s: max_kv=%d must be >= 1", who, max_kv);
+  if (num_slots < 1)
+    return fail(DDT_EINVAL, "%s: num_slots=%lld must be >= 1", who, (long long)num_slots);
+  if (dtype != DDT_F32 && dtype != DDT_BF16)
+    return fail(DDT_EINVAL, "%s: dtype=%d is not DDT_F32 or DDT_BF16", who, dtype);
+  if (!(sm_scale > 0.0f) || sm_scale == INFINITY)
+    return fail(DDT_EINVAL, "%s: sm_scale must be finite and > 0", who);
+  if (!attn_variant_supported(dtype, d_lat, d_rope))
+    return fail(DDT_EUNSUPPORTED,
+                "%s: (dtype=%d, d_lat=%d, d_rope=%d) not compiled in; supported: "
+                "(bf16,512,64) (bf16,64,16) (f32,64,16)", who, dtype, d_lat, d_rope);
+  if (!q_lat || !q_pe || !c_kv || !k_pe || !req_to_slot || !prefix_len || !n_nodes || !vis ||
+      !out)
+    return fail(DDT_EINVAL, "%s: NULL array argument", who);
+  plan = ddt::plan_verify_attn(B, Q, H, max_kv, d_lat, device_cu_count());
+  if (!workspace || workspace_bytes < plan.ws_bytes)
+    return fail(DDT_EINVAL, "%s: workspace of %zu bytes given, %zu needed", who,
+                workspace ? workspace_bytes : (size_t)0, plan.ws_bytes);
+  return DDT_OK;
+}
+
+}  // namespace
+
 int ddt_verify_attn(const void* q_lat, const void* q_pe, const void* c_kv, const void* k_pe,
                     int64_t num_slots, const int32_t* req_to_slot, int max_kv,
                     const int32_t* prefix_len, const int32_t* n_nodes, const uint64_t* vis,
                     int B, int Q, int H, int d_lat, int d_rope, int dtype, float sm_scale,
                     float* out, float* lse, void* workspace, size_t workspace_bytes,
                     void* stream) {
-  if (B < 1 || B > DDT_MAX_BATCH_ATTN)
-    return fail(DDT_EINVAL, "ddt_verify_attn: B=%d outside [1, %d]", B, DDT_MAX_BATCH_ATTN);
-  if (Q < 1 || Q > DDT_MAX_Q)
-    return fail(DDT_EINVAL, "ddt_verify_attn: Q=%d outside [1, %d]", Q, DDT_MAX_Q);
-  if (H < 1) return fail(DDT_EINVAL, "ddt_verify_attn: H=%d must be >= 1", H);
-  if (max_kv < 1) return fail(DDT_EINVAL, "ddt_verify_attn: max_kv=%d must be >= 1", max_kv);
-  if (num_slots < 1)
-    return fail(DDT_EINVAL, "ddt_verify_attn: num_slots=%lld must be >= 1", (long long)num_slots);
-  if (dtype != DDT_F32 && dtype != DDT_BF16)
-    return fail(DDT_EINVAL, "ddt_verify_attn: dtype=%d is not DDT_F32 or DDT_BF16", dtype);
-  if (!(sm_scale > 0.0f) || sm_scale == INFINITY)
-    return fail(DDT_EINVAL, "ddt_verify_attn: sm_scale must be finite and > 0");
-  if (!attn_variant_supported(dtype, d_lat, d_rope))
-    return fail(DDT_EUNSUPPORTED,
-                "ddt_verify_attn: (dtype=%d, d_lat=%d, d_rope=%d) not compiled in; supported: "
-                "(bf16,512,64) (bf16,64,16) (f32,64,16)", dtype, d_lat, d_rope);
-  if (!q_lat || !q_pe || !c_kv || !k_pe || !req_to_slot || !prefix_len || !n_nodes || !vis ||
-      !out)
-    return fail(DDT_EINVAL, "ddt_verify_attn: NULL array argument");
-  const ddt::AttnPlan plan = ddt::plan_verify_attn(B, Q, H, max_kv, d_lat, device_cu_count());
-  if (!workspace || workspace_bytes < plan.ws_bytes)
-    return fail(DDT_EINVAL, "ddt_verify_attn: workspace of %zu bytes given, %zu needed",
-                workspace ? workspace_bytes : (size_t)0, plan.ws_bytes);
+  ddt::AttnPlan plan;
+  const int rc = check_verify_attn("ddt_verify_attn", q_lat, q_pe, c_kv, k_pe, num_slots,
+                                   req_to_slot, max_kv, prefix_len, n_nodes, vis, B, Q, H,
+                                   d_lat, d_rope, dtype, sm_scale, out, workspace,
+                                   workspace_bytes, plan);
+  if (rc != DDT_OK) return rc;
   const hipError_t e = ddt::launch_verify_attn(
       dtype, d_lat, d_rope, q_lat, q_pe, c_kv, k_pe, num_slots, req_to_slot, max_kv, prefix_len,
       n_nodes, vis, B, Q, H, sm_scale, out, lse, workspace, plan,
       static_cast<hipStream_t>(stream));
   return launch_status(e, "ddt_verify_attn");
+}
+
+int ddt_verify_attn_kernel_times(const void* q_lat, const void* q_pe, const void* c_kv,
+                                 const void* k_pe, int64_t num_slots,
+                                 const int32_t* req_to_slot, int max_kv,
+                                 const int32_t* prefix_len, const int32_t* n_nodes,
+                                 const uint64_t* vis, int B, int Q, int H, int d_lat,
+                                 int d_rope, int dtype, float sm_scale, float* out, float* lse,
+                                 void* workspace, size_t workspace_bytes, void* stream,
+                                 int reps, float* kernel_ms) {
+  static const char* who = "ddt_verify_attn_kernel_times";
+  if (reps < 1 || reps > 100000)
+    return fail(DDT_EINVAL, "%s: reps=%d outside [1, 100000]", who, reps);
+  if (!kernel_ms) return fail(DDT_EINVAL, "%s: NULL kernel_ms", who);
+  ddt::AttnPlan plan;
+  const int rc = check_verify_attn(who, q_lat, q_pe, c_kv, k_pe, num_slots, req_to_slot,
+                                   max_kv, prefix_len, n_nodes, vis, B, Q, H, d_lat, d_rope,
+                                   dtype, sm_scale, out, workspace, workspace_bytes, plan);
+  if (rc != DDT_OK) return rc;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+  hipError_t e = hipSuccess;
+  for (int i = 0; i < 3 && e == hipSuccess; ++i) e = hipEventCreate(&ev[i]);
+  const int phase[2] = {ddt::kPhaseAttention, ddt::kPhaseMerge};
+  if (e == hipSuccess) e = hipEventRecord(ev[0], st);
+  for (int p = 0; p < 2 && e == hipSuccess; ++p) {
+    for (int r = 0; r < reps && e == hipSuccess; ++r)
+      e = ddt::launch_verify_attn(dtype, d_lat, d_rope, q_lat, q_pe, c_kv, k_pe, num_slots,
+                                  req_to_slot, max_kv, prefix_len, n_nodes, vis, B, Q, H,
+                                  sm_scale, out, lse, workspace, plan, st, phase[p]);
+    if (e == hipSuccess) e = hipEventRecord(ev[p + 1], st);
+  }
+  if (e == hipSuccess) e = hipEventSynchronize(ev[2]);
+  float ms[2] = {0.0f, 0.0f};
+  for (int p = 0; p < 2 && e == hipSuccess; ++p) e = hipEventElapsedTime(&ms[p], ev[p], ev[p + 1]);
+  for (int i = 0; i < 3; ++i)
+    if (ev[i]) (void)hipEventDestroy(ev[i]);
+  if (e != hipSuccess) return launch_status(e, who);
+  kernel_ms[0] = ms[0] / (float)reps;
+  kernel_ms[1] = ms[1] / (float)reps;
+  return DDT_OK;
 }
 
 int ddt_tree_accept(const int32_t* node_token, const int32_t* parent, const int32_t* n_nodes,

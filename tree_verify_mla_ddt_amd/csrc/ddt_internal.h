@@ -70,6 +70,12 @@ hipError_t launch_tree_accept_sampling(int dtype, const void* logits, int V,
 // The key range of every 128-row tile is split across a fixed grid of
 // workgroups (see attn_split.h, which holds the plan); partial results go to
 // the workspace and a merge kernel combines them.
+// Kernels of one verify-attention call: the attention kernel (prefix stream,
+// tree window, unsplit rows finished in place) and the merge of split rows.
+// A call runs both, in this order; the kernel-time measurement runs each
+// phase on its own.
+constexpr int kPhaseAttention = 1, kPhaseMerge = 2, kPhaseAll = 3;
+
 hipError_t launch_verify_attn(int dtype, int d_lat, int d_rope, const void* q_lat,
                               const void* q_pe, const void* c_kv, const void* k_pe,
                               int64_t num_slots, const int32_t* req_to_slot,
@@ -77,6 +83,6 @@ hipError_t launch_verify_attn(int dtype, int d_lat, int d_rope, const void* q_la
                               const int32_t* n_nodes, const uint64_t* vis, int B,
                               int Q, int H, float sm_scale, float* out, float* lse,
                               void* workspace, const AttnPlan& plan,
-                              hipStream_t stream);
+                              hipStream_t stream, int phases = kPhaseAll);
 
 }  // namespace ddt

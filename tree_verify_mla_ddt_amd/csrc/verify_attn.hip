@@ -1939,7 +1939,8 @@ hipError_t launch_impl(const void* q_lat, const void* q_pe, const void* c_kv, co
                        int64_t num_slots, const int32_t* req_to_slot, int max_kv,
                        const int32_t* prefix_len, const int32_t* n_nodes, const uint64_t* vis,
                        int B, int Q, int H, float sm_scale, float* out, float* lse,
-                       void* workspace, const AttnPlan& plan, hipStream_t stream) {
+                       void* workspace, const AttnPlan& plan, hipStream_t stream,
+                       int phases) {
   float* ws_o = static_cast<float*>(workspace);
   float* ws_lse = ws_o + (size_t)2 * plan.grid * kRowsPerWG * DL;
   long long* ws_pref = reinterpret_cast<long long*>(ws_lse + (size_t)2 * plan.grid * kRowsPerWG);
@@ -1947,7 +1948,8 @@ hipError_t launch_impl(const void* q_lat, const void* q_pe, const void* c_kv, co
   // that split can apply (B * row tiles >= G); the kernel decides from the data
   // whether it does.
   const bool split2 = (long long)B * plan.row_tiles >= plan.grid;
-  if constexpr (Geo<T, DL, DR>::kBF16 && DL == 512 && DR == 64) {
+  if (!(phases & kPhaseAttention)) {
+  } else if constexpr (Geo<T, DL, DR>::kBF16 && DL == 512 && DR == 64) {
     auto kernel = split2 ? verify_attn_wide_kernel<DL, DR, true>
                          : verify_attn_wide_kernel<DL, DR, false>;
     hipLaunchKernelGGL(kernel, dim3(split2 ? 2 * plan.grid : plan.grid), dim3(kThreadsW), 0,
@@ -1965,7 +1967,7 @@ hipError_t launch_impl(const void* q_lat, const void* q_pe, const void* c_kv, co
                        sm_scale, out, lse, ws_o, ws_lse, ws_pref, plan.grid, pair_spin_limit());
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !(phases & kPhaseMerge)) return e;
   // Thin merge workgroups (2 rows of 512) when there are so few row tiles that
   // the wide merge would leave most CUs idle.
   const int units = B * plan.row_tiles;
@@ -1990,20 +1992,20 @@ hipError_t launch_verify_attn(int dtype, int d_lat, int d_rope, const void* q_la
                               const int32_t* prefix_len, const int32_t* n_nodes,
                               const uint64_t* vis, int B, int Q, int H, float sm_scale,
                               float* out, float* lse, void* workspace, const AttnPlan& plan,
-                              hipStream_t stream) {
+                              hipStream_t stream, int phases) {
   // dtype: 0 = f32, 1 = bf16 (validated by the caller).
   if (dtype == 1 && d_lat == 512 && d_rope == 64)
     return launch_impl<uint16_t, 512, 64>(q_lat, q_pe, c_kv, k_pe, num_slots, req_to_slot,
                                           max_kv, prefix_len, n_nodes, vis, B, Q, H, sm_scale,
-                                          out, lse, workspace, plan, stream);
+                                          out, lse, workspace, plan, stream, phases);
   if (dtype == 1 && d_lat == 64 && d_rope == 16)
     return launch_impl<uint16_t, 64, 16>(q_lat, q_pe, c_kv, k_pe, num_slots, req_to_slot,
                                          max_kv, prefix_len, n_nodes, vis, B, Q, H, sm_scale,
-                                         out, lse, workspace, plan, stream);
+                                         out, lse, workspace, plan, stream, phases);
   if (dtype == 0 && d_lat == 64 && d_rope == 16)
     return launch_impl<float, 64, 16>(q_lat, q_pe, c_kv, k_pe, num_slots, req_to_slot, max_kv,
                                       prefix_len, n_nodes, vis, B, Q, H, sm_scale, out, lse,
-                                      workspace, plan, stream);
+                                      workspace, plan, stream, phases);
   return hipErrorInvalidValue;
 }
 

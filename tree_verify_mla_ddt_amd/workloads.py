@@ -18,6 +18,8 @@ case; one pool slot per token, prefix then tree entries per request):
                every 4th request has top-1 prob 0.995 (tree degenerates to a chain)
   b8_l32k_q65  B=8  H=64 512+64 bf16 L=32768   D=15 K=16  budget 64, top-1 prob 0.9,
                accept length drawn uniformly from 1..16 through the target tokens
+  b64_l2k_q9_h8, b8_l32k_q65_h8   the two above with H=8 (a tensor-parallel
+               rank's head share)
 """
 from __future__ import annotations
 
@@ -47,6 +49,10 @@ CONFIGS = {
                         D=15, K=16, budget=64, vocab=VOCAB_K2, p_match=None, seed=4,
                         all_p1=0.9, accept_lengths=(1, 16)),
 }
+# One GPU's share of the heads under 8-way tensor parallelism (64 / 8 = 8 heads):
+# the same requests with H = 8.
+CONFIGS["b64_l2k_q9_h8"] = dict(CONFIGS["b64_l2k_q9"], H=8)
+CONFIGS["b8_l32k_q65_h8"] = dict(CONFIGS["b8_l32k_q65"], H=8)
 DEFAULT_SM_SCALE = 1.0 / math.sqrt(128 + 64)
 
 
