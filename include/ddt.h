@@ -214,6 +214,33 @@ int ddt_verify_attn_kernel_times(const void* q_lat, const void* q_pe, const void
                                  int reps, float* kernel_ms);
 
 /* ---------------------------------------------------------------------------
+ * ddt_verify_attn_noalloc -- ddt_verify_attn for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops and harnesses
+ * that forbid hipMalloc): the same kernels and results, with the workspace
+ * taken from a static device array that each GPU holds from the library's
+ * first use until the process ends.
+ *
+ * Arguments, checks and outputs as for ddt_verify_attn, without the workspace.
+ * The array holds ddt_verify_attn_noalloc_max_bytes() bytes (about 128.3 MiB),
+ * the largest workspace ddt_verify_attn_workspace_size gives on a device of up
+ * to 256 compute units; a call whose plan needs more returns DDT_EUNSUPPORTED
+ * with nothing enqueued.  The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine); the first call on a device looks up that
+ * device's copy of the array once.  Every call on one GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (on different streams, or from
+ * different threads without ordering) race and give undefined results; calls
+ * ordered on one stream do not.  Nothing in the array needs clearing: each
+ * call writes every entry it reads.
+ * ------------------------------------------------------------------------- */
+size_t ddt_verify_attn_noalloc_max_bytes(void);
+
+int ddt_verify_attn_noalloc(const void* q_lat, const void* q_pe, const void* c_kv,
+                            const void* k_pe, int64_t num_slots, const int32_t* req_to_slot,
+                            int max_kv, const int32_t* prefix_len, const int32_t* n_nodes,
+                            const uint64_t* vis, int B, int Q, int H, int d_lat, int d_rope,
+                            int dtype, float sm_scale, float* out, float* lse, void* stream);
+
+/* ---------------------------------------------------------------------------
  * ddt_tree_accept -- greedy follow-the-verified-tree acceptance ([P2]
  * tree_accept row; composition with ddt_tree_build on device).
  *

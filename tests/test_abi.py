@@ -120,6 +120,31 @@ def test_verify_attn_kernel_times_rejects(lib, kw, code, needle):
     assert needle in ddt.last_error()
 
 
+def call_attn_noalloc(lib, B=1, Q=9, H=64, d_lat=512, d_rope=64, dtype=ddt.DDT_BF16,
+                      null_out=False):
+    p = ctypes.c_void_p(16)
+    return lib.ddt_verify_attn_noalloc(p, p, p, p, 100, p, 100, p, p, p, B, Q, H, d_lat, d_rope,
+                                       dtype, ctypes.c_float(0.07), NULL if null_out else p, p,
+                                       NULL)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(B=0), ddt.DDT_EINVAL, "ddt_verify_attn_noalloc: B=0"),
+    (dict(Q=129), ddt.DDT_EINVAL, "ddt_verify_attn_noalloc: Q=129"),
+    (dict(d_lat=256), ddt.DDT_EUNSUPPORTED, "not compiled in"),
+    (dict(null_out=True), ddt.DDT_EINVAL, "NULL"),
+])
+def test_verify_attn_noalloc_rejects(lib, kw, code, needle):
+    assert call_attn_noalloc(lib, **kw) == code
+    assert needle in ddt.last_error()
+
+
+def test_noalloc_scratch_size(lib):
+    # two partial 128-row tiles of 513 floats for each of 256 workgroups, and the
+    # work prefix of 512 requests
+    assert lib.ddt_verify_attn_noalloc_max_bytes() == 2 * 256 * 128 * 513 * 4 + 514 * 8
+
+
 def test_workspace_size_query(lib):
     n = lib.ddt_verify_attn_workspace_size(8, 65, 64, 32833, 512)
     assert n > 0

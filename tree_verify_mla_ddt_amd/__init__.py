@@ -24,7 +24,7 @@ MAX_Q = 128
 
 EXPORTED = ("ddt_version", "ddt_last_error", "ddt_tree_build",
             "ddt_verify_attn_workspace_size", "ddt_verify_attn", "ddt_verify_attn_kernel_times",
-            "ddt_tree_accept",
+            "ddt_verify_attn_noalloc_max_bytes", "ddt_verify_attn_noalloc", "ddt_tree_accept",
             "ddt_kv_commit", "ddt_draft_topk_workspace_size", "ddt_draft_topk",
             "ddt_tree_accept_sampling_workspace_size", "ddt_tree_accept_sampling")
 
@@ -59,6 +59,10 @@ def load_library(path: str | None = None):
     lib.ddt_verify_attn.restype = i32
     lib.ddt_verify_attn_kernel_times.argtypes = list(lib.ddt_verify_attn.argtypes) + [i32, vp]
     lib.ddt_verify_attn_kernel_times.restype = i32
+    lib.ddt_verify_attn_noalloc_max_bytes.argtypes = []
+    lib.ddt_verify_attn_noalloc_max_bytes.restype = sz
+    lib.ddt_verify_attn_noalloc.argtypes = list(lib.ddt_verify_attn.argtypes[:19]) + [vp]
+    lib.ddt_verify_attn_noalloc.restype = i32
     lib.ddt_tree_accept.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp]
     lib.ddt_tree_accept.restype = i32
     lib.ddt_kv_commit.argtypes = [vp, i32, vp, vp, vp, vp, i32, i32, vp, vp, vp]
@@ -177,9 +181,10 @@ def workspace_size(B: int, Q: int, H: int, max_kv: int, d_lat: int) -> int:
 
 
 def _attn_args(q_lat, q_pe, c_kv, k_pe, req_to_slot, prefix_len, n_nodes, vis, sm_scale,
-               out, lse, workspace, want_lse):
-    """Checked C arguments of ddt_verify_attn (everything but the stream) and the
-    output tensors."""
+               out, lse, workspace, want_lse, with_workspace=True):
+    """Checked C arguments of ddt_verify_attn (everything but the stream; without
+    the two workspace arguments when with_workspace is false) and the output
+    tensors."""
     dt = q_lat.dtype
     if dt not in (torch.bfloat16, torch.float32):
         raise TypeError("q_lat must be bf16 or f32")
@@ -207,12 +212,14 @@ def _attn_args(q_lat, q_pe, c_kv, k_pe, req_to_slot, prefix_len, n_nodes, vis, s
     if lse is not None:
         _dev(lse, "lse", torch.float32, shape=(B, Q, H), device=dev)
     lib = load_library()
-    need = int(lib.ddt_verify_attn_workspace_size(B, Q, H, max_kv, d_lat))
-    workspace = _workspace(workspace, need, dev)
     args = (_ptr(q_lat), _ptr(q_pe), _ptr(c_kv), _ptr(k_pe), S, _ptr(req_to_slot), max_kv,
             _ptr(prefix_len), _ptr(n_nodes), _ptr(vis), B, Q, H, d_lat, d_rope,
             DDT_BF16 if dt == torch.bfloat16 else DDT_F32, float(sm_scale), _ptr(out),
-            _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size())
+            _ptr(lse))
+    if with_workspace:
+        need = int(lib.ddt_verify_attn_workspace_size(B, Q, H, max_kv, d_lat))
+        workspace = _workspace(workspace, need, dev)
+        args += (_ptr(workspace), workspace.numel() * workspace.element_size())
     return lib, args, out, lse
 
 
@@ -229,6 +236,20 @@ def verify_attn(q_lat: torch.Tensor, q_pe: torch.Tensor, c_kv: torch.Tensor, k_p
     lib, args, out, lse = _attn_args(q_lat, q_pe, c_kv, k_pe, req_to_slot, prefix_len, n_nodes,
                                      vis, sm_scale, out, lse, workspace, want_lse)
     _check(lib.ddt_verify_attn(*args, _stream()))
+    return out, lse
+
+
+def verify_attn_noalloc(q_lat: torch.Tensor, q_pe: torch.Tensor, c_kv: torch.Tensor,
+                        k_pe: torch.Tensor, req_to_slot: torch.Tensor, prefix_len: torch.Tensor,
+                        n_nodes: torch.Tensor, vis: torch.Tensor, sm_scale: float,
+                        out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                        want_lse: bool = True):
+    """ddt_verify_attn_noalloc: verify_attn with the library's static scratch array
+    as workspace.  Pass `out` (and `lse`, or want_lse=False) to allocate nothing."""
+    lib, args, out, lse = _attn_args(q_lat, q_pe, c_kv, k_pe, req_to_slot, prefix_len, n_nodes,
+                                     vis, sm_scale, out, lse, None, want_lse,
+                                     with_workspace=False)
+    _check(lib.ddt_verify_attn_noalloc(*args, _stream()))
     return out, lse
 
 

@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(HERE, "libddt.so")
 # Host-side checker of the attention work split (CPU tests only).
 CHECK_PATH = os.path.join(HERE, "libddt_split_check.so")
 SOURCES = ["api.hip", "draft_topk.hip", "tree_build.hip", "tree_accept.hip",
-           "tree_accept_sampling.hip", "kv_commit.hip", "verify_attn.hip"]
+           "tree_accept_sampling.hip", "kv_commit.hip", "verify_attn.hip", "noalloc.hip"]
 ARCH = os.environ.get("DDT_OFFLOAD_ARCH", "gfx950")
 
 

@@ -12,8 +12,10 @@
 #include "ddt_internal.h"
 
 namespace {
-
 thread_local char g_err[512] = "";
+}  // namespace
+
+namespace ddt {
 
 int fail(int code, const char* fmt, ...) {
   va_list ap;
@@ -46,7 +48,51 @@ bool attn_variant_supported(int dtype, int d_lat, int d_rope) {
          (dtype == DDT_F32 && d_lat == 64 && d_rope == 16);
 }
 
-}  // namespace
+}  // namespace ddt
+
+using ddt::attn_variant_supported;
+using ddt::device_cu_count;
+using ddt::fail;
+using ddt::launch_status;
+using ddt::ok;
+
+namespace ddt {
+
+int check_verify_attn(const char* who, const void* q_lat, const void* q_pe, const void* c_kv,
+                      const void* k_pe, int64_t num_slots, const int32_t* req_to_slot,
+                      int max_kv, const int32_t* prefix_len, const int32_t* n_nodes,
+                      const uint64_t* vis, int B, int Q, int H, int d_lat, int d_rope,
+                      int dtype, float sm_scale, const float* out, const void* workspace,
+                      size_t workspace_bytes, bool check_ws, AttnPlan& plan) {
+  if (B < 1 || B > DDT_MAX_BATCH_ATTN)
+    return fail(DDT_EINVAL, "%s: B=%d outside [1, %d]", who, B, DDT_MAX_BATCH_ATTN);
+  if (Q < 1 || Q > DDT_MAX_Q)
+    return fail(DDT_EINVAL, "%s: Q=%d outside [1, %d]", who, Q, DDT_MAX_Q);
+  if (H < 1) return fail(DDT_EINVAL, "%s: H=%d must be >= 1", who, H);
+  if (max_kv < 1) return fail(DDT_EINVAL, "%s: max_kv=%d must be >= 1", who, max_kv);
+  if (num_slots < 1)
+    return fail(DDT_EINVAL, "%s: num_slots=%lld must be >= 1", who, (long long)num_slots);
+  if (dtype != DDT_F32 && dtype != DDT_BF16)
+    return fail(DDT_EINVAL, "%s: dtype=%d is not DDT_F32 or DDT_BF16", who, dtype);
+  if (!(sm_scale > 0.0f) || sm_scale == INFINITY)
+    return fail(DDT_EINVAL, "%s: sm_scale must be finite and > 0", who);
+  if (!attn_variant_supported(dtype, d_lat, d_rope))
+    return fail(DDT_EUNSUPPORTED,
+                "%s: (dtype=%d, d_lat=%d, d_rope=%d) not compiled in; supported: "
+                "(bf16,512,64) (bf16,64,16) (f32,64,16)", who, dtype, d_lat, d_rope);
+  if (!q_lat || !q_pe || !c_kv || !k_pe || !req_to_slot || !prefix_len || !n_nodes || !vis ||
+      !out)
+    return fail(DDT_EINVAL, "%s: NULL array argument", who);
+  plan = ddt::plan_verify_attn(B, Q, H, max_kv, d_lat, device_cu_count());
+  if (check_ws && (!workspace || workspace_bytes < plan.ws_bytes))
+    return fail(DDT_EINVAL, "%s: workspace of %zu bytes given, %zu needed", who,
+                workspace ? workspace_bytes : (size_t)0, plan.ws_bytes);
+  return DDT_OK;
+}
+
+}  // namespace ddt
+
+using ddt::check_verify_attn;
 
 extern "C" {
 
@@ -84,43 +130,6 @@ size_t ddt_verify_attn_workspace_size(int B, int Q, int H, int max_kv, int d_lat
   return ddt::plan_verify_attn(B, Q, H, max_kv, d_lat, device_cu_count()).ws_bytes;
 }
 
-namespace {
-
-// Argument checks shared by ddt_verify_attn and its kernel-time measurement;
-// `who` names the entry point in the error text.  On success fills `plan`.
-int check_verify_attn(const char* who, const void* q_lat, const void* q_pe, const void* c_kv,
-                      const void* k_pe, int64_t num_slots, const int32_t* req_to_slot,
-                      int max_kv, const int32_t* prefix_len, const int32_t* n_nodes,
-                      const uint64_t* vis, int B, int Q, int H, int d_lat, int d_rope,
-                      int dtype, float sm_scale, const float* out, const void* workspace,
-                      size_t workspace_bytes, ddt::AttnPlan& plan) {
-  if (B < 1 || B > DDT_MAX_BATCH_ATTN)
-    return fail(DDT_EINVAL, "%s: B=%d outside [1, %d]", who, B, DDT_MAX_BATCH_ATTN);
-  if (Q < 1 || Q > DDT_MAX_Q)
-    return fail(DDT_EINVAL, "%s: Q=%d outside [1, %d]", who, Q, DDT_MAX_Q);
-  if (H < 1) return fail(DDT_EINVAL, "%s: H=%d must be >= 1", who, H);
-  if (max_kv < 1) return fail(DDT_EINVAL, "%s: max_kv=%d must be >= 1", who, max_kv);
-  if (num_slots < 1)
-    return fail(DDT_EINVAL, "%s: num_slots=%lld must be >= 1", who, (long long)num_slots);
-  if (dtype != DDT_F32 && dtype != DDT_BF16)
-    return fail(DDT_EINVAL, "%s: dtype=%d is not DDT_F32 or DDT_BF16", who, dtype);
-  if (!(sm_scale > 0.0f) || sm_scale == INFINITY)
-    return fail(DDT_EINVAL, "%s: sm_scale must be finite and > 0", who);
-  if (!attn_variant_supported(dtype, d_lat, d_rope))
-    return fail(DDT_EUNSUPPORTED,
-                "%s: (dtype=%d, d_lat=%d, d_rope=%d) not compiled in; supported: "
-                "(bf16,512,64) (bf16,64,16) (f32,64,16)", who, dtype, d_lat, d_rope);
-  if (!q_lat || !q_pe || !c_kv || !k_pe || !req_to_slot || !prefix_len || !n_nodes || !vis ||
-      !out)
-    return fail(DDT_EINVAL, "%s: NULL array argument", who);
-  plan = ddt::plan_verify_attn(B, Q, H, max_kv, d_lat, device_cu_count());
-  if (!workspace || workspace_bytes < plan.ws_bytes)
-    return fail(DDT_EINVAL, "%s: workspace of %zu bytes given, %zu needed", who,
-                workspace ? workspace_bytes : (size_t)0, plan.ws_bytes);
-  return DDT_OK;
-}
-
-}  // namespace
 
 int ddt_verify_attn(const void* q_lat, const void* q_pe, const void* c_kv, const void* k_pe,
                     int64_t num_slots, const int32_t* req_to_slot, int max_kv,
@@ -132,7 +141,7 @@ int ddt_verify_attn(const void* q_lat, const void* q_pe, const void* c_kv, const
   const int rc = check_verify_attn("ddt_verify_attn", q_lat, q_pe, c_kv, k_pe, num_slots,
                                    req_to_slot, max_kv, prefix_len, n_nodes, vis, B, Q, H,
                                    d_lat, d_rope, dtype, sm_scale, out, workspace,
-                                   workspace_bytes, plan);
+                                   workspace_bytes, true, plan);
   if (rc != DDT_OK) return rc;
   const hipError_t e = ddt::launch_verify_attn(
       dtype, d_lat, d_rope, q_lat, q_pe, c_kv, k_pe, num_slots, req_to_slot, max_kv, prefix_len,
@@ -156,7 +165,8 @@ int ddt_verify_attn_kernel_times(const void* q_lat, const void* q_pe, const void
   ddt::AttnPlan plan;
   const int rc = check_verify_attn(who, q_lat, q_pe, c_kv, k_pe, num_slots, req_to_slot,
                                    max_kv, prefix_len, n_nodes, vis, B, Q, H, d_lat, d_rope,
-                                   dtype, sm_scale, out, workspace, workspace_bytes, plan);
+                                   dtype, sm_scale, out, workspace, workspace_bytes, true,
+                                   plan);
   if (rc != DDT_OK) return rc;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   hipEvent_t ev[3] = {nullptr, nullptr, nullptr};

@@ -1,8 +1,9 @@
 // ddt_internal.h -- declarations shared by the HIP sources of libddt.so.
 //
 // Kernels are written for gfx950 (CDNA4): 64-lane wavefronts, MFMA matrix
-// cores, 160 KiB of LDS per compute unit.  Only the C entry points in api.hip
-// are exported; everything here has internal visibility.
+// cores, 160 KiB of LDS per compute unit.  The library's interface is the C
+// entry points that ddt.h declares (api.hip, noalloc.hip); the C++ functions
+// declared here are internal to it and not part of that interface.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -84,5 +85,25 @@ hipError_t launch_verify_attn(int dtype, int d_lat, int d_rope, const void* q_la
                               int Q, int H, float sm_scale, float* out, float* lse,
                               void* workspace, const AttnPlan& plan,
                               hipStream_t stream, int phases = kPhaseAll);
+
+// Helpers of the C entry points (api.hip).  fail() records the message that
+// ddt_last_error() returns and passes `code` through; ok() clears it;
+// launch_status() maps a HIP launch status to DDT_OK / DDT_ELAUNCH.
+int fail(int code, const char* fmt, ...);
+int ok();
+int launch_status(hipError_t e, const char* what);
+int device_cu_count();  // compute units of the current device, 0 if unknown
+bool attn_variant_supported(int dtype, int d_lat, int d_rope);
+
+// Checks of ddt_verify_attn's arguments; `who` names the entry point in the
+// error text.  On success fills `plan` from the current device.  With
+// check_ws false the workspace arguments are ignored (the caller supplies the
+// workspace itself and checks its size against plan.ws_bytes).
+int check_verify_attn(const char* who, const void* q_lat, const void* q_pe, const void* c_kv,
+                      const void* k_pe, int64_t num_slots, const int32_t* req_to_slot,
+                      int max_kv, const int32_t* prefix_len, const int32_t* n_nodes,
+                      const uint64_t* vis, int B, int Q, int H, int d_lat, int d_rope,
+                      int dtype, float sm_scale, const float* out, const void* workspace,
+                      size_t workspace_bytes, bool check_ws, AttnPlan& plan);
 
 }  // namespace ddt
