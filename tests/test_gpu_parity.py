@@ -297,6 +297,33 @@ def test_verify_attn_max_shape():
                o_out, o_lse, TOL[wl.dtype], "b8_l32k_q65")
 
 
+@pytest.mark.parametrize("name,overrides", [
+    ("b1_l2k_q9", {}),                                   # narrow form, linear split
+    ("b4_l4k_q33", {"L": 900}),                          # wide form, linear split
+    ("b8_l32k_q65", {"L": 600}),                         # wide form, aligned split
+    ("b64_l2k_q9", {"H": 8, "L": 700}),                  # narrow form, aligned split
+    ("tiny_fp32", {"dtype": "bf16", "B": 3, "H": 16, "L": 300, "budget": 70, "D": 9,
+                   "K": 4}),                             # 64+16 kernel
+])
+def test_verify_attn_far_larger_later_scores(name, overrides):
+    """Keys whose rotary part is scaled by 128 (exactly, in bf16) score far
+    above everything else, so a key range that meets one after its first tile
+    sees scores more than 2^64 above the reference the 512-wide kernels fix at
+    their first tile, and runs again with the range's largest score (and the
+    64-wide kernel rescales).  Every row against the oracle."""
+    note(f"verify_attn far larger later scores {name} {overrides}")
+    wl = workloads.make_workload(name, **overrides)
+    t = tree_for(wl)
+    k_pe = wl.k_pe.clone()
+    for b in range(wl.B):
+        for j in (40, 100, 333, 700, 1500, 2000):
+            if j < int(wl.prefix_len[b]):
+                k_pe[int(wl.req_to_slot[b, j])] *= 128
+    g_out, g_lse = gpu_attn(wl, wl.req_to_slot, wl.prefix_len, t["n_nodes"], t["vis"], k_pe=k_pe)
+    o_out, o_lse = oracle_attn(wl, wl.req_to_slot, wl.prefix_len, t["n_nodes"], t["vis"], k_pe=k_pe)
+    check_attn(g_out, g_lse, o_out, o_lse, TOL[wl.dtype], name)
+
+
 def test_verify_attn_edge_cases():
     """Underfull trees, empty prefixes, single-node trees, out-of-range slot
     ids and clamped lengths, all against the oracle."""

@@ -87,3 +87,32 @@ def test_planted_mistake_is_caught(checker, plant):
     for plen, nn, Q, H in (([2048], [9], 9, 64), ([32768] * 8, [65] * 8, 65, 64)):
         rc, msg = run(checker, plen, nn, Q, H, max(plen) + Q, plant=plant)
         assert rc != 0 and "contributors" in msg, (plant, msg)
+
+
+def plan(lib, B, Q, H, max_kv, d_lat=512, num_cu=256):
+    lib.ddt_split_plan.argtypes = [ctypes.c_int] * 6 + [ctypes.c_void_p] * 4
+    g, nar, rt = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    ws = ctypes.c_ulonglong()
+    lib.ddt_split_plan(B, Q, H, max_kv, d_lat, num_cu, ctypes.byref(g), ctypes.byref(nar),
+                       ctypes.byref(rt), ctypes.byref(ws))
+    return g.value, bool(nar.value), rt.value, ws.value
+
+
+@pytest.mark.parametrize("B,Q,H,L,narrow", [
+    (1, 9, 64, 2048, True),      # 5 row tiles: quarter workgroups
+    (3, 9, 64, 2048, True),      # 15 row tiles
+    (4, 17, 64, 5120, False),    # 36 row tiles: the 128-row form
+    (4, 33, 64, 5120, False),
+    (64, 9, 64, 2048, False),
+    (8, 65, 64, 32768, False),
+    (64, 9, 8, 2048, False),     # the 8-head share: one row tile per request
+    (16, 9, 8, 2048, True),
+])
+def test_narrow_form_choice(checker, B, Q, H, L, narrow):
+    g, nar, rt, ws = plan(checker, B, Q, H, L + Q)
+    assert nar == narrow
+    assert 1 <= g <= (64 if nar else 256)
+    assert (not nar) or B * rt * 16 <= 256
+    assert ws == 2 * g * 128 * 513 * 4 + (B + 2) * 8
+    # the 64-wide latent form never takes it
+    assert not plan(checker, B, Q, H, L + Q, d_lat=64)[1]

@@ -140,6 +140,19 @@ DDT_HD long long contributor_slot(long long gg, long long S_u, long long W, long
   return partial_slot(gg, s0 >= S_u);
 }
 
+// The narrow form runs four workgroups per range, one per 32-row quarter of
+// its row tiles.  Workgroup bid serves range 8 * (bid / 32) + bid % 8 and
+// quarter (bid / 8) % 4, so the four quarters of a range are dealt to the same
+// XCD (bid % 8) and share its L2; the ranges are padded to a multiple of 8.
+constexpr int kQuarters = kRowsPerWG / 32;
+DDT_HD long long narrow_blocks(long long ranges) {
+  return (long long)kQuarters * kXcds * ((ranges + kXcds - 1) / kXcds);
+}
+DDT_HD void narrow_place(long long bid, long long& range, int& quarter) {
+  range = kXcds * (bid / (kXcds * kQuarters)) + bid % kXcds;
+  quarter = (int)((bid / kXcds) % kQuarters);
+}
+
 // One unit (a row tile over a key range) of a workgroup's range: the unit
 // starting at stream position pos, inside request b (pref[b] <= pos <
 // pref[b + 1]).
@@ -163,13 +176,15 @@ DDT_HD UnitPos unit_at(long long pos, long long end, long long pref_b, const Req
 // The attention launch: grid (workgroups per half), row tiles per request and
 // the workspace it needs.
 struct AttnPlan {
-  int grid;          // attention workgroups (at most one per CU)
+  int grid;          // work ranges (attention workgroups per half of the wide form)
   int row_tiles;     // ceil(Q*H / 128)
   int num_cu;        // compute units the plan was made for
+  bool narrow;       // four 32-row workgroups per range instead of one 128-row one
   size_t ws_bytes;   // workspace bytes needed
 };
 
-constexpr int kMinTilesPerWG = 3;  // key tiles per workgroup before splitting further
+constexpr int kMinTilesPerWG = 3;    // key tiles per workgroup before splitting further
+constexpr int kMinTilesNarrow = 4;   // ... per range of the narrow form
 
 inline AttnPlan plan_verify_attn(int B, int Q, int H, int max_kv, int d_lat, int num_cu) {
   AttnPlan p;
@@ -177,21 +192,30 @@ inline AttnPlan plan_verify_attn(int B, int Q, int H, int max_kv, int d_lat, int
   p.row_tiles = (int)((rows + kRowsPerWG - 1) / kRowsPerWG);
   const long long nkb = ((long long)max_kv + kTileKeys - 1) / kTileKeys;
   const long long work = (long long)B * p.row_tiles * nkb;
-  // One resident workgroup per CU (register-bound), but at least kMinTilesPerWG
-  // key tiles each so that query loads and partial outputs stay a small share.
+  // One resident workgroup per CU (LDS-bound), but at least min_tiles key
+  // tiles each so that query loads and partial outputs stay a small share.
   long long cap = num_cu > 0 ? num_cu : 256;
   if (cap > kMaxGrid) cap = kMaxGrid;
   const long long units = (long long)B * p.row_tiles;
-  const long long per_unit = (nkb + kMinTilesPerWG - 1) / kMinTilesPerWG;
+  // Very few row tiles (the 512-wide latent form only, at most a sixteenth of
+  // the CUs, as at batch 1): a range's row tiles are taken by four workgroups
+  // of 32 rows each, so that each row tile is cut into a quarter as many
+  // ranges for the same number of busy CUs, which quarters the partial rows
+  // written and merged.  Each of the four loads the key tiles itself, so with
+  // more row tiles the 128-row form is faster.
+  p.narrow = d_lat == 512 && units * 16 <= cap;
+  const int min_tiles = p.narrow ? kMinTilesNarrow : kMinTilesPerWG;
+  if (p.narrow) cap /= 4;
+  const long long per_unit = (nkb + min_tiles - 1) / min_tiles;
   long long g;
   if (units * per_unit <= cap) {
-    // Few row tiles: cut each into ranges of at most kMinTilesPerWG tiles, so
+    // Few row tiles: cut each into ranges of at most min_tiles tiles, so
     // that every workgroup's range lies inside one row tile (one query load,
     // one partial output) and none is longer than that.
     g = units * per_unit;
   } else {
     g = cap;
-    const long long by_work = (work + kMinTilesPerWG - 1) / kMinTilesPerWG;
+    const long long by_work = (work + min_tiles - 1) / min_tiles;
     if (by_work < g) g = by_work;
     // When a multiple of the row-tile count comes within 10% of that, take it
     // (requests of equal length then give ranges inside one row tile).

@@ -9,7 +9,9 @@
 //    [0, 2G) (the workspace holds 2G), and no slot is written by two units;
 //  * for every row tile, the merge's contributor rule names exactly the slots
 //    the attention kernel wrote for it (none for a tile written directly);
-//  * the grid, the batch and the contributor counts fit the kernels' limits.
+//  * the grid, the batch and the contributor counts fit the kernels' limits;
+//  * in the narrow form, the launch's workgroups take every (range, quarter)
+//    exactly once and the padding workgroups none.
 // Host code only (no kernels); built into its own library for the CPU tests.
 #include <stdio.h>
 
@@ -43,6 +45,22 @@ extern "C" int ddt_split_check(int B, int Q, int H, int max_kv, const int32_t* p
   const size_t need = (size_t)2 * G * kRowsPerWG * ((size_t)d_lat + 1) * sizeof(float) +
                       ((size_t)B + 2) * sizeof(long long);
   if (plan.ws_bytes < need) return fail(msg, msg_len, "workspace too small", (long long)plan.ws_bytes, (long long)need, 0);
+
+  if (plan.narrow) {
+    if (d_lat != 512) return fail(msg, msg_len, "narrow form for another width", d_lat, 0, 0);
+    const long long ranges = ((long long)B * RT >= G ? 2 : 1) * G;
+    const long long blocks = narrow_blocks(ranges);
+    std::vector<int> seen((size_t)(ranges * kQuarters), 0);
+    for (long long bid = 0; bid < blocks; ++bid) {
+      long long r;
+      int q;
+      narrow_place(bid, r, q);
+      if (q < 0 || q >= kQuarters || r < 0) return fail(msg, msg_len, "narrow place", bid, r, q);
+      if (r < ranges) ++seen[(size_t)(r * kQuarters + q)];
+    }
+    for (size_t i = 0; i < seen.size(); ++i)
+      if (seen[i] != 1) return fail(msg, msg_len, "narrow (range, quarter) taken", (long long)i, seen[i], blocks);
+  }
 
   std::vector<ReqInfo> ri(B);
   std::vector<long long> pref(B + 1, 0);
@@ -131,5 +149,16 @@ extern "C" int ddt_split_check(int B, int Q, int H, int max_kv, const int32_t* p
       if (direct.count(unit)) return fail(msg, msg_len, "cut tile also written whole", b, rt, 0);
     }
   }
+  return 0;
+}
+
+// The plan itself, for tests that check which form a shape takes.
+extern "C" int ddt_split_plan(int B, int Q, int H, int max_kv, int d_lat, int num_cu, int* grid,
+                              int* narrow, int* row_tiles, unsigned long long* ws_bytes) {
+  const ddt::AttnPlan p = ddt::plan_verify_attn(B, Q, H, max_kv, d_lat, num_cu);
+  *grid = p.grid;
+  *narrow = p.narrow ? 1 : 0;
+  *row_tiles = p.row_tiles;
+  *ws_bytes = p.ws_bytes;
   return 0;
 }

@@ -68,14 +68,20 @@ typedef __bf16 bf16x4_lds_t __attribute__((__vector_size__(4 * sizeof(__bf16))))
 constexpr int kSplit = 2;                // waves sharing one 32-row block
 constexpr int kWaves = 4 * kSplit;
 constexpr int kThreads = kWaves * kWave;
-constexpr int kRing = 3;                 // slot-id ring (tiles kb .. kb+2)
+// Slot-id ring: tiles kb-1 .. kb+2.  A wave publishes the slot ids of tile
+// kb+2 during step kb, while a slower wave of the same step may still mask
+// tile kb-1 with that tile's validity bits, so four entries are live.
+constexpr int kRing = 4;
 constexpr int kStages = 3;               // key-tile stages in LDS (tiles kb-1 .. kb+1)
 constexpr int kMergeThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // A tile takes the residual pass when some key's probability exceeds this share
-// of its row's running sum (an upper bound on the key's final weight).
-constexpr float kHeavyShare = 1.0f / 32.0f;
+// of its row's running sum (an upper bound on the key's final weight).  A key
+// below it carries at most a sixteenth of the row's weight, so leaving its
+// bf16 rounding (relative 2^-9) uncorrected moves the output by at most
+// 2^-13 times the largest value entry.
+constexpr float kHeavyShare = 1.0f / 16.0f;
 // Reference-max slack of the online softmax, in log2 units.
 constexpr float kRescaleLog2 = 8.0f;
 
@@ -962,13 +968,16 @@ __device__ __forceinline__ void run_unit(Smem<T, DL, DR>& sm, const Args& a, con
   }
 }
 
-// The units of this workgroup's share of the work, handed to `run` one by one.
-// Called by all kThr threads of the workgroup; SM provides pref, wsum and req.
+// The units of the share of the work of workgroup `bl` (0 <= bl < G, or < 2G
+// for the aligned split), handed to `run` one by one.  Called by all kThr
+// threads of the workgroup; SM provides pref, wsum and req.  The workgroup
+// with `write_pref` stores the work prefix and split mode for the merge.
 template <int kThr, bool kSplit2, class SM, class Run>
 __device__ __forceinline__ void for_each_unit(SM& sm, const int32_t* __restrict__ prefix_len,
                                               const int32_t* __restrict__ n_nodes, int B, int Q,
                                               int H, int max_kv, int RT,
-                                              long long* __restrict__ ws_pref, int G, Run&& run) {
+                                              long long* __restrict__ ws_pref, int G,
+                                              long long bl, bool write_pref, Run&& run) {
   work_prefix<kThr>(sm.pref, sm.wsum, sm.req, prefix_len, n_nodes, B, Q, H, max_kv, RT);
   const long long Wtot = uni(sm.pref[B]);
   const long long Gn = G;
@@ -977,7 +986,7 @@ __device__ __forceinline__ void for_each_unit(SM& sm, const int32_t* __restrict_
   if constexpr (kSplit2) {
     // Launched with 2G workgroups for the aligned split (see workgroup_range);
     // the kernel decides from the clamped request sizes whether it applies.
-    second = blockIdx.x >= Gn;
+    second = bl >= Gn;
     const ReqInfo ri0 = req_info_ln(sm.req[0].x, sm.req[0].y, H, RT);
     int same = 1;
     for (int bb = threadIdx.x; bb < B; bb += kThr) {
@@ -987,11 +996,11 @@ __device__ __forceinline__ void for_each_unit(SM& sm, const int32_t* __restrict_
     same = __syncthreads_and(same);
     mode = split_mode(same != 0, ri0.vt, B, Gn);
   }
-  if (blockIdx.x == 0) {  // for the merge kernels: the work prefix and the split mode
+  if (write_pref) {  // for the merge kernels: the work prefix and the split mode
     for (int i = threadIdx.x; i <= B; i += kThr) ws_pref[i] = sm.pref[i];
     if (threadIdx.x == 0) ws_pref[B + 1] = mode;
   }
-  const long long gid = logical_gid(blockIdx.x - (second ? Gn : 0), Gn);
+  const long long gid = logical_gid(bl - (second ? Gn : 0), Gn);
   long long start, end;
   const ReqInfo ri0 = req_info_ln(sm.req[0].x, sm.req[0].y, H, RT);
   workgroup_range(mode, second, gid, Wtot, ri0.nkb, Gn, start, end);
@@ -1059,7 +1068,7 @@ __global__ __launch_bounds__(kThreads) void verify_attn_kernel(
   if ((threadIdx.x & 63) == 0) sm.xflag[threadIdx.x >> 6] = 0;
   int seq = 0;  // this wave's pair-sync sequence (see pair_post)
   for_each_unit<kThreads, kSplit2>(sm, prefix_len, n_nodes, B, Q, H, max_kv, RT, ws_pref, G,
-                                   [&](const Unit& u, long long) __attribute__((always_inline)) {
+                                   blockIdx.x, blockIdx.x == 0, [&](const Unit& u, long long) __attribute__((always_inline)) {
                                      if (half == 0) run_unit<T, DL, DR, 0>(sm, args, u, seq);
                                      else run_unit<T, DL, DR, 1>(sm, args, u, seq);
                                    });
@@ -1489,6 +1498,8 @@ __device__ __forceinline__ void run_unit_w(SmemW<DL, DR>& sm, const Args& a, con
       __syncthreads();
       issue_tile_w<DL, DR>(sm.stage[u.kb0 % kStages], sm.slot[u.kb0 % kRing], c_kv, k_pe, wave,
                            lane);
+      __builtin_amdgcn_s_waitcnt(0);  // the first tile is in LDS before its scores are read
+      __syncthreads();
     }
     step(u.kb0, std::true_type{});
     for (int kb = u.kb0 + 1; kb < u.kb1; ++kb) step(kb, std::false_type{});
@@ -1571,8 +1582,417 @@ void verify_attn_wide_kernel(
   const Args args{q_lat, q_pe, c_kv, k_pe, num_slots, req_to_slot, max_kv, vis, Q, H,
                   sm_scale * kLog2e, out, lse, ws_o, ws_lse, 0};
   for_each_unit<kThreadsW, kSplit2>(sm, prefix_len, n_nodes, B, Q, H, max_kv, RT, ws_pref, G,
-                                    [&](const Unit& u, long long) __attribute__((always_inline)) {
+                                    blockIdx.x, blockIdx.x == 0, [&](const Unit& u, long long) __attribute__((always_inline)) {
                                       run_unit_w<DL, DR>(sm, args, u);
+                                    });
+}
+
+// ----------------------------------------------------------------------------
+// Narrow form (bf16, 512 + 64, few row tiles): four workgroups share each work
+// range, one per 32-row quarter of its row tiles.  Inside a workgroup the four
+// waves (one per SIMD) split the contraction of QK^T, nine MFMA steps each, and
+// the output columns, 128 each.  The partial scores meet in LDS once per tile;
+// every wave sums them in the same order and runs the same softmax, then
+// multiplies by its own 128 value columns.  A workgroup holds a quarter of the
+// rows of the wide form, so a row tile can be cut into a quarter as many key
+// ranges for the same number of busy CUs; at small batches that is what
+// bounds the call: partial rows written, flushed at the kernel's end and read
+// again by the merge.
+constexpr int kStepsN = 9;  // QK^T MFMA steps per wave (36 / 4)
+constexpr int kNCBn = 4;    // 32-column output blocks per wave (16 / 4)
+
+template <int DL, int DR>
+struct SmemN {
+  using G = Geo<uint16_t, DL, DR>;
+  alignas(1024) unsigned char stage[kStages][G::kStageBytes];
+  float4 sx[2][kWavesW][4][kWave];  // partial scores of each wave, by tile parity
+  alignas(16) int32_t slot[kRing][kTileKeys];  // pool slot of each key of a tile (0 when invalid)
+  uint32_t valid[kRing];            // bit m: key m of the tile is in range with a valid slot
+  uint64_t visrow[32][2];           // visibility bitset of each row's tree node
+  long long pref[kMaxBatch + 1];
+  int2 req[kMaxBatch];  // per request: clamped prefix length, tree size
+  long long wsum[kWavesW];
+};
+
+template <int DL, int DR>
+__device__ __forceinline__ void run_unit_n(SmemN<DL, DR>& sm, const Args& a, const Unit& u,
+                                           int quarter) {
+  using G = Geo<uint16_t, DL, DR>;
+  using T = uint16_t;
+  constexpr int kLatSteps = DL / G::kKStep;  // QK^T steps over the latent part
+  static_assert(G::kSwz && DR == 64 && G::kNK == kWavesW * kStepsN &&
+                    G::kNCB == kWavesW * kNCBn && kLatSteps == 32,
+                "narrow form shape");
+  const int tid = threadIdx.x;
+  const int wave = uni(tid >> 6);
+  int lane = tid;
+  __asm__ __volatile__("" : "+v"(lane));
+  lane &= 63;
+  const int n = lane & 31;
+  const int g = lane >> 5;
+  const int W = (a.Q + 63) >> 6;
+  const long long QH = (long long)a.Q * a.H;
+  const T* q_lat = static_cast<const T*>(a.q_lat);
+  const T* q_pe = static_cast<const T*>(a.q_pe);
+  const T* c_kv = static_cast<const T*>(a.c_kv);
+  const T* k_pe = static_cast<const T*>(a.k_pe);
+  const int32_t* slots_b = a.req_to_slot + (long long)u.b * a.max_kv;
+
+  // Every wave holds the same 32 rows: row n of the quarter in lanes n, n + 32.
+  const int rloc = quarter * 32 + n;  // row within the tile
+  const long long r_loc = (long long)u.rt * kRowsPerWG + rloc;
+  int heads = a.H;
+  __asm__ __volatile__("" : "+s"(heads));
+  const int node = (int)(r_loc / heads);
+  const bool row_exists = r_loc < QH;
+  const bool row_live = row_exists && node < u.ri.nb;
+  const bool live = __ballot(row_live) != 0;  // the same in every wave
+
+  float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.0f;
+  f32x16_t o[kNCBn];
+#pragma unroll
+  for (int c = 0; c < kNCBn; ++c) o[c] = f32x16_t{};
+
+  if (live) {
+    auto start_tiles = [&]() __attribute__((always_inline)) {
+      int32_t raw0 = -1, raw1 = -1;
+      if (tid < kTileKeys) {
+        raw0 = fetch_slot(slots_b, u.kb0 * kTileKeys + tid, u.nkeys);
+        if (u.kb0 + 1 < u.kb1) raw1 = fetch_slot(slots_b, (u.kb0 + 1) * kTileKeys + tid, u.nkeys);
+        publish_slots(sm.slot[u.kb0 % kRing], &sm.valid[u.kb0 % kRing], raw0, a.num_slots, tid);
+        if (u.kb0 + 1 < u.kb1)
+          publish_slots(sm.slot[(u.kb0 + 1) % kRing], &sm.valid[(u.kb0 + 1) % kRing], raw1,
+                        a.num_slots, tid);
+      }
+    };
+    uint64_t vis0 = 0, vis1 = 0;
+    if (wave == 0 && g == 0 && row_live) {
+      const uint64_t* vr = a.vis + ((long long)u.b * a.Q + node) * W;
+      vis0 = vr[0];
+      if (W > 1) vis1 = vr[1];
+    }
+    start_tiles();
+    if (wave == 0 && g == 0) {
+      sm.visrow[n][0] = vis0;
+      sm.visrow[n][1] = vis1;
+    }
+    __syncthreads();
+    issue_tile_w<DL, DR>(sm.stage[u.kb0 % kStages], sm.slot[u.kb0 % kRing], c_kv, k_pe, wave,
+                         lane);
+
+    // This wave's query operands (steps 9w .. 9w+8: latent chunk 2s + g of
+    // the row for s < 32, rope chunk 2(s - 32) + g after), straight from
+    // global memory.
+    bf16x8_t q[kStepsN];
+    {
+      long long gr = (long long)u.b * QH + r_loc;
+      const long long rlast = (long long)u.b * QH + QH - 1;  // rows past it are unused
+      gr = gr < rlast ? gr : rlast;
+#pragma unroll
+      for (int k = 0; k < kStepsN; ++k) {
+        const int st = kStepsN * wave + k;
+        const T* src = st < kLatSteps ? q_lat + gr * DL + 16 * st + 8 * g
+                                      : q_pe + gr * DR + 16 * (st - kLatSteps) + 8 * g;
+        q[k] = row_live ? *reinterpret_cast<const bf16x8_t*>(src) : bf16x8_t{};
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // the first tile is in LDS
+    __syncthreads();
+
+    bool overflow = false;
+    float sv[16];
+    float p[16];
+    float4 gs[kWavesW][4];  // the four waves' partial scores of the previous tile
+    float mh0 = 0.0f, mh1 = 0.0f, mref = 0.0f, psum = 0.0f;
+    bf16x8_t p0 = bf16x8_t{}, p1 = bf16x8_t{};
+    bool h0 = false, h1 = false;
+
+    // Invisible keys of tile kb get -inf in sv (see the wide form's mask).
+    auto mask = [&](int kb, int lane_it) __attribute__((always_inline)) {
+      const int key0 = kb * kTileKeys;
+      const uint32_t valid = (uint32_t)uni((int)sm.valid[kb % kRing]);
+      const bool tree_tile = key0 + kTileKeys > u.ri.L;
+      if (tree_tile || valid != 0xFFFFFFFFu) {
+        const int nn = lane_it & 31;
+        const int gg = lane_it >> 5;
+        uint32_t okm = valid;
+        if (tree_tile) {
+          const uint64_t* vr = sm.visrow[nn];
+          okm &= tree_window(vr[0], vr[1], key0 - u.ri.L);
+        }
+        okm >>= 4 * gg;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          sv[i] = ((okm >> (8 * (i >> 2) + (i & 3))) & 1u) ? sv[i] : -INFINITY;
+      }
+    };
+
+    // The softmax of tile kb-1 in parts, placed between the score MFMAs of
+    // tile kb: the four partial scores added in wave order and masked, row
+    // maxima and the fixed reference (as in the wide form), probabilities,
+    // operands, row sum and the residual test.
+    auto part = [&](int j, int kbp, int lane_it) __attribute__((always_inline)) {
+      if (j == 0) {
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          float4 acc = gs[0][i4];
+#pragma unroll
+          for (int w = 1; w < kWavesW; ++w) {
+            acc.x += gs[w][i4].x;
+            acc.y += gs[w][i4].y;
+            acc.z += gs[w][i4].z;
+            acc.w += gs[w][i4].w;
+          }
+          sv[4 * i4] = acc.x;
+          sv[4 * i4 + 1] = acc.y;
+          sv[4 * i4 + 2] = acc.z;
+          sv[4 * i4 + 3] = acc.w;
+        }
+        mask(kbp, lane_it);
+      } else if (j == 1) {
+        mh0 = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                    fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+        mh1 = fmaxf(fmaxf(fmaxf(sv[8], sv[9]), fmaxf(sv[10], sv[11])),
+                    fmaxf(fmaxf(sv[12], sv[13]), fmaxf(sv[14], sv[15])));
+        mh0 = xor32_max(mh0);
+        mh1 = xor32_max(mh1);
+        const float mt = fmaxf(mh0, mh1) * a.sl2;  // row max over the tile, log2 units
+        m_seen = fmaxf(m_seen, mt);
+        if (m_ref == -INFINITY) m_ref = mt;
+        overflow = overflow || mt > m_ref + kOverflowLog2;
+        mref = m_ref == -INFINITY ? 0.0f : m_ref;
+      } else if (j < 6) {
+        const int k = 4 * (j - 2);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          p[k + t] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[k + t], a.sl2, -mref));
+      } else if (j == 6) {
+        p0 = pack_p<false>(p);
+        p1 = pack_p<false>(p + 8);
+      } else if (j == 7) {
+        psum = (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]))) +
+               (((p[8] + p[9]) + (p[10] + p[11])) + ((p[12] + p[13]) + (p[14] + p[15])));
+        l_run += psum;
+        const float lrow = xor32_sum(l_run);
+        const float pm0 = __builtin_amdgcn_exp2f(__builtin_fmaf(mh0, a.sl2, -mref));
+        const float pm1 = __builtin_amdgcn_exp2f(__builtin_fmaf(mh1, a.sl2, -mref));
+        h0 = __ballot(pm0 > kHeavyShare * lrow) != 0;
+        h1 = __ballot(pm1 > kHeavyShare * lrow) != 0;
+      }
+    };
+    constexpr int kParts = 8;
+
+    // The four waves' partial scores of tile kb (stored before the barrier
+    // that ended the step of tile kb), read into gs.
+    auto gather = [&](int kb, int lane_it) __attribute__((always_inline)) {
+#pragma unroll
+      for (int w = 0; w < kWavesW; ++w)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) gs[w][i4] = sm.sx[kb & 1][w][i4][lane_it];
+    };
+
+    // This wave's nine steps of S^T = K Q^T for tile kb, stored to LDS; with
+    // `soft`, the softmax of tile kb-1 runs between them.
+    auto do_qk = [&](int kb, int lane_it, auto kSoft) __attribute__((always_inline)) {
+      constexpr bool soft = decltype(kSoft)::value;
+      const int nn = lane_it & 31;
+      const int gg = lane_it >> 5;
+      const uint32_t kt = lds_addr(sm.stage[kb % kStages]);
+      const uint32_t qk_base = kt + nn * G::kLatPitchB + 16 * (gg ^ swz(nn));
+      const int xswz = gg ^ (nn & 7);
+      const uint32_t pe_base = kt + G::kLatBytes + nn * (DR * 2) + 16 * xswz;
+      auto kread = [&](int st) __attribute__((always_inline)) -> bf16x8_t {
+        if (st < kLatSteps)
+          return *(const DDT_LDS bf16x8_t*)(uintptr_t)((qk_base ^ ((st & 7) << 5)) +
+                                                       256 * (st >> 3));
+        return *(const DDT_LDS bf16x8_t*)(uintptr_t)(pe_base ^ (32 * (st - kLatSteps)));
+      };
+      bf16x8_t kop[kStepsN];
+#pragma unroll
+      for (int k = 0; k < kStepsN; ++k) kop[k] = kread(kStepsN * wave + k);
+      if constexpr (soft) gather(kb - 1, lane_it);
+      f32x16_t s;
+#pragma unroll
+      for (int k = 0; k < kStepsN; ++k) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (k == 0) mfma_qk<true, false>(s, kop[k], q[k]);
+        else if (k == kStepsN - 1) mfma_qk<false, true>(s, kop[k], q[k]);
+        else mfma_qk<false, false>(s, kop[k], q[k]);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (soft) {
+          if (k < kParts) part(k, kb - 1, lane_it);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      float4* dst = &sm.sx[kb & 1][wave][0][lane_it];
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+        dst[i4 * kWave] = make_float4(s[4 * i4], s[4 * i4 + 1], s[4 * i4 + 2], s[4 * i4 + 3]);
+    };
+
+    // O^T += V^T P^T of tile kb over this wave's 128 columns (blocks 4w..4w+3).
+    auto do_pv = [&](int kb, int lane_it) __attribute__((always_inline)) {
+      const VtAddr va(lds_addr(sm.stage[kb % kStages]), lane_it);
+      bf16x8_t vop[2 * kNCBn];
+#pragma unroll
+      for (int i = 0; i < 2 * kNCBn; ++i) vop[i] = va.read(kNCBn * wave + i % kNCBn, i / kNCBn);
+#pragma unroll
+      for (int i = 0; i < 2 * kNCBn; ++i)
+        o[i % kNCBn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[i], (i / kNCBn) ? p1 : p0,
+                                                               o[i % kNCBn], 0, 0, 0);
+      if (h0) {
+        const bf16x8_t r = pack_p<true>(p);
+#pragma unroll
+        for (int c = 0; c < kNCBn; ++c)
+          o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va.read(kNCBn * wave + c, 0), r, o[c],
+                                                         0, 0, 0);
+      }
+      if (h1) {
+        const bf16x8_t r = pack_p<true>(p + 8);
+#pragma unroll
+        for (int c = 0; c < kNCBn; ++c)
+          o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va.read(kNCBn * wave + c, 1), r, o[c],
+                                                         0, 0, 0);
+      }
+    };
+
+    // Step kb: tile kb+1 starts loading; this wave's share of tile kb's
+    // scores, with tile kb-1's softmax between the MFMAs; tile kb-1's value
+    // product; one barrier (tile kb+1 landed, tile kb's partial scores stored).
+    auto step = [&](int kb, auto kFirst) __attribute__((always_inline)) {
+      constexpr bool first = decltype(kFirst)::value;
+      int lane_it = lane;
+      __asm__ __volatile__("" : "+v"(lane_it));
+      int32_t ahead = -1;
+      if (tid < kTileKeys && kb + 2 < u.kb1)
+        ahead = fetch_slot(slots_b, (kb + 2) * kTileKeys + tid, u.nkeys);
+      // Tile kb+1 goes to the stage tile kb-2 used, whose value product ran
+      // before the previous step's barrier.
+      if (kb + 1 < u.kb1)
+        issue_tile_w<DL, DR>(sm.stage[(kb + 1) % kStages], sm.slot[(kb + 1) % kRing], c_kv,
+                             k_pe, wave, lane_it);
+      if constexpr (first) {
+        do_qk(kb, lane_it, std::false_type{});
+      } else {
+        do_qk(kb, lane_it, std::true_type{});
+        do_pv(kb - 1, lane_it);
+      }
+      __builtin_amdgcn_s_waitcnt(0);  // tile kb+1 in LDS; partial scores stored
+      if (tid < kTileKeys && kb + 2 < u.kb1)
+        publish_slots(sm.slot[(kb + 2) % kRing], &sm.valid[(kb + 2) % kRing], ahead,
+                      a.num_slots, tid);
+      __syncthreads();
+    };
+
+    for (int attempt = 0;; ++attempt) {
+      if (attempt > 0) {
+        // The rerun: references at each row's largest score, which no tile of
+        // the range exceeds.
+#pragma unroll
+        for (int c = 0; c < kNCBn; ++c) o[c] = f32x16_t{};
+        l_run = 0.0f;
+        m_ref = m_seen;
+        start_tiles();
+        __syncthreads();
+        issue_tile_w<DL, DR>(sm.stage[u.kb0 % kStages], sm.slot[u.kb0 % kRing], c_kv, k_pe,
+                             wave, lane);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
+      step(u.kb0, std::true_type{});
+      for (int kb = u.kb0 + 1; kb < u.kb1; ++kb) step(kb, std::false_type{});
+      // Drain: the last tile's softmax and value product.
+      {
+        int lane_it = lane;
+        __asm__ __volatile__("" : "+v"(lane_it));
+        gather(u.kb1 - 1, lane_it);
+#pragma unroll
+        for (int j = 0; j < kParts; ++j) part(j, u.kb1 - 1, lane_it);
+        do_pv(u.kb1 - 1, lane_it);
+      }
+      // Every wave's last value product has read the key stages before the
+      // epilogue (or a rerun) writes them.
+      if (!__syncthreads_or(attempt == 0 && overflow)) break;
+      overflow = false;
+    }
+  }
+
+  // Row sum over the two lanes of the row (the same in every wave).
+  const float l = xor32_sum(l_run);
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  const float lse_v = l > 0.0f ? (m_ref + log2f(l)) * kLn2 : -INFINITY;
+  float* dst_lse = nullptr;
+  if (u.complete) {
+    if (row_exists && a.lse) dst_lse = a.lse + (long long)u.b * QH + r_loc;
+  } else if (row_live) {
+    dst_lse = a.ws_lse + u.slot * kRowsPerWG + rloc;
+  }
+  // This wave's 128 columns of the 32 rows go out through LDS (the key stages
+  // are free now) in two passes of 64 columns; every store instruction writes
+  // four 256-byte row segments.
+  constexpr int kPCb = 2, kPCols = 32 * kPCb, kPitch = kPCols + 4;  // floats
+  static_assert(kWavesW * 32 * kPitch * 4 <= kStages * G::kStageBytes, "epilogue staging");
+  float* buf = reinterpret_cast<float*>(sm.stage[0]) + wave * (32 * kPitch);
+  const uint32_t live_m = (uint32_t)__ballot(row_live);  // bit r: row r of the quarter
+  const uint32_t exist_m = (uint32_t)__ballot(row_exists);
+  const uint32_t write_m = u.complete ? exist_m : live_m;
+  float* base = u.complete
+                    ? a.out + ((long long)u.b * QH + (long long)u.rt * kRowsPerWG + quarter * 32) * DL
+                    : a.ws_o + ((long long)u.slot * kRowsPerWG + quarter * 32) * DL;
+  base += 32 * kNCBn * wave;
+  const int c4 = lane & 15;
+#pragma unroll
+  for (int pass = 0; pass < kNCBn / kPCb; ++pass) {
+#pragma unroll
+    for (int c = 0; c < kPCb; ++c) {
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4) {
+        const int cb = pass * kPCb + c;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (row_live)
+          v = make_float4(o[cb][4 * t4] * inv, o[cb][4 * t4 + 1] * inv, o[cb][4 * t4 + 2] * inv,
+                          o[cb][4 * t4 + 3] * inv);
+        *reinterpret_cast<float4*>(buf + n * kPitch + c * 32 + 8 * t4 + 4 * g) = v;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's parked rows are in LDS
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 4 * i + (lane >> 4);
+      const float4 v = *reinterpret_cast<const float4*>(buf + r * kPitch + 4 * c4);
+      float* d = base + (long long)r * DL + pass * kPCols + 4 * c4;
+      if ((write_m >> r) & 1u) *reinterpret_cast<float4*>(d) = v;
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next pass overwrites
+  }
+  if (dst_lse && g == 0 && wave == 0) *dst_lse = row_live ? lse_v : -INFINITY;
+  // Each wave parks its rows in its own part of stage 0, and the next unit
+  // writes the stages only after the barrier of its prologue.
+}
+
+// Workgroups are placed by narrow_place (the four quarters of a range on one
+// XCD); ranges past the grid (padding to whole groups of 8) have nothing to do.
+template <int DL, int DR, bool kSplit2>
+__global__ __launch_bounds__(kThreadsW, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void verify_attn_narrow_kernel(
+    const uint16_t* __restrict__ q_lat, const uint16_t* __restrict__ q_pe,
+    const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ k_pe, int64_t num_slots,
+    const int32_t* __restrict__ req_to_slot, int max_kv, const int32_t* __restrict__ prefix_len,
+    const int32_t* __restrict__ n_nodes, const uint64_t* __restrict__ vis, int B, int Q, int H,
+    int RT, float sm_scale, float* __restrict__ out, float* __restrict__ lse,
+    float* __restrict__ ws_o, float* __restrict__ ws_lse, long long* __restrict__ ws_pref,
+    int G) {
+  __shared__ SmemN<DL, DR> sm;
+  long long bl;
+  int quarter;
+  narrow_place(blockIdx.x, bl, quarter);
+  if (bl >= (kSplit2 ? 2LL : 1LL) * G) return;
+  const Args args{q_lat, q_pe, c_kv, k_pe, num_slots, req_to_slot, max_kv, vis, Q, H,
+                  sm_scale * kLog2e, out, lse, ws_o, ws_lse, 0};
+  for_each_unit<kThreadsW, kSplit2>(sm, prefix_len, n_nodes, B, Q, H, max_kv, RT, ws_pref, G,
+                                    bl, bl == 0 && quarter == 0,
+                                    [&](const Unit& u, long long) __attribute__((always_inline)) {
+                                      run_unit_n<DL, DR>(sm, args, u, quarter);
                                     });
 }
 
@@ -1950,6 +2370,18 @@ hipError_t launch_impl(const void* q_lat, const void* q_pe, const void* c_kv, co
   const bool split2 = (long long)B * plan.row_tiles >= plan.grid;
   if (!(phases & kPhaseAttention)) {
   } else if constexpr (Geo<T, DL, DR>::kBF16 && DL == 512 && DR == 64) {
+    if (plan.narrow) {
+      // Four workgroups per range, the ranges padded to whole groups of 8
+      // (one per XCD).
+      const long long blocks = narrow_blocks(split2 ? 2LL * plan.grid : (long long)plan.grid);
+      auto kernel = split2 ? verify_attn_narrow_kernel<DL, DR, true>
+                           : verify_attn_narrow_kernel<DL, DR, false>;
+      hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreadsW), 0, stream,
+                         static_cast<const T*>(q_lat), static_cast<const T*>(q_pe),
+                         static_cast<const T*>(c_kv), static_cast<const T*>(k_pe), num_slots,
+                         req_to_slot, max_kv, prefix_len, n_nodes, vis, B, Q, H, plan.row_tiles,
+                         sm_scale, out, lse, ws_o, ws_lse, ws_pref, plan.grid);
+    } else {
     auto kernel = split2 ? verify_attn_wide_kernel<DL, DR, true>
                          : verify_attn_wide_kernel<DL, DR, false>;
     hipLaunchKernelGGL(kernel, dim3(split2 ? 2 * plan.grid : plan.grid), dim3(kThreadsW), 0,
@@ -1957,6 +2389,7 @@ hipError_t launch_impl(const void* q_lat, const void* q_pe, const void* c_kv, co
                        static_cast<const T*>(c_kv), static_cast<const T*>(k_pe), num_slots,
                        req_to_slot, max_kv, prefix_len, n_nodes, vis, B, Q, H, plan.row_tiles,
                        sm_scale, out, lse, ws_o, ws_lse, ws_pref, plan.grid);
+    }
   } else {
     auto kernel =
         split2 ? verify_attn_kernel<T, DL, DR, true> : verify_attn_kernel<T, DL, DR, false>;
