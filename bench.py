@@ -402,6 +402,39 @@ class StepRunner:
         return t_step, t_call, t_kern, t_merge, roof
 
 
+CEILING_MODES = {0: "MFMA only (16 accumulators, operands in registers)",
+                 1: "attention tile operand traffic (LDS reads, one barrier per tile)",
+                 2: "attention tile operand traffic + next tile's global->LDS loads"}
+
+
+def run_ceiling(iters=4000):
+    """What one CU's four waves sustain on v_mfma_f32_32x32x16_bf16 alone and with
+    the attention tile's operand traffic, on random and on zero operand values
+    (libddt_ceiling.so, csrc/ceiling.hip); prints one JSON line."""
+    import ctypes
+    from tree_verify_mla_ddt_amd import build as libbuild
+    if not os.path.exists(libbuild.CEILING_PATH):
+        raise SystemExit("libddt_ceiling.so not built (run __graft_entry__.build())")
+    lib = ctypes.CDLL(libbuild.CEILING_PATH)
+    lib.ddt_ceiling_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+    lib.ddt_ceiling_run.restype = ctypes.c_int
+    res = {}
+    for random in (1, 0):
+        for mode, label in CEILING_MODES.items():
+            tf, cyc = ctypes.c_double(), ctypes.c_double()
+            n = iters if mode == 0 else iters // 2
+            rc = lib.ddt_ceiling_run(mode, n, random, ctypes.byref(tf), ctypes.byref(cyc))
+            if rc != 0:
+                raise SystemExit(f"ddt_ceiling_run failed ({rc})")
+            key = f"mode{mode}_{'random' if random else 'zero'}"
+            res[key] = {"what": label, "tflops": round(tf.value, 1),
+                        "frac_of_2500": round(tf.value / PEAK_BF16_TFLOPS, 4),
+                        "cycles_per_mfma": round(cyc.value, 2)}
+            log(f"[ceiling] {key}: {tf.value:.0f} TFLOP/s, {cyc.value:.1f} cycles per MFMA ({label})")
+    print(json.dumps({"ceiling": res}), flush=True)
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -528,12 +561,17 @@ def main():
                     help="also run a plain 256 MiB device copy (reference for byte counters)")
     ap.add_argument("--workload", default=PRIMARY,
                     help="headline workload (default: the batch-1 configuration)")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="run the MFMA / attention-tile ceiling microbenchmark and exit")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="record the workload's HBM bytes per attention call from two "
                          "rocprofv3 --pmc output directories (FETCH_SIZE, WRITE_SIZE) and exit")
     args = ap.parse_args()
     if args.traffic_from:
         write_traffic(args.workload, *args.traffic_from)
+        return
+    if args.ceiling:
+        run_ceiling()
         return
     if args.gpus != 1:
         print(f"bench.py: the verify step runs on one GPU; --gpus {args.gpus} is not "

@@ -13,6 +13,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "libddt.so")
 # Host-side checker of the attention work split (CPU tests only).
 CHECK_PATH = os.path.join(HERE, "libddt_split_check.so")
+# Measured ceilings of the attention tile (bench.py --ceiling).
+CEILING_PATH = os.path.join(HERE, "libddt_ceiling.so")
 SOURCES = ["api.hip", "draft_topk.hip", "tree_build.hip", "tree_accept.hip",
            "tree_accept_sampling.hip", "kv_commit.hip", "verify_attn.hip", "noalloc.hip"]
 ARCH = os.environ.get("DDT_OFFLOAD_ARCH", "gfx950")
@@ -43,6 +45,19 @@ def build_split_check() -> str:
     return CHECK_PATH
 
 
+def build_ceiling() -> str:
+    """The ceiling microbenchmark (csrc/ceiling.hip) as its own library."""
+    tmp = CEILING_PATH + ".tmp"
+    cmd = ["hipcc", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           os.path.join(CSRC, "ceiling.hip"), "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}{res.stderr}")
+    os.replace(tmp, CEILING_PATH)
+    return CEILING_PATH
+
+
 def build(verbose: bool = False, resource_report: bool = False) -> str:
     tmp = LIB_PATH + ".tmp"
     res = subprocess.run(hipcc_command(tmp, resource_report), capture_output=True, text=True)
@@ -54,6 +69,7 @@ def build(verbose: bool = False, resource_report: bool = False) -> str:
         print(log)
     os.replace(tmp, LIB_PATH)
     build_split_check()
+    build_ceiling()
     return LIB_PATH
 
 

@@ -90,6 +90,8 @@ __global__ __launch_bounds__(kWave) void tree_build_kernel(
   const int lane = threadIdx.x;
   const int DK = D * K;
   const size_t in0 = (size_t)b * DK;
+  // Loaded first so that its latency overlaps the build (positions use it).
+  const int32_t L = prefix_len[b];
   for (int t = lane; t < DK; t += kWave) {
     s_logp[t] = topk_logp[in0 + t];
     s_ids[t] = topk_ids[in0 + t];
@@ -233,7 +235,6 @@ __global__ __launch_bounds__(kWave) void tree_build_kernel(
   __syncthreads();
 
   const int W = (Q + 63) >> 6;
-  const int32_t L = prefix_len[b];
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int i = lane + k * kWave;
