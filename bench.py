@@ -82,8 +82,8 @@ def source_digest():
 
 
 COPY_BYTES = 256 << 20  # the --copy-calibration copy
-ATTN_KERNELS = ("verify_attn_kernel", "verify_attn_wide_kernel", "verify_merge_kernel",
-                "verify_merge_wide_kernel")
+ATTN_KERNELS = ("verify_attn_kernel", "verify_attn_wide_kernel", "verify_attn_narrow_kernel",
+                "verify_merge_kernel", "verify_merge_wide_kernel")
 
 
 def _counter_rows(directory):
@@ -111,7 +111,8 @@ def _per_launch_kib(rows, counter):
                 per_kernel.setdefault(k, []).append(v)
         if "copyBuffer" in name and int(r["Grid_Size"]) * 2048 == COPY_BYTES:
             copy.append(v)  # the calibration copy moves 2 KiB per work-item
-    if not ({"verify_attn_kernel", "verify_attn_wide_kernel"} & set(per_kernel)) or not copy:
+    if not ({"verify_attn_kernel", "verify_attn_wide_kernel", "verify_attn_narrow_kernel"}
+            & set(per_kernel)) or not copy:
         raise SystemExit(f"{counter}: attention kernel or calibration copy missing")
     att = sum(sum(v) / len(v) for v in per_kernel.values())
     return att, sum(copy) / len(copy)
@@ -378,8 +379,7 @@ class StepRunner:
         return {"bound": "mfma" if mfma else "hbm", "achieved": round(ach, 3), "peak": peak,
                 "unit": unit, "frac": round(ach / peak, 4),
                 "traffic": measured_traffic(name),
-                "kernel": ("verify_attn_wide_kernel" if wl.dtype == "bf16" and wl.d_lat == 512
-                           else "verify_attn_kernel"),
+                "kernel": self.attn_kernel_name(),
                 "kernel_us": round(kernel_ms * 1e3, 3), "merge_kernel_us": round(merge_ms * 1e3, 3),
                 "call_us": round(call_ms * 1e3, 3), "call_achieved": round(call_ach, 3),
                 "call_frac": round(call_ach / peak, 4),
@@ -388,6 +388,18 @@ class StepRunner:
                 "kernel_mfma_frac": round(tf(kernel_ms) / peak_f, 4),
                 "kernel_hbm_gbs": round(gb(kernel_ms), 1),
                 "kernel_hbm_frac": round(gb(kernel_ms) / PEAK_HBM_GBS, 4)}
+
+    def attn_kernel_name(self):
+        """The attention kernel the library launches for this workload: the
+        512-wide bf16 form runs four 32-row workgroups per range (narrow) when
+        its row tiles number at most a sixteenth of the CUs, else 128-row ones
+        (wide); the 64-wide forms run the paired-wave kernel."""
+        wl = self.wl
+        if not (wl.dtype == "bf16" and wl.d_lat == 512):
+            return "verify_attn_kernel"
+        units = wl.B * ((wl.Q * wl.H + 127) // 128)
+        cus = self.torch.cuda.get_device_properties(0).multi_processor_count
+        return "verify_attn_narrow_kernel" if units * 16 <= cus else "verify_attn_wide_kernel"
 
     def measure(self, steps, warmup, kernel_reps=MIN_REPLAYS):
         """Step and attention-call graph replays plus kernel times; returns the
