@@ -135,3 +135,45 @@ def test_commit_twice_in_a_row():
     np.testing.assert_array_equal(d_plen.cpu().numpy(), o2["prefix_len"])
     np.testing.assert_array_equal(g2["freed_slots"].cpu().numpy(), o2["freed_slots"])
     np.testing.assert_array_equal(g2["n_freed"].cpu().numpy(), o2["n_freed"])
+
+
+@pytest.mark.parametrize("slack", [-3, 0, 1, 5])
+def test_step_at_slot_table_capacity(slack):
+    """A verify step whose longest tree ends exactly at the slot table's capacity
+    (slack 0: L_b + n_b = max_kv), short of it, or past it (slack -3, against the
+    stated precondition): attention against the oracle, accept bit-exact, and the
+    commit bit-exact.  Attention and commit clamp an overrunning tree to
+    max_kv - L_b alike; accept does not see max_kv, and the commit cuts the path
+    at the clamp.  Requests that fit commit their whole accepted path."""
+    note(f"capacity edge slack={slack}")
+    wl = workloads.make_workload("b4_l4k_q33", L=700)
+    t = oracle.tree_build(wl.topk_logp, wl.topk_ids, wl.root_token, wl.prefix_len, wl.budget)
+    need = wl.prefix_len.astype(np.int64) + t["n_nodes"]
+    max_kv = int(need.max()) + slack
+    r2s = np.ascontiguousarray(wl.req_to_slot[:, :max_kv])
+    tgt = workloads.synth_target_argmax(wl, t["node_token"], t["parent"], t["depth"],
+                                        t["n_nodes"])
+    # attention on the clamped table
+    f = lambda x: x.float().numpy()
+    o_out, o_lse = oracle.verify_attn(f(wl.q_lat), f(wl.q_pe), f(wl.c_kv), f(wl.k_pe), r2s,
+                                      wl.prefix_len, t["n_nodes"], t["vis"], wl.sm_scale)
+    tdev = lambda x: x.contiguous().cuda()
+    g_out, g_lse = ddt.verify_attn(tdev(wl.q_lat), tdev(wl.q_pe), tdev(wl.c_kv), tdev(wl.k_pe),
+                                   dev(r2s), dev(wl.prefix_len), dev(t["n_nodes"]),
+                                   dev(t["vis"].view(np.int64)), wl.sm_scale)
+    torch.cuda.synchronize()
+    err = float(np.abs(g_out.cpu().numpy().astype(np.float64) - o_out).max())
+    assert err <= 2e-3, err
+    # accept, then commit into the table
+    oa = oracle.tree_accept(t["node_token"], t["parent"], t["n_nodes"], tgt)
+    acc = ddt.tree_accept(dev(t["node_token"]), dev(t["parent"]), dev(t["n_nodes"]), dev(tgt))
+    torch.cuda.synchronize()
+    for k in oa:
+        np.testing.assert_array_equal(acc[k].cpu().numpy(), oa[k], err_msg=k)
+    oc = oracle.kv_commit(r2s, wl.prefix_len, t["n_nodes"], oa["accept_len"], oa["accept_nodes"])
+    gc = gpu_commit(r2s, wl.prefix_len, t["n_nodes"], oa["accept_len"], oa["accept_nodes"])
+    assert_same(gc, oc)
+    assert (oc["prefix_len"] <= max_kv).all()
+    fits = need <= max_kv
+    assert fits.any() and (slack < 0) == (not fits.all())
+    np.testing.assert_array_equal(oc["prefix_len"][fits], (wl.prefix_len + oa["accept_len"])[fits])
