@@ -381,8 +381,10 @@ def test_verify_attn_determinism():
     np.testing.assert_array_equal(l1.view(np.uint32), l2.view(np.uint32))
 
 
-@pytest.mark.parametrize("name,overrides", [("b4_l4k_q17", {"L": 900}),
-                                            ("b64_l2k_q9", {"L": 300})])
+@pytest.mark.parametrize("name,overrides", [("b1_l2k_q9", {"L": 600}),
+                                            ("b4_l4k_q17", {"L": 900}),
+                                            ("b64_l2k_q9", {"L": 300}),
+                                            ("tiny_fp32", {})])
 def test_verify_attn_kernel_times_matches_call(name, overrides):
     """The kernel-time measurement leaves the call's exact result in out / lse
     and reports positive per-launch times."""
