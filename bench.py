@@ -256,6 +256,12 @@ class StepRunner:
     def time_graph(self, g, n, warmup, repeats=REPEATS):
         return self._time(g.replay, n, warmup, repeats)
 
+    def steps_in_one_graph(self, copies, n=MIN_REPLAYS):
+        """Per-step time of graph replays that hold `copies` consecutive steps."""
+        g = self.capture(lambda: [self.step() for _ in range(copies)])
+        t = self.time_graph(g, n, 5)
+        return Timing([x / copies for x in t.per], n * copies)
+
     def time_eager(self, fn, n, warmup, repeats=REPEATS):
         return self._time(fn, n, warmup, repeats)
 
@@ -637,6 +643,10 @@ def main():
         "attn_kernel_us": t_kern.summary(),
         "merge_kernel_us": t_merge.summary(),
         "step_eager_us": t_eager.summary(),
+        # The same step four times in one graph: the replay period per step
+        # without the per-launch cost of a graph (what a step embedded in a
+        # larger captured loop would take).
+        "step_x4_graph_us": runner.steps_in_one_graph(4).summary(),
         "kv_commit_step_ms": round(runner.commit_ms(), 5),
         "draft_topk": runner.topk_stats(),
         "accept_sampling": runner.sampling_stats(),
