@@ -141,8 +141,9 @@ def test_verify_attn_noalloc_rejects(lib, kw, code, needle):
 
 def test_noalloc_scratch_size(lib):
     # two partial 128-row tiles of 513 floats for each of 256 workgroups, and the
-    # work prefix of 512 requests
-    assert lib.ddt_verify_attn_noalloc_max_bytes() == 2 * 256 * 128 * 513 * 4 + 514 * 8
+    # stream prefix of 512 requests, the split mode and the start cost (rounded up
+    # to 16 bytes)
+    assert lib.ddt_verify_attn_noalloc_max_bytes() == 2 * 256 * 128 * 513 * 4 + 516 * 8
 
 
 def test_workspace_size_query(lib):

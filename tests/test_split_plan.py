@@ -24,23 +24,28 @@ def checker():
         libbuild.build_split_check()
     lib = ctypes.CDLL(libbuild.CHECK_PATH)
     lib.ddt_split_check.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p] * 2 + \
-        [ctypes.c_int] * 3 + [ctypes.c_char_p, ctypes.c_int]
+        [ctypes.c_int] * 3 + [ctypes.c_char_p, ctypes.c_int, ctypes.c_void_p]
     lib.ddt_split_check.restype = ctypes.c_int
     return lib
 
 
-def run(lib, plen, nn, Q, H, max_kv, num_cu=256, d_lat=512, plant=0):
+def run(lib, plen, nn, Q, H, max_kv, num_cu=256, d_lat=512, plant=0, stats=None):
     plen = np.ascontiguousarray(plen, np.int32)
     nn = np.ascontiguousarray(nn, np.int32)
     msg = ctypes.create_string_buffer(256)
+    st = np.zeros(5, np.int64)
     rc = lib.ddt_split_check(len(plen), Q, H, max_kv, plen.ctypes.data, nn.ctypes.data, num_cu,
-                             d_lat, plant, msg, 256)
+                             d_lat, plant, msg, 256, st.ctypes.data)
+    if stats is not None:
+        stats[:] = st
     return rc, msg.value.decode()
 
 
 def check(lib, plen, nn, Q, H, max_kv, num_cu=256, d_lat=512):
-    rc, msg = run(lib, plen, nn, Q, H, max_kv, num_cu, d_lat)
+    st = np.zeros(5, np.int64)
+    rc, msg = run(lib, plen, nn, Q, H, max_kv, num_cu, d_lat, stats=st)
     assert rc == 0, (msg, len(plen), Q, H, max_kv, num_cu)
+    return st
 
 
 @pytest.mark.parametrize("name", list(workloads.CONFIGS))
@@ -55,6 +60,7 @@ def test_benchmark_shapes(checker, name):
 
 def test_random_shapes(checker):
     rng = np.random.default_rng(123)
+    seen = np.zeros(3, np.int64)  # start cost charged, ranges ending inside one, ranges over 2+ tiles
     for case in range(1500):
         B = int(rng.choice([1, 2, 3, 4, 7, 8, 16, 33, 64, 100, 512]))
         Q = int(rng.choice([1, 2, 9, 17, 33, 65, 100, 128]))
@@ -75,7 +81,25 @@ def test_random_shapes(checker):
             nn = rng.integers(0, Q + 1, size=B)
         max_kv = max(1, Lmax + Q - int(rng.integers(0, 3)))
         cu = int(rng.choice([256, 256, 304, 120, 64, 1024]))
-        check(checker, plen, nn, Q, H, max_kv, cu, int(rng.choice([64, 512])))
+        st = check(checker, plen, nn, Q, H, max_kv, cu, int(rng.choice([64, 512])))
+        seen += [st[0] > 0, st[1], st[2]]
+    assert (seen > 0).all(), seen
+
+
+def test_start_cost_balances_ranges(checker):
+    """Ragged batch-4 requests (4096 +-25% keys, 17 tree nodes, 64 heads): the
+    ranges cross row tiles, so starting one is charged; no range then carries
+    more than its share of the stream plus one start cost, counting a start
+    cost for every row tile it begins; with requests of equal length cut into
+    whole multiples of the row-tile count nothing is charged."""
+    rng = np.random.default_rng(7)
+    for _ in range(20):
+        plen = rng.integers(3072, 5121, size=4)
+        st = check(checker, plen, [17] * 4, 17, 64, int(plen.max()) + 17)
+        assert st[0] == 4 and st[2] > 0
+        assert st[3] <= st[4] + st[0], st
+    st = check(checker, [2048], [9], 9, 64, 2057)
+    assert st[0] == 0 and st[2] == 0
 
 
 @pytest.mark.parametrize("plant", [1, 2])
@@ -113,6 +137,6 @@ def test_narrow_form_choice(checker, B, Q, H, L, narrow):
     assert nar == narrow
     assert 1 <= g <= (64 if nar else 256)
     assert (not nar) or B * rt * 16 <= 256
-    assert ws == 2 * g * 128 * 513 * 4 + (B + 2) * 8
+    assert ws == 2 * g * 128 * 513 * 4 + (B + 3) * 8
     # the 64-wide latent form never takes it
     assert not plan(checker, B, Q, H, L + Q, d_lat=64)[1]

@@ -4,7 +4,14 @@
 // The attention kernels cut the (request, 128-row tile, 32-key tile) work into
 // contiguous ranges, one per workgroup; row tiles whose key range is cut are
 // written as partial results to workspace slots and combined by the merge
-// kernels.  Everything that decides which workgroup takes which tiles, which
+// kernels.
+//
+// The work is one stream of positions.  Each row tile with work occupies a
+// segment of nkb + c positions: c positions that stand for the cost of
+// starting the tile in a workgroup (query load, pipeline fill, partial output;
+// a few key tiles' worth), then its nkb key tiles.  Ranges are equal cuts of
+// the stream, so a range that crosses into a second row tile takes that many
+// fewer key tiles.  c is 0 when every range lies inside one row tile anyway.  Everything that decides which workgroup takes which tiles, which
 // slot a partial result lands in and which slots the merge reads is here, so
 // that a host program (the split checker) runs exactly the code the kernels
 // run.
@@ -21,6 +28,7 @@ constexpr int kRowsPerWG = 128;   // rows per tile
 constexpr int kMaxBatch = 512;    // requests the attention kernels take
 constexpr int kXcds = 8;          // XCDs the workgroups are dealt to
 constexpr int kMaxGrid = 1024;    // upper bound of the attention grid
+constexpr int kUnitCost = 4;      // stream positions charged for starting a row tile
 
 #define DDT_HD __host__ __device__ __forceinline__
 
@@ -82,13 +90,27 @@ DDT_HD long long split_mode(bool same, int vt0, int B, long long G) {
   return (same && vt0 > 0 && U >= G) ? U : -1;
 }
 
+// Start cost c of a row tile in the stream (see the top of this file): 0 when
+// the ranges never cross a row tile, that is when every row tile has the same
+// key-tile count (`same`) and the number of row tiles in the cut stream
+// divides G; else kUnitCost.  Under the aligned split (mode >= 0) only the
+// leftover units r = mode mod G form a cut stream.
+DDT_HD int unit_cost(long long mode, bool same, long long units, long long G) {
+  if (mode >= 0) {
+    const long long r = mode % G;
+    return (r == 0 || G % r == 0) ? 0 : kUnitCost;
+  }
+  return (same && units > 0 && G % units == 0) ? 0 : kUnitCost;
+}
+
 // Range [start, end) of the stream taken by the workgroup with logical id gid
 // in the first (second = false) or second half of an aligned-split launch.
-// Under the aligned split unit u covers tiles [u*nkb, (u+1)*nkb): the first G
-// workgroups take q = U / G whole units each, the second G the r = U - q*G
-// leftover units as one stream cut into G ranges.  Otherwise the whole work
-// Wtot is cut into G ranges (first half only).
-DDT_HD void workgroup_range(long long mode, bool second, long long gid, long long Wtot, int nkb0,
+// Under the aligned split every unit is a segment of seg = nkb + c positions,
+// unit u covering [u*seg, (u+1)*seg): the first G workgroups take q = U / G
+// whole units each, the second G the r = U - q*G leftover units as one stream
+// cut into G ranges.  Otherwise the whole stream Wtot is cut into G ranges
+// (first half only).
+DDT_HD void workgroup_range(long long mode, bool second, long long gid, long long Wtot, int seg,
                             long long G, long long& start, long long& end) {
   if (mode < 0) {
     start = range_start(gid, Wtot, G);
@@ -96,33 +118,42 @@ DDT_HD void workgroup_range(long long mode, bool second, long long gid, long lon
     if (second) end = start;
     return;
   }
-  const long long nkb = nkb0, q = mode / G, r = mode - q * G;
+  const long long q = mode / G, r = mode - q * G;
   if (!second) {
-    start = gid * q * nkb;
-    end = start + q * nkb;
+    start = gid * q * seg;
+    end = start + q * seg;
   } else {
-    start = q * G * nkb + range_start(gid, r * nkb, G);
-    end = q * G * nkb + range_start(gid + 1, r * nkb, G);
+    start = q * G * seg + range_start(gid, r * seg, G);
+    end = q * G * seg + range_start(gid + 1, r * seg, G);
   }
 }
 
-// For a row tile with work, its place in the stream that holds it: S (first
-// key tile) and W (stream length); false for a whole unit of the aligned
-// split (written directly).  pref: exclusive work prefix over requests, with
-// pref[B] the total.
+// For a row tile with work, its place in the stream that holds it: S (start of
+// its segment) and W (stream length); false for a whole unit of the aligned
+// split (written directly).  pref: exclusive stream prefix over requests, with
+// pref[B] the total; c: the start cost.
 DDT_HD bool stream_place(long long mode, const long long* pref, int B, int b, int rt,
-                         const ReqInfo& ri, long long G, long long& S, long long& W) {
+                         const ReqInfo& ri, long long G, int c, long long& S, long long& W) {
+  const long long seg = (long long)ri.nkb + c;
   if (mode >= 0) {
     const long long q = mode / G, r = mode - q * G;
     const long long u = (long long)b * ri.vt + rt;
     if (u < q * G) return false;
-    S = (u - q * G) * ri.nkb;
-    W = r * ri.nkb;
+    S = (u - q * G) * seg;
+    W = r * seg;
     return true;
   }
-  S = pref[b] + (long long)rt * ri.nkb;
+  S = pref[b] + (long long)rt * seg;
   W = pref[B];
   return true;
+}
+
+// The ranges that hold a key tile of the row tile whose segment starts at S:
+// g_first .. g_last (equal when one range holds them all).
+DDT_HD void tile_owners(long long S, long long W, long long G, int nkb, int c, long long& g_first,
+                        long long& g_last) {
+  g_first = range_owner(S + c, W, G);
+  g_last = range_owner(S + c + nkb - 1, W, G);
 }
 
 // Workspace slot a workgroup writes a partial result of a cut row tile to:
@@ -131,8 +162,9 @@ DDT_HD bool stream_place(long long mode, const long long* pref, int B, int b, in
 DDT_HD long long partial_slot(long long gid, bool head) { return 2 * gid + (head ? 0 : 1); }
 
 // The merge's rule: contributor gg (g_first <= gg <= g_last, the ranges
-// overlapping a row tile whose stream place starts at S_u) wrote slot
-// 2gg (its range starts inside the tile) or 2gg + 1, or nothing (empty range).
+// holding key tiles of a row tile whose segment starts at S_u) wrote slot
+// 2gg (its range starts inside the segment) or 2gg + 1, or nothing (empty
+// range).
 DDT_HD long long contributor_slot(long long gg, long long S_u, long long W, long long G) {
   const long long s0 = range_start(gg, W, G);
   const long long s1 = range_start(gg + 1, W, G);
@@ -154,19 +186,25 @@ DDT_HD void narrow_place(long long bid, long long& range, int& quarter) {
 }
 
 // One unit (a row tile over a key range) of a workgroup's range: the unit
-// starting at stream position pos, inside request b (pref[b] <= pos <
-// pref[b + 1]).
+// whose segment holds stream position pos, inside request b (pref[b] <= pos <
+// pref[b + 1]), with start cost c.  Key tiles [kb0, kb1) (empty when the
+// range ends inside the start cost); adv: the positions of the range it
+// takes, so that the next unit starts at pos + adv.
 struct UnitPos {
   int rt, kb0, kb1;
+  long long adv;
   bool complete;
 };
-DDT_HD UnitPos unit_at(long long pos, long long end, long long pref_b, const ReqInfo& ri) {
+DDT_HD UnitPos unit_at(long long pos, long long end, long long pref_b, const ReqInfo& ri, int c) {
   UnitPos u;
+  const long long seg = (long long)ri.nkb + c;
   const long long off = pos - pref_b;
-  u.rt = (int)(off / ri.nkb);
-  u.kb0 = (int)(off % ri.nkb);
-  const long long left = end - pos;
-  u.kb1 = (long long)(ri.nkb - u.kb0) < left ? ri.nkb : u.kb0 + (int)left;
+  u.rt = (int)(off / seg);
+  const long long in = off % seg;                              // position inside the segment
+  const long long stop = seg - in < end - pos ? seg : in + (end - pos);
+  u.kb0 = in > c ? (int)(in - c) : 0;
+  u.kb1 = stop > c ? (int)(stop - c) : 0;
+  u.adv = stop - in;
   u.complete = u.kb0 == 0 && u.kb1 == ri.nkb;
   return u;
 }
@@ -224,10 +262,11 @@ inline AttnPlan plan_verify_attn(int B, int Q, int H, int max_kv, int d_lat, int
   if (g < 1) g = 1;
   p.grid = (int)g;
   p.num_cu = num_cu > 0 ? num_cu : 256;
-  // Partial outputs and log-sum-exps (two slots per workgroup), then the work
-  // prefix over requests and the split mode that the merge kernels read.
+  // Partial outputs and log-sum-exps (two slots per workgroup), then the
+  // stream prefix over requests, the split mode and the start cost that the
+  // merge kernels read.
   p.ws_bytes = (size_t)2 * p.grid * kRowsPerWG * ((size_t)d_lat + 1) * sizeof(float) +
-               ((size_t)B + 2) * sizeof(long long);
+               ((size_t)B + 3) * sizeof(long long);
   return p;
 }
 

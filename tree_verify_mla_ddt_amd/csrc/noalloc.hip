@@ -14,11 +14,12 @@ namespace {
 // The largest workspace any verify-attention plan takes on a device of up to
 // kScratchCUs compute units (MI355X has 256): two partial 128-row tiles of
 // d_lat + 1 floats for each of kScratchCUs workgroups at d_lat = 512, then the
-// work prefix of DDT_MAX_BATCH_ATTN requests.  About 128.3 MiB.
+// stream prefix of DDT_MAX_BATCH_ATTN requests, split mode and start cost
+// (rounded up to 16 bytes).  About 128.3 MiB.
 constexpr int kScratchCUs = 256;
 constexpr size_t kScratchBytes =
     (size_t)2 * kScratchCUs * ddt::kRowsPerWG * (512 + 1) * sizeof(float) +
-    ((size_t)DDT_MAX_BATCH_ATTN + 2) * sizeof(long long);
+    ((size_t)DDT_MAX_BATCH_ATTN + 4) * sizeof(long long);
 static_assert(kScratchBytes % 16 == 0, "scratch rows stay 16-byte aligned");
 
 // The array itself.  In host code `scratch` names a host-side stand-in, never

@@ -5,6 +5,8 @@
 // checks, for one set of request sizes:
 //  * every (request, row tile, key tile) with work is taken by exactly one
 //    workgroup, and no range walks into a row tile without work;
+//  * the stream (row-tile segments of start cost c plus key tiles) is cut as
+//    the kernels cut it, and ranges that end inside a start cost run nothing;
 //  * a workgroup writes at most one partial result per slot, its slots lie in
 //    [0, 2G) (the workspace holds 2G), and no slot is written by two units;
 //  * for every row tile, the merge's contributor rule names exactly the slots
@@ -32,9 +34,13 @@ int fail(char* msg, int len, const char* what, long long a, long long b, long lo
 
 // plant != 0 plants a mistake in the merge's view (1: head and tail slots
 // swapped, 2: the last contributor dropped), to show the check catches it.
+// stats (may be NULL) receives: [0] the start cost c, [1] ranges that end
+// inside a start cost, [2] ranges holding key tiles of two or more row tiles,
+// [3] the largest (key tiles + c per row tile begun) over ranges, [4] the
+// stream length per range rounded up.
 extern "C" int ddt_split_check(int B, int Q, int H, int max_kv, const int32_t* prefix_len,
                                const int32_t* n_nodes, int num_cu, int d_lat, int plant,
-                               char* msg, int msg_len) {
+                               char* msg, int msg_len, long long* stats) {
   using namespace ddt;
   if (msg && msg_len > 0) msg[0] = '\0';
   if (B < 1 || B > kMaxBatch || Q < 1 || H < 1 || max_kv < 1) return fail(msg, msg_len, "bad args", B, Q, H);
@@ -43,7 +49,7 @@ extern "C" int ddt_split_check(int B, int Q, int H, int max_kv, const int32_t* p
   const int RT = plan.row_tiles;
   if (G < 1 || G > kMaxGrid) return fail(msg, msg_len, "grid out of range", G, 0, 0);
   const size_t need = (size_t)2 * G * kRowsPerWG * ((size_t)d_lat + 1) * sizeof(float) +
-                      ((size_t)B + 2) * sizeof(long long);
+                      ((size_t)B + 3) * sizeof(long long);
   if (plan.ws_bytes < need) return fail(msg, msg_len, "workspace too small", (long long)plan.ws_bytes, (long long)need, 0);
 
   if (plan.narrow) {
@@ -63,22 +69,25 @@ extern "C" int ddt_split_check(int B, int Q, int H, int max_kv, const int32_t* p
   }
 
   std::vector<ReqInfo> ri(B);
-  std::vector<long long> pref(B + 1, 0);
+  std::vector<long long> tiles(B + 1, 0);  // key tiles with work before request b
+  long long units = 0;
+  bool same = true;
   for (int b = 0; b < B; ++b) {
     ri[b] = req_info(prefix_len, n_nodes, b, Q, H, max_kv, RT);
-    pref[b + 1] = pref[b] + (long long)ri[b].vt * ri[b].nkb;
+    tiles[b + 1] = tiles[b] + (long long)ri[b].vt * ri[b].nkb;
+    units += ri[b].vt;
+    if (ri[b].nkb != ri[0].nkb || ri[b].vt != ri[0].vt) same = false;
   }
-  const long long Wtot = pref[B];
   const bool split2 = (long long)B * RT >= G;
-  long long mode = -1;
-  if (split2) {
-    bool same = true;
-    for (int b = 0; b < B; ++b)
-      if (ri[b].nkb != ri[0].nkb || ri[b].vt != ri[0].vt) same = false;
-    mode = split_mode(same, ri[0].vt, B, G);
-  }
+  const long long mode = split2 ? split_mode(same, ri[0].vt, B, G) : -1;
+  const int c = unit_cost(mode, same, units, G);
+  if (c < 0 || c > kUnitCost) return fail(msg, msg_len, "start cost", c, mode, units);
+  std::vector<long long> pref(B + 1, 0);  // the stream prefix
+  for (int b = 0; b < B; ++b) pref[b + 1] = pref[b] + (long long)ri[b].vt * (ri[b].nkb + c);
+  const long long Wtot = pref[B];
 
-  std::vector<int> cover((size_t)Wtot, 0);
+  long long n_empty = 0, n_multi = 0, max_load = 0;
+  std::vector<int> cover((size_t)tiles[B], 0);
   std::map<long long, std::set<long long>> written;  // unit (b * RT + rt) -> slots
   std::map<long long, long long> slot_owner;         // slot -> unit
   std::set<long long> direct;                        // units written whole
@@ -87,22 +96,36 @@ extern "C" int ddt_split_check(int B, int Q, int H, int max_kv, const int32_t* p
       const long long gid = logical_gid(bl, G);
       if (gid < 0 || gid >= G) return fail(msg, msg_len, "logical id out of range", bl, gid, G);
       long long start, end;
-      workgroup_range(mode, half == 1, gid, Wtot, ri[0].nkb, G, start, end);
+      workgroup_range(mode, half == 1, gid, Wtot, ri[0].nkb + c, G, start, end);
       if (start >= end) continue;
       if (start < 0 || end > Wtot) return fail(msg, msg_len, "range outside the work", start, end, Wtot);
       int b = 0;
       while (b + 1 < B && pref[b + 1] <= start) ++b;
       long long pos = start;
-      int tails = 0;
+      int tails = 0, n_units = 0;
+      long long load = 0;
       while (pos < end) {
         while (pref[b + 1] <= pos) ++b;
         if (b >= B || ri[b].vt == 0) return fail(msg, msg_len, "walked into a request without work", b, pos, gid);
-        const UnitPos up = unit_at(pos, end, pref[b], ri[b]);
-        if (up.rt < 0 || up.rt >= ri[b].vt || up.kb0 < 0 || up.kb1 > ri[b].nkb || up.kb0 >= up.kb1)
-          return fail(msg, msg_len, "unit outside its request", b, up.rt, up.kb0);
+        const UnitPos up = unit_at(pos, end, pref[b], ri[b], c);
+        if (up.adv < 1 || pos + up.adv > end)
+          return fail(msg, msg_len, "unit advance", pos, up.adv, end);
         const bool head = pos == start;
+        pos += up.adv;
+        if (up.kb1 <= up.kb0) {
+          // Only a range's last unit may be empty, and only by ending inside
+          // the start cost of its row tile.
+          if (pos != end || up.kb0 != 0 || up.kb1 != 0)
+            return fail(msg, msg_len, "empty unit not at a range's end", b, up.rt, up.kb0);
+          ++n_empty;
+          continue;
+        }
+        ++n_units;
+        load += (up.kb1 - up.kb0) + (up.kb0 == 0 ? c : 0);
+        if (up.rt < 0 || up.rt >= ri[b].vt || up.kb0 < 0 || up.kb1 > ri[b].nkb)
+          return fail(msg, msg_len, "unit outside its request", b, up.rt, up.kb0);
         for (int kb = up.kb0; kb < up.kb1; ++kb)
-          ++cover[(size_t)(pref[b] + (long long)up.rt * ri[b].nkb + kb)];
+          ++cover[(size_t)(tiles[b] + (long long)up.rt * ri[b].nkb + kb)];
         const long long unit = (long long)b * RT + up.rt;
         if (up.complete) {
           direct.insert(unit);
@@ -115,12 +138,13 @@ extern "C" int ddt_split_check(int B, int Q, int H, int max_kv, const int32_t* p
           slot_owner[slot] = unit;
           written[unit].insert(slot);
         }
-        pos += up.kb1 - up.kb0;
       }
+      if (n_units > 1) ++n_multi;
+      if (load > max_load) max_load = load;
     }
   }
-  for (long long t = 0; t < Wtot; ++t)
-    if (cover[(size_t)t] != 1) return fail(msg, msg_len, "tile covered", t, cover[(size_t)t], Wtot);
+  for (long long t = 0; t < tiles[B]; ++t)
+    if (cover[(size_t)t] != 1) return fail(msg, msg_len, "tile covered", t, cover[(size_t)t], tiles[B]);
 
   // The merge's view of every row tile with work.
   for (int b = 0; b < B; ++b) {
@@ -129,11 +153,12 @@ extern "C" int ddt_split_check(int B, int Q, int H, int max_kv, const int32_t* p
       const auto wit = written.find(unit);
       const size_t nw = wit == written.end() ? 0 : wit->second.size();
       long long S, W;
-      if (!stream_place(mode, pref.data(), B, b, rt, ri[b], G, S, W)) {
+      if (!stream_place(mode, pref.data(), B, b, rt, ri[b], G, c, S, W)) {
         if (nw != 0 || !direct.count(unit)) return fail(msg, msg_len, "whole unit not written whole", b, rt, (long long)nw);
         continue;
       }
-      const long long gf = range_owner(S, W, G), gl = range_owner(S + ri[b].nkb - 1, W, G);
+      long long gf, gl;
+      tile_owners(S, W, G, ri[b].nkb, c, gf, gl);
       if (gf == gl) {
         if (nw != 0 || !direct.count(unit)) return fail(msg, msg_len, "uncut tile not written directly", b, rt, (long long)nw);
         continue;
@@ -148,6 +173,13 @@ extern "C" int ddt_split_check(int B, int Q, int H, int max_kv, const int32_t* p
         return fail(msg, msg_len, "merge contributors differ from written slots", b, rt, (long long)contrib.size() - (long long)nw);
       if (direct.count(unit)) return fail(msg, msg_len, "cut tile also written whole", b, rt, 0);
     }
+  }
+  if (stats) {
+    stats[0] = c;
+    stats[1] = n_empty;
+    stats[2] = n_multi;
+    stats[3] = max_load;
+    stats[4] = (Wtot + G - 1) / G;
   }
   return 0;
 }

@@ -151,51 +151,85 @@ __device__ __forceinline__ long long uni(long long v) {
   return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
 }
 
-// Exclusive prefix of work (key tiles) over requests into s_pref[0..B], and
-// (when s_req is given) each request's clamped prefix length and tree size
-// into s_req[0..B); called by all kBlock threads of a workgroup.
+// The split of a launch: mode (split_mode, -1 for one stream) and the start
+// cost c of a row tile in the stream.
+struct SplitMode {
+  long long mode;
+  int c;
+};
+
+// Exclusive stream prefix over requests into s_pref[0..B] (each row tile with
+// work is a segment of nkb + c positions) and (when s_req is given) each
+// request's clamped prefix length and tree size into s_req[0..B); called by
+// all kBlock threads of a workgroup.  s_wsum holds 2 * kBlock / kWave values.
+// The split mode applies to a launch of 2G workgroups (split2), and c is
+// decided from the request sizes unless given (c_given >= 0, as the merge
+// kernels read it from the workspace).
 template <int kBlock>
-__device__ void work_prefix(long long* s_pref, long long* s_wsum, int2* s_req,
-                            const int32_t* prefix_len, const int32_t* n_nodes, int B, int Q, int H,
-                            int max_kv, int RT) {
+__device__ SplitMode work_prefix(long long* s_pref, long long* s_wsum, int2* s_req,
+                                 const int32_t* prefix_len, const int32_t* n_nodes, int B, int Q,
+                                 int H, int max_kv, int RT, long long G, bool split2,
+                                 int c_given) {
   constexpr int kPer = (kMaxBatch + kBlock - 1) / kBlock;  // requests per thread
+  constexpr int kW = kBlock / kWave;
   const int t = threadIdx.x;
+  const ReqInfo r0 = req_info(prefix_len, n_nodes, 0, Q, H, max_kv, RT);
   long long w[kPer];
-  long long mine = 0;
+  int v[kPer];
+  long long mine = 0, umine = 0;
+  int same = 1;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
     const int b = kPer * t + k;
     w[k] = 0;
+    v[k] = 0;
     if (b < B) {
       const ReqInfo r = req_info(prefix_len, n_nodes, b, Q, H, max_kv, RT);
       w[k] = (long long)r.vt * r.nkb;
+      v[k] = r.vt;
+      if (r.vt != r0.vt || r.nkb != r0.nkb) same = 0;
       if (s_req) s_req[b] = make_int2(r.L, r.nb);
     }
     mine += w[k];
+    umine += v[k];
   }
-  long long incl = mine;
+  long long incl = mine, uincl = umine;
   const int lane = t & 63, wv = t >> 6;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const long long o = __shfl_up(incl, off);
-    if (lane >= off) incl += o;
+    const long long uo = __shfl_up(uincl, off);
+    if (lane >= off) {
+      incl += o;
+      uincl += uo;
+    }
   }
-  if (lane == 63) s_wsum[wv] = incl;
-  __syncthreads();
-  long long before = 0;
-  for (int k = 0; k < wv; ++k) before += s_wsum[k];
-  long long run = before + incl - mine;
+  if (lane == 63) {
+    s_wsum[wv] = incl;
+    s_wsum[kW + wv] = uincl;
+  }
+  same = __syncthreads_and(same);
+  long long before = 0, ubefore = 0, tot = 0, utot = 0;
+  for (int k = 0; k < kW; ++k) {
+    if (k < wv) {
+      before += s_wsum[k];
+      ubefore += s_wsum[kW + k];
+    }
+    tot += s_wsum[k];
+    utot += s_wsum[kW + k];
+  }
+  SplitMode sp;
+  sp.mode = split2 ? split_mode(same != 0, r0.vt, B, G) : -1;
+  sp.c = c_given >= 0 ? c_given : unit_cost(sp.mode, same != 0, utot, G);
+  long long run = before + incl - mine + sp.c * (ubefore + uincl - umine);
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
     if (kPer * t + k < B) s_pref[kPer * t + k] = run;
-    run += w[k];
+    run += w[k] + (long long)sp.c * v[k];
   }
-  if (t == 0) {
-    long long tot = 0;
-    for (int k = 0; k < kBlock / kWave; ++k) tot += s_wsum[k];
-    s_pref[B] = tot;
-  }
+  if (t == 0) s_pref[B] = tot + sp.c * utot;
   __syncthreads();
+  return sp;
 }
 
 template <typename T, int DL, int DR>
@@ -214,7 +248,7 @@ struct Smem {
   uint64_t visrow[kRowsPerWG][2];   // visibility bitset of each row's tree node
   long long pref[kMaxBatch + 1];
   int2 req[kMaxBatch];  // per request: clamped prefix length, tree size
-  long long wsum[kWaves];
+  long long wsum[2 * kWaves];
 };
 
 // Raw pool slot id of key `j` of the request (-1 past the request); its range
@@ -978,32 +1012,26 @@ __device__ __forceinline__ void for_each_unit(SM& sm, const int32_t* __restrict_
                                               int H, int max_kv, int RT,
                                               long long* __restrict__ ws_pref, int G,
                                               long long bl, bool write_pref, Run&& run) {
-  work_prefix<kThr>(sm.pref, sm.wsum, sm.req, prefix_len, n_nodes, B, Q, H, max_kv, RT);
-  const long long Wtot = uni(sm.pref[B]);
   const long long Gn = G;
-  long long mode = -1;
-  bool second = false;
-  if constexpr (kSplit2) {
-    // Launched with 2G workgroups for the aligned split (see workgroup_range);
-    // the kernel decides from the clamped request sizes whether it applies.
-    second = bl >= Gn;
-    const ReqInfo ri0 = req_info_ln(sm.req[0].x, sm.req[0].y, H, RT);
-    int same = 1;
-    for (int bb = threadIdx.x; bb < B; bb += kThr) {
-      const ReqInfo r = req_info_ln(sm.req[bb].x, sm.req[bb].y, H, RT);
-      if (r.nkb != ri0.nkb || r.vt != ri0.vt) same = 0;
-    }
-    same = __syncthreads_and(same);
-    mode = split_mode(same != 0, ri0.vt, B, Gn);
-  }
-  if (write_pref) {  // for the merge kernels: the work prefix and the split mode
+  // Launched with 2G workgroups for the aligned split (see workgroup_range);
+  // the kernel decides from the clamped request sizes whether it applies.
+  const SplitMode sp = work_prefix<kThr>(sm.pref, sm.wsum, sm.req, prefix_len, n_nodes, B, Q, H,
+                                         max_kv, RT, Gn, kSplit2, -1);
+  const long long Wtot = uni(sm.pref[B]);
+  const long long mode = uni(sp.mode);
+  const int c = uni(sp.c);
+  const bool second = kSplit2 && bl >= Gn;
+  if (write_pref) {  // for the merge kernels: stream prefix, split mode, start cost
     for (int i = threadIdx.x; i <= B; i += kThr) ws_pref[i] = sm.pref[i];
-    if (threadIdx.x == 0) ws_pref[B + 1] = mode;
+    if (threadIdx.x == 0) {
+      ws_pref[B + 1] = mode;
+      ws_pref[B + 2] = c;
+    }
   }
   const long long gid = logical_gid(bl - (second ? Gn : 0), Gn);
   long long start, end;
   const ReqInfo ri0 = req_info_ln(sm.req[0].x, sm.req[0].y, H, RT);
-  workgroup_range(mode, second, gid, Wtot, ri0.nkb, Gn, start, end);
+  workgroup_range(mode, second, gid, Wtot, ri0.nkb + c, Gn, start, end);
   start = uni(start);
   end = uni(end);
   if (start >= end) return;
@@ -1038,14 +1066,15 @@ __device__ __forceinline__ void for_each_unit(SM& sm, const int32_t* __restrict_
       const int2 ln = sm.req[b];
       u.ri = req_info_ln(uni(ln.x), uni(ln.y), H, RT);
     }
-    const UnitPos up = unit_at(pos, end, uni(sm.pref[b]), u.ri);
+    const UnitPos up = unit_at(pos, end, uni(sm.pref[b]), u.ri, c);
     u.rt = up.rt;
     u.kb0 = up.kb0;
     u.kb1 = up.kb1;
     u.complete = up.complete;
     u.slot = partial_slot(gid, head);
     u.nkeys = u.ri.L + u.ri.nb;
-    pos += u.kb1 - u.kb0;
+    pos += up.adv;
+    if (u.kb1 <= u.kb0) continue;  // the range ends inside this tile's start cost
     if (head != (pass == 1)) continue;
     run(u, gid);
     if (pass == 1) break;
@@ -1096,7 +1125,7 @@ struct SmemW {
   alignas(128) unsigned char qpe[kRowsPerWG][DR * 2];  // rope part of the query tile
   long long pref[kMaxBatch + 1];
   int2 req[kMaxBatch];  // per request: clamped prefix length, tree size
-  long long wsum[kWavesW];
+  long long wsum[2 * kWavesW];
 };
 
 // Direct loads of one key tile by the four waves: wave w fills the latent rows
@@ -1611,7 +1640,7 @@ struct SmemN {
   uint64_t visrow[32][2];           // visibility bitset of each row's tree node
   long long pref[kMaxBatch + 1];
   int2 req[kMaxBatch];  // per request: clamped prefix length, tree size
-  long long wsum[kWavesW];
+  long long wsum[2 * kWavesW];
 };
 
 template <int DL, int DR>
@@ -2046,13 +2075,13 @@ __global__ __launch_bounds__(kMergeThreads) void verify_merge_kernel(
   // recorded them.
   const long long Gn = grid_attn;
   const long long mode = ws_pref[B + 1];
+  const int c = (int)ws_pref[B + 2];
 
   const bool has_work = rt < ri.vt;
   if (has_work) {
-    long long S_u, Wtot;
-    if (!stream_place(mode, ws_pref, B, b, rt, ri, Gn, S_u, Wtot)) return;  // a whole unit
-    const long long g_first = range_owner(S_u, Wtot, Gn);
-    const long long g_last = range_owner(S_u + ri.nkb - 1, Wtot, Gn);
+    long long S_u, Wtot, g_first, g_last;
+    if (!stream_place(mode, ws_pref, B, b, rt, ri, Gn, c, S_u, Wtot)) return;  // a whole unit
+    tile_owners(S_u, Wtot, Gn, ri.nkb, c, g_first, g_last);
     if (g_first == g_last) return;  // written directly by the attention kernel
     // Each contributing workgroup (non-empty range) wrote its partial for this
     // tile into slot 2g when the tile holds the start of its range, else 2g+1.
@@ -2206,16 +2235,18 @@ __global__ __launch_bounds__(kMergeThreads) void verify_merge_wide_kernel(
     const long long* __restrict__ ws_pref) {
   using MG = MergeGeoW<DL>;
   __shared__ long long s_pref[kMaxBatch + 1];
-  __shared__ long long s_wsum[kMergeThreads / kWave];
+  __shared__ long long s_wsum[2 * kMergeThreads / kWave];
   __shared__ int s_src[kMaxGrid];
   __shared__ int s_cnt;
   __shared__ float s_lse[MG::kRows];
   __shared__ float s_w[kMergeBatchW][MG::kRows];
-  // The split mode the attention kernel recorded; the aligned split needs no
-  // work prefix.
+  // The split mode and start cost the attention kernel recorded; the aligned
+  // split needs no stream prefix.
   const long long mode = ws_pref[B + 1];
+  const int c = (int)ws_pref[B + 2];
   if (mode < 0)
-    work_prefix<kMergeThreads>(s_pref, s_wsum, nullptr, prefix_len, n_nodes, B, Q, H, max_kv, RT);
+    work_prefix<kMergeThreads>(s_pref, s_wsum, nullptr, prefix_len, n_nodes, B, Q, H, max_kv, RT,
+                               grid_attn, false, c);
   const int tid = threadIdx.x;
   // Units in reverse: under the aligned split the row tiles to merge are the
   // last ones, and are dispatched first this way.
@@ -2229,10 +2260,9 @@ __global__ __launch_bounds__(kMergeThreads) void verify_merge_wide_kernel(
 
   const bool has_work = rt < ri.vt;
   if (has_work) {
-    long long S_u, Wtot;
-    if (!stream_place(mode, s_pref, B, b, rt, ri, Gn, S_u, Wtot)) return;  // a whole unit
-    const long long g_first = range_owner(S_u, Wtot, Gn);
-    const long long g_last = range_owner(S_u + ri.nkb - 1, Wtot, Gn);
+    long long S_u, Wtot, g_first, g_last;
+    if (!stream_place(mode, s_pref, B, b, rt, ri, Gn, c, S_u, Wtot)) return;  // a whole unit
+    tile_owners(S_u, Wtot, Gn, ri.nkb, c, g_first, g_last);
     if (g_first == g_last) return;  // written directly by the attention kernel
     // Each contributing workgroup (non-empty range) wrote its partial for this
     // tile into slot 2g when the tile holds the start of its range, else 2g+1.
