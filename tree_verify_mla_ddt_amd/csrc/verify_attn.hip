@@ -1467,19 +1467,21 @@ __device__ __forceinline__ void run_unit_w(SmemW<DL, DR>& sm, const Args& a, con
       __builtin_amdgcn_sched_barrier(0);
     }
     // Residual pass: (p - bf16(p)) of the key halves that hold a heavy key,
-    // through the same V^T operands.
-    if (h0) {
-      const bf16x8_t r = pack_p<true>(p);
+    // through the same V^T operands, read kAheadPV MFMAs ahead.
+    auto residual = [&](int k1, const bf16x8_t r) __attribute__((always_inline)) {
+      bf16x8_t vr[kNCB];
 #pragma unroll
-      for (int cb = 0; cb < kNCB; ++cb)
-        o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va.read(cb, 0), r, o[cb], 0, 0, 0);
-    }
-    if (h1) {
-      const bf16x8_t r = pack_p<true>(p + 8);
+      for (int cb = 0; cb < kAheadPV; ++cb) vr[cb] = va.read(cb, k1);
 #pragma unroll
-      for (int cb = 0; cb < kNCB; ++cb)
-        o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va.read(cb, 1), r, o[cb], 0, 0, 0);
-    }
+      for (int cb = 0; cb < kNCB; ++cb) {
+        if (cb + kAheadPV < kNCB) vr[cb + kAheadPV] = va.read(cb + kAheadPV, k1);
+        __builtin_amdgcn_sched_barrier(0);
+        o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[cb], r, o[cb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    if (h0) residual(0, pack_p<true>(p));
+    if (h1) residual(1, pack_p<true>(p + 8));
   };
 
   // Step kb: QK^T of tile kb (with part A of tile kb-1's softmax), then the
@@ -1869,20 +1871,18 @@ __device__ __forceinline__ void run_unit_n(SmemN<DL, DR>& sm, const Args& a, con
       for (int i = 0; i < 2 * kNCBn; ++i)
         o[i % kNCBn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[i], (i / kNCBn) ? p1 : p0,
                                                                o[i % kNCBn], 0, 0, 0);
-      if (h0) {
-        const bf16x8_t r = pack_p<true>(p);
+      // Residual pass of the key halves with a heavy key: all of a half's
+      // operand reads are issued before its MFMAs.
+      auto residual = [&](int k1, const bf16x8_t r) __attribute__((always_inline)) {
+        bf16x8_t vr[kNCBn];
+#pragma unroll
+        for (int c = 0; c < kNCBn; ++c) vr[c] = va.read(kNCBn * wave + c, k1);
 #pragma unroll
         for (int c = 0; c < kNCBn; ++c)
-          o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va.read(kNCBn * wave + c, 0), r, o[c],
-                                                         0, 0, 0);
-      }
-      if (h1) {
-        const bf16x8_t r = pack_p<true>(p + 8);
-#pragma unroll
-        for (int c = 0; c < kNCBn; ++c)
-          o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va.read(kNCBn * wave + c, 1), r, o[c],
-                                                         0, 0, 0);
-      }
+          o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[c], r, o[c], 0, 0, 0);
+      };
+      if (h0) residual(0, pack_p<true>(p));
+      if (h1) residual(1, pack_p<true>(p + 8));
     };
 
     // Step kb: tile kb+1 starts loading; this wave's share of tile kb's
