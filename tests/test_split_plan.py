@@ -96,7 +96,7 @@ def test_start_cost_balances_ranges(checker):
     for _ in range(20):
         plen = rng.integers(3072, 5121, size=4)
         st = check(checker, plen, [17] * 4, 17, 64, int(plen.max()) + 17)
-        assert st[0] == 4 and st[2] > 0
+        assert st[0] == 6 and st[2] > 0
         assert st[3] <= st[4] + st[0], st
     st = check(checker, [2048], [9], 9, 64, 2057)
     assert st[0] == 0 and st[2] == 0

@@ -28,7 +28,7 @@ constexpr int kRowsPerWG = 128;   // rows per tile
 constexpr int kMaxBatch = 512;    // requests the attention kernels take
 constexpr int kXcds = 8;          // XCDs the workgroups are dealt to
 constexpr int kMaxGrid = 1024;    // upper bound of the attention grid
-constexpr int kUnitCost = 4;      // stream positions charged for starting a row tile
+constexpr int kUnitCost = 6;      // stream positions charged for starting a row tile
 
 #define DDT_HD __host__ __device__ __forceinline__
 

@@ -36,7 +36,7 @@
 //    tile holds a key whose weight is a sizeable share of its row's running sum
 //    (concentrated attention, short contexts), the bf16 rounding residual of
 //    the probabilities goes through a second MFMA against the same value
-//    operand, which brings the value product to ~2^-17 relative accuracy.
+//    operand, which brings the value product to ~2^-16 relative accuracy.
 //  * The mask: prefix keys are always visible; a tree key k is visible when bit
 //    k of the row's node bitset is set; keys beyond the request or with a slot
 //    id outside the pool are invisible (their tile rows hold pool row 0, which
@@ -79,8 +79,8 @@ constexpr float kLn2 = 0.6931471805599453f;
 // A tile takes the residual pass when some key's probability exceeds this share
 // of its row's running sum (an upper bound on the key's final weight).  A key
 // below it carries at most a sixteenth of the row's weight, so leaving its
-// bf16 rounding (relative 2^-9) uncorrected moves the output by at most
-// 2^-13 times the largest value entry.
+// bf16 rounding (round to nearest: relative 2^-8 at most) uncorrected moves the
+// output by at most 2^-12 times the largest value entry.
 constexpr float kHeavyShare = 1.0f / 16.0f;
 // Reference-max slack of the online softmax, in log2 units.
 constexpr float kRescaleLog2 = 8.0f;
