@@ -2214,8 +2214,11 @@ __global__ __launch_bounds__(kMergeThreads) void verify_merge_kernel(
 }
 
 // The merge for many row tiles: 8 rows of 512 (16 of 64) per workgroup, the
-// work prefix recomputed per workgroup, contributors' chunks accumulated four
-// at a time.
+// work prefix recomputed per workgroup.  The first kMergePreW contributors'
+// partial rows are requested before the row log-sum-exps are reduced (they do
+// not depend on them), and the log-sum-exps read for that reduction are kept
+// in LDS for the weights, so the bulk of the reads starts one dependent round
+// trip after the contributor list.
 template <int DL>
 struct MergeGeoW {
   static constexpr int kChunks = DL / 4;                          // float4 per row
@@ -2226,6 +2229,7 @@ struct MergeGeoW {
   static_assert(kRowsPerWG % kRows == 0 && kLanesPerRow <= kWave, "merge tiling");
 };
 constexpr int kMergeBatchW = 32;  // contributors whose weights are staged at once
+constexpr int kMergePreW = 4;     // contributors whose rows are requested up front
 
 template <int DL>
 __global__ __launch_bounds__(kMergeThreads) void verify_merge_wide_kernel(
@@ -2239,6 +2243,7 @@ __global__ __launch_bounds__(kMergeThreads) void verify_merge_wide_kernel(
   __shared__ int s_src[kMaxGrid];
   __shared__ int s_cnt;
   __shared__ float s_lse[MG::kRows];
+  __shared__ float s_lv[kMergeBatchW][MG::kRows];  // LSEs of the first batch's contributors
   __shared__ float s_w[kMergeBatchW][MG::kRows];
   // The split mode and start cost the attention kernel recorded; the aligned
   // split needs no stream prefix.
@@ -2287,17 +2292,46 @@ __global__ __launch_bounds__(kMergeThreads) void verify_merge_wide_kernel(
   __syncthreads();
   const int cnt = s_cnt;
 
+  // Rows of this thread's chunks and the first kMergePreW contributors' partial
+  // rows, requested now.  Rows that no contributor wrote (not live) read stale
+  // workspace; their sums are discarded below, and every address stays inside
+  // the workspace.
+  float4 acc[MG::kItems];
+  int rl_of[MG::kItems];
+#pragma unroll
+  for (int it = 0; it < MG::kItems; ++it) {
+    acc[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+    rl_of[it] = (tid + it * kMergeThreads) / MG::kChunks;
+  }
+  const int chunk = tid % MG::kChunks;
+  const int npre = cnt < kMergePreW ? cnt : kMergePreW;
+  float4 pre[kMergePreW][MG::kItems];
+#pragma unroll
+  for (int k = 0; k < kMergePreW; ++k) {
+#pragma unroll
+    for (int it = 0; it < MG::kItems; ++it) pre[k][it] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (k < npre) {
+      const float* src = ws_o + ((long long)s_src[k] * kRowsPerWG + r0) * DL + chunk * 4;
+#pragma unroll
+      for (int it = 0; it < MG::kItems; ++it)
+        pre[k][it] = *reinterpret_cast<const float4*>(src + (long long)rl_of[it] * DL);
+    }
+  }
+
   // Row log-sum-exp: kLanesPerRow lanes per row, each over every
-  // kLanesPerRow-th contributor, then a butterfly over the group.
+  // kLanesPerRow-th contributor (keeping the first batch's values in LDS),
+  // then a butterfly over the group.
   {
     const int rl = tid / MG::kLanesPerRow, j = tid % MG::kLanesPerRow;
     const int rr = r0 + rl;
     const long long r_loc = (long long)rt * kRowsPerWG + rr;
     const bool live = r_loc < QH && (int)(r_loc / H) < ri.nb;
     float m = -INFINITY, z = 0.0f;
+    for (int k = j; k < kMergeBatchW; k += MG::kLanesPerRow) s_lv[k][rl] = -INFINITY;
     if (live) {
       for (int k = j; k < cnt; k += MG::kLanesPerRow) {
         const float v = ws_lse[(long long)s_src[k] * kRowsPerWG + rr];
+        if (k < kMergeBatchW) s_lv[k][rl] = v;
         if (v == -INFINITY) continue;
         if (v > m) {
           z = z * __expf(m - v) + 1.0f;
@@ -2321,14 +2355,6 @@ __global__ __launch_bounds__(kMergeThreads) void verify_merge_wide_kernel(
   }
   __syncthreads();
 
-  float4 acc[MG::kItems];
-  int rl_of[MG::kItems];
-#pragma unroll
-  for (int it = 0; it < MG::kItems; ++it) {
-    acc[it] = make_float4(0.f, 0.f, 0.f, 0.f);
-    rl_of[it] = (tid + it * kMergeThreads) / MG::kChunks;
-  }
-  const int chunk = tid % MG::kChunks;
   for (int k0 = 0; k0 < cnt; k0 += kMergeBatchW) {
     const int nk = cnt - k0 < kMergeBatchW ? cnt - k0 : kMergeBatchW;
     for (int e = tid; e < kMergeBatchW * MG::kRows; e += kMergeThreads) {
@@ -2336,16 +2362,29 @@ __global__ __launch_bounds__(kMergeThreads) void verify_merge_wide_kernel(
       const float lt = s_lse[rl];
       float w = 0.0f;
       if (k < nk && lt != -INFINITY) {
-        const float v = ws_lse[(long long)s_src[k0 + k] * kRowsPerWG + r0 + rl];
+        const float v = k0 == 0 ? s_lv[k][rl]
+                                : ws_lse[(long long)s_src[k0 + k] * kRowsPerWG + r0 + rl];
         if (v != -INFINITY) w = __expf(v - lt);
       }
       s_w[k][rl] = w;
     }
     __syncthreads();
-    // Rows that no contributor wrote (not live) read stale workspace here; their
-    // sums are discarded below, and every address stays inside the workspace.
+    if (k0 == 0) {
+#pragma unroll
+      for (int k = 0; k < kMergePreW; ++k) {
+        if (k >= npre) break;
+#pragma unroll
+        for (int it = 0; it < MG::kItems; ++it) {
+          const float w = s_w[k][rl_of[it]];
+          acc[it].x = __builtin_fmaf(w, pre[k][it].x, acc[it].x);
+          acc[it].y = __builtin_fmaf(w, pre[k][it].y, acc[it].y);
+          acc[it].z = __builtin_fmaf(w, pre[k][it].z, acc[it].z);
+          acc[it].w = __builtin_fmaf(w, pre[k][it].w, acc[it].w);
+        }
+      }
+    }
 #pragma unroll 8
-    for (int k = 0; k < nk; ++k) {
+    for (int k = k0 == 0 ? npre : 0; k < nk; ++k) {
       const float* src = ws_o + ((long long)s_src[k0 + k] * kRowsPerWG + r0) * DL + chunk * 4;
 #pragma unroll
       for (int it = 0; it < MG::kItems; ++it) {
