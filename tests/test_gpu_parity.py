@@ -239,6 +239,11 @@ def tree_for(wl):
     ("b64_l2k_q9", {"L": 40}, True),
     ("b64_l2k_q9", {"L": 520}, False),
     ("b64_l2k_q9", {"L": 300, "L_jitter": 0.25}, True),
+    # 100 uniform requests: 500 row tiles on a 256-range grid, so the aligned
+    # split leaves 244 row tiles that do not divide the grid and charges their
+    # start cost: leftover ranges cross row tiles and some end inside a start
+    # cost (nothing to run).
+    ("b64_l2k_q9", {"B": 100, "L": 100}, True),
     ("b8_l32k_q65", {"B": 2, "L": 600}, True),
     # Q=65 with eight uniform requests: 264 row tiles, at least one per
     # workgroup, so the aligned split runs (eight leftover row tiles, each
