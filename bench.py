@@ -43,7 +43,10 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_attn_traffic.json")
-ATTN_SOURCE = os.path.join(ROOT, "tree_verify_mla_ddt_amd", "csrc", "verify_attn.hip")
+# The attention kernels and the work split they run: the traffic record is
+# valid for exactly these sources.
+ATTN_SOURCES = [os.path.join(ROOT, "tree_verify_mla_ddt_amd", "csrc", f)
+                for f in ("verify_attn.hip", "attn_split.h")]
 
 
 def log(msg):
@@ -77,8 +80,11 @@ def attn_work(wl, tree):
 
 
 def source_digest():
-    with open(ATTN_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in ATTN_SOURCES:
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode() + b"\0" + f.read() + b"\0")
+    return h.hexdigest()[:16]
 
 
 COPY_BYTES = 256 << 20  # the --copy-calibration copy

@@ -4,17 +4,17 @@
 // The attention kernels cut the (request, 128-row tile, 32-key tile) work into
 // contiguous ranges, one per workgroup; row tiles whose key range is cut are
 // written as partial results to workspace slots and combined by the merge
-// kernels.
+// kernels.  Everything that decides which workgroup takes which tiles, which
+// slot a partial result lands in and which slots the merge reads is here, so
+// that a host program (the split checker) runs exactly the code the kernels
+// run.
 //
 // The work is one stream of positions.  Each row tile with work occupies a
 // segment of nkb + c positions: c positions that stand for the cost of
 // starting the tile in a workgroup (query load, pipeline fill, partial output;
 // a few key tiles' worth), then its nkb key tiles.  Ranges are equal cuts of
 // the stream, so a range that crosses into a second row tile takes that many
-// fewer key tiles.  c is 0 when every range lies inside one row tile anyway.  Everything that decides which workgroup takes which tiles, which
-// slot a partial result lands in and which slots the merge reads is here, so
-// that a host program (the split checker) runs exactly the code the kernels
-// run.
+// fewer key tiles.  c is 0 when every range lies inside one row tile anyway.
 #pragma once
 
 #include <hip/hip_runtime.h>
