@@ -351,14 +351,21 @@ def test_verify_attn_edge_cases():
         check_attn(g_out, g_lse, o_out, o_lse, TOL[wl.dtype], label)
 
 
-@pytest.mark.parametrize("Q,H,L,B", [(1, 64, 2048, 2), (128, 8, 333, 2), (65, 64, 70, 1),
-                                     (2, 1, 31, 3), (9, 3, 1, 2)])
-def test_verify_attn_shapes(Q, H, L, B):
-    """Decode (Q=1), the widest tree (Q=128, two bitset words), odd head counts
-    and tiny prefixes, with random trees."""
-    note(f"verify_attn shape Q={Q} H={H} L={L} B={B}")
-    rng = np.random.default_rng(Q * 1000 + H)
-    wl = workloads.make_workload("b1_l2k_q9", B=B, L=L, budget=Q - 1, H=H, D=8, K=16)
+@pytest.mark.parametrize("Q,H,L,B,jitter", [
+    (1, 64, 2048, 2, 0.0), (128, 8, 333, 2, 0.0), (65, 64, 70, 1, 0.0), (2, 1, 31, 3, 0.0),
+    (9, 3, 1, 2, 0.0),
+    # The limits: 512 requests (two per thread in the work prefix), uniform
+    # (aligned split of 512 row tiles) and ragged (one stream); the widest tree
+    # at 64 heads (64 row tiles of one request); 128 heads (a node per row tile).
+    (2, 8, 20, 512, 0.0), (3, 8, 40, 512, 0.9), (128, 64, 50, 1, 0.0), (9, 128, 100, 2, 0.0),
+])
+def test_verify_attn_shapes(Q, H, L, B, jitter):
+    """Decode (Q=1), the widest tree (Q=128, two bitset words), odd head counts,
+    tiny prefixes and the batch limit, with random trees."""
+    note(f"verify_attn shape Q={Q} H={H} L={L} B={B} jitter={jitter}")
+    rng = np.random.default_rng(Q * 1000 + H + B)
+    wl = workloads.make_workload("b1_l2k_q9", B=B, L=L, budget=Q - 1, H=H, D=8, K=16,
+                                 L_jitter=jitter)
     par = np.full((B, Q), -1, np.int32)
     for b in range(B):
         for i in range(1, Q):
