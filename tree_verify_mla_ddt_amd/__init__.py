@@ -16,7 +16,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libddt.so")
+# DDT_LIB names another build of the same library (the host-sanitized one).
+LIB_PATH = os.environ.get("DDT_LIB") or os.path.join(_HERE, "libddt.so")
 
 DDT_OK, DDT_EINVAL, DDT_EUNSUPPORTED, DDT_ELAUNCH = 0, -1, -2, -3
 DDT_F32, DDT_BF16 = 0, 1

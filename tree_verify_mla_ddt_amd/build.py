@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "libddt.so")
 # Host-side checker of the attention work split (CPU tests only).
-CHECK_PATH = os.path.join(HERE, "libddt_split_check.so")
+CHECK_PATH = os.environ.get("DDT_SPLIT_CHECK_LIB") or os.path.join(HERE, "libddt_split_check.so")
 # Measured ceilings of the attention tile (bench.py --ceiling).
 CEILING_PATH = os.path.join(HERE, "libddt_ceiling.so")
 SOURCES = ["api.hip", "draft_topk.hip", "tree_build.hip", "tree_accept.hip",
@@ -32,17 +32,43 @@ def hipcc_command(out_path: str, resource_report: bool = False) -> list[str]:
     return cmd
 
 
+def split_check_command(out_path: str) -> list[str]:
+    return ["hipcc", f"--offload-arch={ARCH}", "-O2", "-std=c++17", "-fPIC", "-shared",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            os.path.join(CSRC, "split_check.hip"), "-o", out_path]
+
+
 def build_split_check() -> str:
     """The host-only split checker (csrc/split_check.hip) as its own library."""
     tmp = CHECK_PATH + ".tmp"
-    cmd = ["hipcc", f"--offload-arch={ARCH}", "-O2", "-std=c++17", "-fPIC", "-shared",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           os.path.join(CSRC, "split_check.hip"), "-o", tmp]
-    res = subprocess.run(cmd, capture_output=True, text=True)
+    res = subprocess.run(split_check_command(tmp), capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}{res.stderr}")
     os.replace(tmp, CHECK_PATH)
     return CHECK_PATH
+
+
+# AddressSanitizer + UndefinedBehaviorSanitizer for the host pass only (each
+# option behind -Xarch_host); the device code is compiled as usual.  The host
+# code is the argument validation of every entry point, the launch planning and
+# the split checker.  Such a build needs clang's ASan runtime loaded first
+# (LD_PRELOAD) and is for CPU tests only.
+SAN_HOST_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer",
+                  "-Xarch_host", "-g", "-Xarch_host", "-O1"]
+
+
+def build_sanitized(out_dir: str) -> tuple[str, str]:
+    """libddt.so and the split checker with sanitized host code, into out_dir."""
+    os.makedirs(out_dir, exist_ok=True)
+    lib = os.path.join(out_dir, "libddt_san.so")
+    check = os.path.join(out_dir, "libddt_split_check_san.so")
+    for cmd in (hipcc_command(lib), split_check_command(check)):
+        cmd = cmd[:-2] + SAN_HOST_FLAGS + cmd[-2:]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}{res.stderr}")
+    return lib, check
 
 
 def build_ceiling() -> str:
