@@ -132,7 +132,7 @@ __global__ __launch_bounds__(kWave) void tree_build_kernel(
   // each pair is read or written (slots are handed out one per node at most);
   // std::false_type is the general pop.
   int n = 1;
-  auto pop = [&](auto low_tag) -> bool __attribute__((always_inline)) {
+  auto pop = [&](auto low_tag) __attribute__((always_inline)) -> bool {
     constexpr bool kLow = decltype(low_tag)::value;
     // The best key: the largest score word (one 32-bit DPP max), then, only
     // when several slots share it, the largest low word among them.  Live
