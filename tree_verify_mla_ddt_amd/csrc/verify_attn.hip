@@ -150,6 +150,12 @@ __device__ __forceinline__ long long uni(long long v) {
   const int hi = __builtin_amdgcn_readfirstlane((int)(v >> 32));
   return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
 }
+// The value lane `l` holds (l uniform).
+__device__ __forceinline__ long long lane_value(long long v, int l) {
+  const int lo = __builtin_amdgcn_readlane((int)(v & 0xFFFFFFFFll), l);
+  const int hi = __builtin_amdgcn_readlane((int)(v >> 32), l);
+  return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
+}
 
 // The split of a launch: mode (split_mode, -1 for one stream) and the start
 // cost c of a row tile in the stream.
@@ -158,77 +164,99 @@ struct SplitMode {
   int c;
 };
 
+// One DPP step of a wave scan: the value of the lane CTRL selects, 0 where it
+// selects none (rows outside ROW_MASK, lanes shifted in at a row's start).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_take(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ long long dpp_take(long long v) {
+  const uint64_t u = (uint64_t)v;
+  const uint32_t lo = (uint32_t)dpp_take<CTRL, ROW_MASK>((int)(uint32_t)u);
+  const uint32_t hi = (uint32_t)dpp_take<CTRL, ROW_MASK>((int)(uint32_t)(u >> 32));
+  return (long long)(((uint64_t)hi << 32) | lo);
+}
+
+// Inclusive sum over lanes 0..lane of a wavefront: shifts by 1, 2, 4, 8
+// inside each 16-lane row, then row 0's total into row 1 and row 2's into row
+// 3 (row_bcast:15), then the total of rows 0-1 into rows 2 and 3
+// (row_bcast:31).
+template <typename V>
+__device__ __forceinline__ V wave_inclusive_sum(V v) {
+  v += dpp_take<0x111, 0xF>(v);  // row_shr:1
+  v += dpp_take<0x112, 0xF>(v);  // row_shr:2
+  v += dpp_take<0x114, 0xF>(v);  // row_shr:4
+  v += dpp_take<0x118, 0xF>(v);  // row_shr:8
+  v += dpp_take<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
+  v += dpp_take<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
+  return v;
+}
+
 // Exclusive stream prefix over requests into s_pref[0..B] (each row tile with
 // work is a segment of nkb + c positions) and (when s_req is given) each
 // request's clamped prefix length and tree size into s_req[0..B); called by
-// all kBlock threads of a workgroup.  s_wsum holds 2 * kBlock / kWave values.
-// The split mode applies to a launch of 2G workgroups (split2), and c is
-// decided from the request sizes unless given (c_given >= 0, as the merge
-// kernels read it from the workspace).
+// all threads of a workgroup, computed by its first wave and published with
+// one barrier; s_wsum holds at least 2 values.  Request b sits in lane b % 64
+// of row b / 64; a row is one wave scan, so batches up to 64 take one.  The
+// split mode applies to a launch of 2G
+// workgroups (split2), and c is decided from the request sizes unless given
+// (c_given >= 0, as the merge kernels read it from the workspace).
 template <int kBlock>
 __device__ SplitMode work_prefix(long long* s_pref, long long* s_wsum, int2* s_req,
                                  const int32_t* prefix_len, const int32_t* n_nodes, int B, int Q,
                                  int H, int max_kv, int RT, long long G, bool split2,
                                  int c_given) {
-  constexpr int kPer = (kMaxBatch + kBlock - 1) / kBlock;  // requests per thread
-  constexpr int kW = kBlock / kWave;
+  static_assert(kBlock >= kWave, "one full wavefront computes the prefix");
+  constexpr int kRows = kMaxBatch / kWave;
   const int t = threadIdx.x;
-  const ReqInfo r0 = req_info(prefix_len, n_nodes, 0, Q, H, max_kv, RT);
-  long long w[kPer];
-  int v[kPer];
-  long long mine = 0, umine = 0;
-  int same = 1;
+  if (t < kWave) {
+    const ReqInfo r0 = req_info(prefix_len, n_nodes, 0, Q, H, max_kv, RT);
+    long long ew[kRows];  // work of the requests before this one
+    long long ev[kRows];  // row tiles with work before this one
+    long long wtot = 0, vtot = 0;
+    bool differs = false;
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    const int b = kPer * t + k;
-    w[k] = 0;
-    v[k] = 0;
-    if (b < B) {
-      const ReqInfo r = req_info(prefix_len, n_nodes, b, Q, H, max_kv, RT);
-      w[k] = (long long)r.vt * r.nkb;
-      v[k] = r.vt;
-      if (r.vt != r0.vt || r.nkb != r0.nkb) same = 0;
-      if (s_req) s_req[b] = make_int2(r.L, r.nb);
+    for (int k = 0; k < kRows; ++k) {
+      ew[k] = 0;
+      ev[k] = 0;
+      if (k * kWave < B) {
+        const int b = k * kWave + t;
+        long long w = 0, v = 0;
+        if (b < B) {
+          const ReqInfo r = req_info(prefix_len, n_nodes, b, Q, H, max_kv, RT);
+          w = (long long)r.vt * r.nkb;
+          v = r.vt;
+          if (r.vt != r0.vt || r.nkb != r0.nkb) differs = true;
+          if (s_req) s_req[b] = make_int2(r.L, r.nb);
+        }
+        const long long iw = wave_inclusive_sum(w);
+        const long long iv = wave_inclusive_sum(v);
+        ew[k] = wtot + iw - w;
+        ev[k] = vtot + iv - v;
+        wtot += lane_value(iw, kWave - 1);
+        vtot += lane_value(iv, kWave - 1);
+      }
     }
-    mine += w[k];
-    umine += v[k];
-  }
-  long long incl = mine, uincl = umine;
-  const int lane = t & 63, wv = t >> 6;
+    const bool same = __ballot(differs) == 0;
+    SplitMode sp;
+    sp.mode = split2 ? split_mode(same, r0.vt, B, G) : -1;
+    sp.c = c_given >= 0 ? c_given : unit_cost(sp.mode, same, vtot, G);
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const long long o = __shfl_up(incl, off);
-    const long long uo = __shfl_up(uincl, off);
-    if (lane >= off) {
-      incl += o;
-      uincl += uo;
+    for (int k = 0; k < kRows; ++k) {
+      const int b = k * kWave + t;
+      if (b < B) s_pref[b] = ew[k] + sp.c * ev[k];
+    }
+    if (t == 0) {
+      s_pref[B] = wtot + sp.c * vtot;
+      s_wsum[0] = sp.mode;
+      s_wsum[1] = sp.c;
     }
   }
-  if (lane == 63) {
-    s_wsum[wv] = incl;
-    s_wsum[kW + wv] = uincl;
-  }
-  same = __syncthreads_and(same);
-  long long before = 0, ubefore = 0, tot = 0, utot = 0;
-  for (int k = 0; k < kW; ++k) {
-    if (k < wv) {
-      before += s_wsum[k];
-      ubefore += s_wsum[kW + k];
-    }
-    tot += s_wsum[k];
-    utot += s_wsum[kW + k];
-  }
-  SplitMode sp;
-  sp.mode = split2 ? split_mode(same != 0, r0.vt, B, G) : -1;
-  sp.c = c_given >= 0 ? c_given : unit_cost(sp.mode, same != 0, utot, G);
-  long long run = before + incl - mine + sp.c * (ubefore + uincl - umine);
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    if (kPer * t + k < B) s_pref[kPer * t + k] = run;
-    run += w[k] + (long long)sp.c * v[k];
-  }
-  if (t == 0) s_pref[B] = tot + sp.c * utot;
   __syncthreads();
+  SplitMode sp;
+  sp.mode = s_wsum[0];
+  sp.c = (int)s_wsum[1];
   return sp;
 }
 
@@ -1052,33 +1080,49 @@ __device__ __forceinline__ void for_each_unit(SM& sm, const int32_t* __restrict_
   // last, so that at any moment the workgroups of one XCD (consecutive ranges,
   // mostly the same request) stream nearly the same key tiles and share them
   // in L2 instead of trailing each other by a range's offset.
-  const int b_head = b;
-  for (int pass = 0; pass < 2; ++pass) {
-  long long pos = start;
-  b = b_head;
-  while (pos < end) {
-    while (uni(sm.pref[b + 1]) <= pos) ++b;
-    b = uni(b);
-    const bool head = pos == start;
+  // The unit at stream position pos of request b (pref[b] <= pos).
+  auto unit_of = [&](long long pos, int b, long long& adv) __attribute__((always_inline)) {
     Unit u;
     u.b = b;
-    {
-      const int2 ln = sm.req[b];
-      u.ri = req_info_ln(uni(ln.x), uni(ln.y), H, RT);
-    }
+    const int2 ln = sm.req[b];
+    u.ri = req_info_ln(uni(ln.x), uni(ln.y), H, RT);
     const UnitPos up = unit_at(pos, end, uni(sm.pref[b]), u.ri, c);
     u.rt = up.rt;
     u.kb0 = up.kb0;
     u.kb1 = up.kb1;
     u.complete = up.complete;
-    u.slot = partial_slot(gid, head);
+    u.slot = partial_slot(gid, pos == start);
     u.nkeys = u.ri.L + u.ri.nb;
-    pos += up.adv;
+    adv = up.adv;
+    return u;
+  };
+  // The head is computed first (for its length); when later units follow it
+  // is computed again after them rather than kept across their runs.
+  long long adv;
+  Unit u = unit_of(start, b, adv);
+  long long pos = start + adv;
+  const int b_head = b;
+  bool later = pos < end;
+  bool head_left = true;
+  for (;;) {
+    if (later) {
+      if (pos < end) {
+        while (uni(sm.pref[b + 1]) <= pos) ++b;
+        b = uni(b);
+        u = unit_of(pos, b, adv);
+        pos += adv;
+      } else {
+        u = unit_of(start, b_head, adv);
+        later = false;
+        head_left = false;
+      }
+    } else if (head_left) {
+      head_left = false;  // u is the head
+    } else {
+      break;
+    }
     if (u.kb1 <= u.kb0) continue;  // the range ends inside this tile's start cost
-    if (head != (pass == 1)) continue;
     run(u, gid);
-    if (pass == 1) break;
-  }
   }
 }
 
