@@ -308,6 +308,16 @@ __device__ __forceinline__ int pe_swz(int c, int key) {
   else return c;
 }
 
+// A 16-byte store at device scope (sc1): it writes through this XCD's L2, so
+// the row leaves no dirty line behind for the release at the kernel's end,
+// which otherwise writes back every workgroup's output after the last one
+// finishes.  A vector store with no result register.
+__device__ __forceinline__ void store_through(float* d, const float4 v) {
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  const v4f x = {v.x, v.y, v.z, v.w};
+  __asm__ __volatile__("global_store_dwordx4 %0, %1, off sc1" : : "v"(d), "v"(x) : "memory");
+}
+
 // Direct global -> LDS load of 16 bytes per lane: lane l's bytes land at LDS
 // address lds + 16*l.  Issued as inline assembly: the compiler's wait-count
 // pass would otherwise make every later LDS read wait for these loads (it
@@ -1009,7 +1019,7 @@ __device__ __forceinline__ void run_unit(Smem<T, DL, DR>& sm, const Args& a, con
         const int r = 4 * i + (lane >> 4);
         const float4 v = *reinterpret_cast<const float4*>(buf + r * kPitch + 4 * c4);
         float* d = base + (long long)r * DL + (kCb0 + pass * kPCb) * 32 + 4 * c4;
-        if ((write_m >> r) & 1u) *reinterpret_cast<float4*>(d) = v;
+        if ((write_m >> r) & 1u) store_through(d, v);
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next pass overwrites
     }
@@ -1636,7 +1646,7 @@ __device__ __forceinline__ void run_unit_w(SmemW<DL, DR>& sm, const Args& a, con
       const int r = 4 * i + (lane >> 4);
       const float4 v = *reinterpret_cast<const float4*>(buf + r * kPitch + 4 * c4);
       float* d = base + (long long)r * DL + pass * kPCols + 4 * c4;
-      if ((write_m >> r) & 1u) *reinterpret_cast<float4*>(d) = v;
+      if ((write_m >> r) & 1u) store_through(d, v);
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next pass overwrites
   }
@@ -2034,7 +2044,7 @@ __device__ __forceinline__ void run_unit_n(SmemN<DL, DR>& sm, const Args& a, con
       const int r = 4 * i + (lane >> 4);
       const float4 v = *reinterpret_cast<const float4*>(buf + r * kPitch + 4 * c4);
       float* d = base + (long long)r * DL + pass * kPCols + 4 * c4;
-      if ((write_m >> r) & 1u) *reinterpret_cast<float4*>(d) = v;
+      if ((write_m >> r) & 1u) store_through(d, v);
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next pass overwrites
   }
