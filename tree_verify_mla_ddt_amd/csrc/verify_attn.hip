@@ -199,14 +199,12 @@ __device__ __forceinline__ V wave_inclusive_sum(V v) {
 // all threads of a workgroup, computed by its first wave and published with
 // one barrier; s_wsum holds at least 2 values.  Request b sits in lane b % 64
 // of row b / 64; a row is one wave scan, so batches up to 64 take one.  The
-// split mode applies to a launch of 2G
-// workgroups (split2), and c is decided from the request sizes unless given
-// (c_given >= 0, as the merge kernels read it from the workspace).
+// split mode applies to a launch of 2G workgroups (split2); the start cost c
+// follows from the split mode and the request sizes.
 template <int kBlock>
 __device__ SplitMode work_prefix(long long* s_pref, long long* s_wsum, int2* s_req,
                                  const int32_t* prefix_len, const int32_t* n_nodes, int B, int Q,
-                                 int H, int max_kv, int RT, long long G, bool split2,
-                                 int c_given) {
+                                 int H, int max_kv, int RT, long long G, bool split2) {
   static_assert(kBlock >= kWave, "one full wavefront computes the prefix");
   constexpr int kRows = kMaxBatch / kWave;
   const int t = threadIdx.x;
@@ -241,7 +239,7 @@ __device__ SplitMode work_prefix(long long* s_pref, long long* s_wsum, int2* s_r
     const bool same = __ballot(differs) == 0;
     SplitMode sp;
     sp.mode = split2 ? split_mode(same, r0.vt, B, G) : -1;
-    sp.c = c_given >= 0 ? c_given : unit_cost(sp.mode, same, vtot, G);
+    sp.c = unit_cost(sp.mode, same, vtot, G);
 #pragma unroll
     for (int k = 0; k < kRows; ++k) {
       const int b = k * kWave + t;
@@ -1054,7 +1052,7 @@ __device__ __forceinline__ void for_each_unit(SM& sm, const int32_t* __restrict_
   // Launched with 2G workgroups for the aligned split (see workgroup_range);
   // the kernel decides from the clamped request sizes whether it applies.
   const SplitMode sp = work_prefix<kThr>(sm.pref, sm.wsum, sm.req, prefix_len, n_nodes, B, Q, H,
-                                         max_kv, RT, Gn, kSplit2, -1);
+                                         max_kv, RT, Gn, kSplit2);
   const long long Wtot = uni(sm.pref[B]);
   const long long mode = uni(sp.mode);
   const int c = uni(sp.c);
@@ -2081,11 +2079,12 @@ void verify_attn_narrow_kernel(
 
 // Combines the partial results of row tiles whose key range was cut, and writes
 // the padding output of row tiles with no live row.  Two variants share the
-// contributor rule (slot 2g holds a workgroup's head unit, 2g+1 its tail):
+// contributor rule (slot 2g holds a workgroup's head unit, 2g+1 its tail) and
+// read the work prefix, split mode and start cost from the workspace (the
+// attention kernel's first workgroup stores them):
 //  * verify_merge_kernel (few row tiles, as at batch 1): thin workgroups of
-//    MergeGeo::kRows rows, so that many CUs share the work; the work prefix
-//    comes from the workspace (the attention kernel's first workgroup stores
-//    it); the contributing partial slots are compacted once into LDS; each
+//    MergeGeo::kRows rows, so that many CUs share the work; the contributing
+//    partial slots are compacted once into LDS; each
 //    row's total log-sum-exp is reduced by a group of lanes; then, for batches
 //    of MergeGeo::kBatch contributors, the per-(contributor, row) weights go to
 //    LDS and every thread accumulates its float4 chunks with all of a batch's
@@ -2117,13 +2116,16 @@ __global__ __launch_bounds__(kMergeThreads) void verify_merge_kernel(
   __shared__ float s_lv[MG::kBatch][MG::kRows];  // LSEs of the first batch's contributors
   __shared__ float s_w[MG::kBatch][MG::kRows];
   const int tid = threadIdx.x;
-  // Units in reverse: under the aligned split the row tiles to merge are the
-  // last ones, and are dispatched first this way.
-  const int u = (int)gridDim.x - 1 - (int)blockIdx.x;
+  // One workgroup per (row tile, row group), the row groups of a tile
+  // consecutive; row tiles in reverse: under the aligned split the tiles to
+  // merge are the last ones, and all their workgroups are dispatched before
+  // those of tiles with nothing to merge.
+  constexpr int kGroups = kRowsPerWG / MG::kRows;
+  const int u = (int)(gridDim.x / kGroups) - 1 - (int)(blockIdx.x / kGroups);
   const int b = u / RT, rt = u % RT;
   const ReqInfo ri = req_info(prefix_len, n_nodes, b, Q, H, max_kv, RT);
   const long long QH = (long long)Q * H;
-  const int r0 = blockIdx.y * MG::kRows;                   // first row within the tile
+  const int r0 = (int)(blockIdx.x % kGroups) * MG::kRows;  // first row within the tile
   if ((long long)rt * kRowsPerWG + r0 >= QH) return;
   // Work prefix over requests and the split mode, as the attention kernel
   // recorded them.
@@ -2267,8 +2269,8 @@ __global__ __launch_bounds__(kMergeThreads) void verify_merge_kernel(
   }
 }
 
-// The merge for many row tiles: 8 rows of 512 (16 of 64) per workgroup, the
-// work prefix recomputed per workgroup.  The first kMergePreW contributors'
+// The merge for many row tiles: 8 rows of 512 (16 of 64) per workgroup.  The
+// first kMergePreW contributors'
 // partial rows are requested before the row log-sum-exps are reduced (they do
 // not depend on them), and the log-sum-exps read for that reduction are kept
 // in LDS for the weights, so the bulk of the reads starts one dependent round
@@ -2283,7 +2285,8 @@ struct MergeGeoW {
   static_assert(kRowsPerWG % kRows == 0 && kLanesPerRow <= kWave, "merge tiling");
 };
 constexpr int kMergeBatchW = 32;  // contributors whose weights are staged at once
-constexpr int kMergePreW = 4;     // contributors whose rows are requested up front
+
+constexpr int kMergePreW = 3;     // contributors whose rows are requested up front
 
 template <int DL>
 __global__ __launch_bounds__(kMergeThreads) void verify_merge_wide_kernel(
@@ -2292,176 +2295,206 @@ __global__ __launch_bounds__(kMergeThreads) void verify_merge_wide_kernel(
     const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
     const long long* __restrict__ ws_pref) {
   using MG = MergeGeoW<DL>;
-  __shared__ long long s_pref[kMaxBatch + 1];
-  __shared__ long long s_wsum[2 * kMergeThreads / kWave];
   __shared__ int s_src[kMaxGrid];
   __shared__ int s_cnt;
   __shared__ float s_lse[MG::kRows];
   __shared__ float s_lv[kMergeBatchW][MG::kRows];  // LSEs of the first batch's contributors
   __shared__ float s_w[kMergeBatchW][MG::kRows];
-  // The split mode and start cost the attention kernel recorded; the aligned
-  // split needs no stream prefix.
+  // The stream prefix, split mode and start cost the attention kernel
+  // recorded.
   const long long mode = ws_pref[B + 1];
   const int c = (int)ws_pref[B + 2];
-  if (mode < 0)
-    work_prefix<kMergeThreads>(s_pref, s_wsum, nullptr, prefix_len, n_nodes, B, Q, H, max_kv, RT,
-                               grid_attn, false, c);
-  const int tid = threadIdx.x;
-  // Units in reverse: under the aligned split the row tiles to merge are the
-  // last ones, and are dispatched first this way.
-  const int u = (int)gridDim.x - 1 - (int)blockIdx.x;
-  const int b = u / RT, rt = u % RT;
-  const ReqInfo ri = req_info(prefix_len, n_nodes, b, Q, H, max_kv, RT);
-  const long long QH = (long long)Q * H;
-  const int r0 = blockIdx.y * MG::kRows;                   // first row within the tile
-  if ((long long)rt * kRowsPerWG + r0 >= QH) return;
-  const long long Gn = grid_attn;
+  // Under the aligned split every request has the same row-tile count vt0 =
+  // mode / B, and units b * vt0 + rt below q * G are whole (written by the
+  // attention kernel): such items are skipped without reading the request.
+  const long long q_whole = mode >= 0 ? (mode / grid_attn) * grid_attn : 0;
+  const int vt0 = mode >= 0 ? (int)(mode / B) : 0;
+  // One work item per (row tile, row group), the row groups of a tile
+  // consecutive and the row tiles in reverse: under the aligned split the
+  // tiles to merge are the last ones.  The grid holds at most the workgroups
+  // the chip keeps resident, each taking every gridDim.x-th item, so that
+  // items with nothing to merge (whole units under the aligned split) cost a
+  // few instructions instead of a dispatch.
+  constexpr int kGroups = kRowsPerWG / MG::kRows;
+  const int units = B * RT;
+  auto item = [&](int i) __attribute__((always_inline)) {
+    // The thread index through an empty asm, so that per-thread values are
+    // formed inside each item rather than hoisted and held across the loop.
+    int tid = threadIdx.x;
+    __asm__ __volatile__("" : "+v"(tid));
+    const int u = units - 1 - i / kGroups;
+    const int b = u / RT, rt = u % RT;
+    const long long QH = (long long)Q * H;
+    const int r0 = (i % kGroups) * MG::kRows;  // first row within the tile
+    if ((long long)rt * kRowsPerWG + r0 >= QH) return;
+    if (rt < vt0 && (long long)b * vt0 + rt < q_whole) return;
+    const ReqInfo ri = req_info(prefix_len, n_nodes, b, Q, H, max_kv, RT);
+    const long long Gn = grid_attn;
 
-  const bool has_work = rt < ri.vt;
-  if (has_work) {
-    long long S_u, Wtot, g_first, g_last;
-    if (!stream_place(mode, s_pref, B, b, rt, ri, Gn, c, S_u, Wtot)) return;  // a whole unit
-    tile_owners(S_u, Wtot, Gn, ri.nkb, c, g_first, g_last);
-    if (g_first == g_last) return;  // written directly by the attention kernel
-    // Each contributing workgroup (non-empty range) wrote its partial for this
-    // tile into slot 2g when the tile holds the start of its range, else 2g+1.
-    if (tid < kWave) {
-      const int cnt = (int)(g_last - g_first + 1);
-      int base = 0;
-      for (int k0 = 0; k0 < cnt; k0 += kWave) {
-        const long long gg = g_first + k0 + tid;
-        int src = -1;
-        if (k0 + tid < cnt) src = (int)contributor_slot(gg, S_u, Wtot, Gn);
-        const uint64_t m = __ballot(src >= 0);
-        const int at = base + (int)__builtin_amdgcn_mbcnt_hi(
-                                  (unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
-        if (src >= 0) s_src[at] = src;
-        base += __popcll(m);
-      }
-      if (tid == 0) s_cnt = base;
-    }
-  } else if (tid == 0) {
-    s_cnt = 0;
-  }
-  __syncthreads();
-  const int cnt = s_cnt;
-
-  // Rows of this thread's chunks and the first kMergePreW contributors' partial
-  // rows, requested now.  Rows that no contributor wrote (not live) read stale
-  // workspace; their sums are discarded below, and every address stays inside
-  // the workspace.
-  float4 acc[MG::kItems];
-  int rl_of[MG::kItems];
-#pragma unroll
-  for (int it = 0; it < MG::kItems; ++it) {
-    acc[it] = make_float4(0.f, 0.f, 0.f, 0.f);
-    rl_of[it] = (tid + it * kMergeThreads) / MG::kChunks;
-  }
-  const int chunk = tid % MG::kChunks;
-  const int npre = cnt < kMergePreW ? cnt : kMergePreW;
-  float4 pre[kMergePreW][MG::kItems];
-#pragma unroll
-  for (int k = 0; k < kMergePreW; ++k) {
-#pragma unroll
-    for (int it = 0; it < MG::kItems; ++it) pre[k][it] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (k < npre) {
-      const float* src = ws_o + ((long long)s_src[k] * kRowsPerWG + r0) * DL + chunk * 4;
-#pragma unroll
-      for (int it = 0; it < MG::kItems; ++it)
-        pre[k][it] = *reinterpret_cast<const float4*>(src + (long long)rl_of[it] * DL);
-    }
-  }
-
-  // Row log-sum-exp: kLanesPerRow lanes per row, each over every
-  // kLanesPerRow-th contributor (keeping the first batch's values in LDS),
-  // then a butterfly over the group.
-  {
-    const int rl = tid / MG::kLanesPerRow, j = tid % MG::kLanesPerRow;
-    const int rr = r0 + rl;
-    const long long r_loc = (long long)rt * kRowsPerWG + rr;
-    const bool live = r_loc < QH && (int)(r_loc / H) < ri.nb;
-    float m = -INFINITY, z = 0.0f;
-    for (int k = j; k < kMergeBatchW; k += MG::kLanesPerRow) s_lv[k][rl] = -INFINITY;
-    if (live) {
-      for (int k = j; k < cnt; k += MG::kLanesPerRow) {
-        const float v = ws_lse[(long long)s_src[k] * kRowsPerWG + rr];
-        if (k < kMergeBatchW) s_lv[k][rl] = v;
-        if (v == -INFINITY) continue;
-        if (v > m) {
-          z = z * __expf(m - v) + 1.0f;
-          m = v;
-        } else {
-          z += __expf(v - m);
+    const bool has_work = rt < ri.vt;
+    if (has_work) {
+      long long S_u, Wtot, g_first, g_last;
+      if (!stream_place(mode, ws_pref, B, b, rt, ri, Gn, c, S_u, Wtot)) return;  // a whole unit
+      tile_owners(S_u, Wtot, Gn, ri.nkb, c, g_first, g_last);
+      if (g_first == g_last) return;  // written directly by the attention kernel
+      // Each contributing workgroup (non-empty range) wrote its partial for this
+      // tile into slot 2g when the tile holds the start of its range, else 2g+1.
+      if (tid < kWave) {
+        const int cnt = (int)(g_last - g_first + 1);
+        int base = 0;
+        for (int k0 = 0; k0 < cnt; k0 += kWave) {
+          const long long gg = g_first + k0 + tid;
+          int src = -1;
+          if (k0 + tid < cnt) src = (int)contributor_slot(gg, S_u, Wtot, Gn);
+          const uint64_t m = __ballot(src >= 0);
+          const int at = base + (int)__builtin_amdgcn_mbcnt_hi(
+                                    (unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+          if (src >= 0) s_src[at] = src;
+          base += __popcll(m);
         }
+        if (tid == 0) s_cnt = base;
       }
-    }
-#pragma unroll
-    for (int off = 1; off < MG::kLanesPerRow; off <<= 1) {
-      const float m2 = __shfl_xor(m, off), z2 = __shfl_xor(z, off);
-      const float mn = fmaxf(m, m2);
-      if (mn != -INFINITY) {
-        z = (m == -INFINITY ? 0.0f : z * __expf(m - mn)) +
-            (m2 == -INFINITY ? 0.0f : z2 * __expf(m2 - mn));
-        m = mn;
-      }
-    }
-    if (j == 0) s_lse[rl] = z > 0.0f ? m + __logf(z) : -INFINITY;
-  }
-  __syncthreads();
-
-  for (int k0 = 0; k0 < cnt; k0 += kMergeBatchW) {
-    const int nk = cnt - k0 < kMergeBatchW ? cnt - k0 : kMergeBatchW;
-    for (int e = tid; e < kMergeBatchW * MG::kRows; e += kMergeThreads) {
-      const int k = e / MG::kRows, rl = e % MG::kRows;
-      const float lt = s_lse[rl];
-      float w = 0.0f;
-      if (k < nk && lt != -INFINITY) {
-        const float v = k0 == 0 ? s_lv[k][rl]
-                                : ws_lse[(long long)s_src[k0 + k] * kRowsPerWG + r0 + rl];
-        if (v != -INFINITY) w = __expf(v - lt);
-      }
-      s_w[k][rl] = w;
+    } else if (tid == 0) {
+      s_cnt = 0;
     }
     __syncthreads();
-    if (k0 == 0) {
+    const int cnt = s_cnt;
+
+    // Rows of this thread's chunks and the first kMergePreW contributors' partial
+    // rows, requested now.  Rows that no contributor wrote (not live) read stale
+    // workspace; their sums are discarded below, and every address stays inside
+    // the workspace.
+    float4 acc[MG::kItems];
+    int rl_of[MG::kItems];
 #pragma unroll
-      for (int k = 0; k < kMergePreW; ++k) {
-        if (k >= npre) break;
+    for (int it = 0; it < MG::kItems; ++it) {
+      acc[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+      rl_of[it] = (tid + it * kMergeThreads) / MG::kChunks;
+    }
+    const int chunk = tid % MG::kChunks;
+    const int npre = cnt < kMergePreW ? cnt : kMergePreW;
+    float4 pre[kMergePreW][MG::kItems];
+#pragma unroll
+    for (int k = 0; k < kMergePreW; ++k) {
+#pragma unroll
+      for (int it = 0; it < MG::kItems; ++it) pre[k][it] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (k < npre) {
+        const float* src = ws_o + ((long long)s_src[k] * kRowsPerWG + r0) * DL + chunk * 4;
+#pragma unroll
+        for (int it = 0; it < MG::kItems; ++it)
+          pre[k][it] = *reinterpret_cast<const float4*>(src + (long long)rl_of[it] * DL);
+      }
+    }
+
+    // Row log-sum-exp: kLanesPerRow lanes per row, each over every
+    // kLanesPerRow-th contributor (keeping the first batch's values in LDS),
+    // then a butterfly over the group.
+    {
+      const int rl = tid / MG::kLanesPerRow, j = tid % MG::kLanesPerRow;
+      const int rr = r0 + rl;
+      const long long r_loc = (long long)rt * kRowsPerWG + rr;
+      const bool live = r_loc < QH && (int)(r_loc / H) < ri.nb;
+      float m = -INFINITY, z = 0.0f;
+      for (int k = j; k < kMergeBatchW; k += MG::kLanesPerRow) s_lv[k][rl] = -INFINITY;
+      if (live) {
+        for (int k = j; k < cnt; k += MG::kLanesPerRow) {
+          const float v = ws_lse[(long long)s_src[k] * kRowsPerWG + rr];
+          if (k < kMergeBatchW) s_lv[k][rl] = v;
+          if (v == -INFINITY) continue;
+          if (v > m) {
+            z = z * __expf(m - v) + 1.0f;
+            m = v;
+          } else {
+            z += __expf(v - m);
+          }
+        }
+      }
+#pragma unroll
+      for (int off = 1; off < MG::kLanesPerRow; off <<= 1) {
+        const float m2 = __shfl_xor(m, off), z2 = __shfl_xor(z, off);
+        const float mn = fmaxf(m, m2);
+        if (mn != -INFINITY) {
+          z = (m == -INFINITY ? 0.0f : z * __expf(m - mn)) +
+              (m2 == -INFINITY ? 0.0f : z2 * __expf(m2 - mn));
+          m = mn;
+        }
+      }
+      if (j == 0) s_lse[rl] = z > 0.0f ? m + __logf(z) : -INFINITY;
+    }
+    __syncthreads();
+
+    for (int k0 = 0; k0 < cnt; k0 += kMergeBatchW) {
+      const int nk = cnt - k0 < kMergeBatchW ? cnt - k0 : kMergeBatchW;
+      for (int e = tid; e < kMergeBatchW * MG::kRows; e += kMergeThreads) {
+        const int k = e / MG::kRows, rl = e % MG::kRows;
+        const float lt = s_lse[rl];
+        float w = 0.0f;
+        if (k < nk && lt != -INFINITY) {
+          const float v = k0 == 0 ? s_lv[k][rl]
+                                  : ws_lse[(long long)s_src[k0 + k] * kRowsPerWG + r0 + rl];
+          if (v != -INFINITY) w = __expf(v - lt);
+        }
+        s_w[k][rl] = w;
+      }
+      __syncthreads();
+      if (k0 == 0) {
+#pragma unroll
+        for (int k = 0; k < kMergePreW; ++k) {
+          if (k >= npre) break;
+#pragma unroll
+          for (int it = 0; it < MG::kItems; ++it) {
+            const float w = s_w[k][rl_of[it]];
+            acc[it].x = __builtin_fmaf(w, pre[k][it].x, acc[it].x);
+            acc[it].y = __builtin_fmaf(w, pre[k][it].y, acc[it].y);
+            acc[it].z = __builtin_fmaf(w, pre[k][it].z, acc[it].z);
+            acc[it].w = __builtin_fmaf(w, pre[k][it].w, acc[it].w);
+          }
+        }
+      }
+#pragma unroll 8
+      for (int k = k0 == 0 ? npre : 0; k < nk; ++k) {
+        const float* src = ws_o + ((long long)s_src[k0 + k] * kRowsPerWG + r0) * DL + chunk * 4;
 #pragma unroll
         for (int it = 0; it < MG::kItems; ++it) {
           const float w = s_w[k][rl_of[it]];
-          acc[it].x = __builtin_fmaf(w, pre[k][it].x, acc[it].x);
-          acc[it].y = __builtin_fmaf(w, pre[k][it].y, acc[it].y);
-          acc[it].z = __builtin_fmaf(w, pre[k][it].z, acc[it].z);
-          acc[it].w = __builtin_fmaf(w, pre[k][it].w, acc[it].w);
+          const float4 v = *reinterpret_cast<const float4*>(src + (long long)rl_of[it] * DL);
+          acc[it].x = __builtin_fmaf(w, v.x, acc[it].x);
+          acc[it].y = __builtin_fmaf(w, v.y, acc[it].y);
+          acc[it].z = __builtin_fmaf(w, v.z, acc[it].z);
+          acc[it].w = __builtin_fmaf(w, v.w, acc[it].w);
         }
       }
+      __syncthreads();
     }
-#pragma unroll 8
-    for (int k = k0 == 0 ? npre : 0; k < nk; ++k) {
-      const float* src = ws_o + ((long long)s_src[k0 + k] * kRowsPerWG + r0) * DL + chunk * 4;
 #pragma unroll
-      for (int it = 0; it < MG::kItems; ++it) {
-        const float w = s_w[k][rl_of[it]];
-        const float4 v = *reinterpret_cast<const float4*>(src + (long long)rl_of[it] * DL);
-        acc[it].x = __builtin_fmaf(w, v.x, acc[it].x);
-        acc[it].y = __builtin_fmaf(w, v.y, acc[it].y);
-        acc[it].z = __builtin_fmaf(w, v.z, acc[it].z);
-        acc[it].w = __builtin_fmaf(w, v.w, acc[it].w);
-      }
+    for (int it = 0; it < MG::kItems; ++it) {
+      const long long r_loc = (long long)rt * kRowsPerWG + r0 + rl_of[it];
+      if (r_loc >= QH) continue;
+      const long long grow = (long long)b * QH + r_loc;
+      const float lt = s_lse[rl_of[it]];
+      *reinterpret_cast<float4*>(out + grow * DL + chunk * 4) =
+          lt != -INFINITY ? acc[it] : make_float4(0.f, 0.f, 0.f, 0.f);
+      if (lse && chunk == 0) lse[grow] = lt;
     }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int it = 0; it < MG::kItems; ++it) {
-    const long long r_loc = (long long)rt * kRowsPerWG + r0 + rl_of[it];
-    if (r_loc >= QH) continue;
-    const long long grow = (long long)b * QH + r_loc;
-    const float lt = s_lse[rl_of[it]];
-    *reinterpret_cast<float4*>(out + grow * DL + chunk * 4) =
-        lt != -INFINITY ? acc[it] : make_float4(0.f, 0.f, 0.f, 0.f);
-    if (lse && chunk == 0) lse[grow] = lt;
-  }
+    __syncthreads();  // the next item rewrites the LDS this one read
+  };
+#pragma unroll 1
+  for (int i = blockIdx.x; i < units * kGroups; i += gridDim.x) item(i);
+}
+
+// Workgroups of the wide merge: all its items, or as many as the chip keeps
+// resident at once (from the compiled kernel's occupancy), whichever is fewer.
+template <int DL>
+int merge_wide_grid(int items, int num_cu) {
+  static const int per_cu = [] {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, verify_merge_wide_kernel<DL>,
+                                                     kMergeThreads, 0) != hipSuccess || n < 1)
+      n = 1;
+    return n;
+  }();
+  const long long resident = (long long)per_cu * (num_cu > 0 ? num_cu : 256);
+  return items < resident ? items : (int)resident;
 }
 
 // Polls of a pair wait before it gives up.  DDT_PAIR_SPIN_LIMIT (read once)
@@ -2529,12 +2562,13 @@ hipError_t launch_impl(const void* q_lat, const void* q_pe, const void* c_kv, co
   const int units = B * plan.row_tiles;
   constexpr int kRn = MergeGeoW<DL>::kRows, kRs = DL >= 256 ? 2 : 16;
   if (units * (kRowsPerWG / kRn) < plan.num_cu)
-    hipLaunchKernelGGL((verify_merge_kernel<DL, kRs>), dim3(units, kRowsPerWG / kRs),
+    hipLaunchKernelGGL((verify_merge_kernel<DL, kRs>), dim3(units * (kRowsPerWG / kRs)),
                        dim3(kMergeThreads), 0, stream, prefix_len, n_nodes, B, Q, H,
                        plan.row_tiles, max_kv, plan.grid, out, lse, ws_o, ws_lse, ws_pref);
   else
     hipLaunchKernelGGL((verify_merge_wide_kernel<DL>),
-                       dim3(units, kRowsPerWG / MergeGeoW<DL>::kRows), dim3(kMergeThreads), 0,
+                       dim3(merge_wide_grid<DL>(units * (kRowsPerWG / kRn), plan.num_cu)),
+                       dim3(kMergeThreads), 0,
                        stream, prefix_len, n_nodes, B, Q, H, plan.row_tiles, max_kv, plan.grid,
                        out, lse, ws_o, ws_lse, ws_pref);
   return hipGetLastError();
