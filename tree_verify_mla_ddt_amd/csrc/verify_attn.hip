@@ -10,47 +10,55 @@
 //
 // Mapping to CDNA4:
 //  * Rows of a request are (node, head) pairs, row = i*H + h, so one request is
-//    an M = Q*H by 576 query matrix against its shared keys.  A workgroup owns a
-//    tile of 128 rows and streams 32-key tiles.  Its 8 waves form 4 pairs; a
-//    pair shares 32 rows and splits both contractions in half: each wave holds
-//    half of the query dimensions (QK^T) and half of the output columns (PV),
-//    so a wave keeps 72 + 128 registers of state and two waves fit per SIMD.
-//    The two partial score blocks of a pair are summed through LDS.
-//  * One key-major LDS tile per stage serves both products.  Scores are
-//    computed transposed, S^T = K Q^T, with the 32x32x16 bf16 MFMA (fp32
-//    inputs: 32x32x2 f32): the query rows stay in registers as the B operand,
-//    the key rows are the A operand (16-byte LDS reads).  In the accumulator
-//    layout each lane then owns one row and 16 of the 32 keys -- exactly the B
-//    operand layout of O^T = V^T P^T -- so probabilities never leave registers.
-//    The V^T operand comes from the same key-major tile through the gfx950
-//    transposing LDS read (ds_read_b64_tr_b16): in each 16-lane group, lanes
-//    4e..4e+3 point at 4-column pieces of key row k0+e and lane i receives
-//    column i of keys k0..k0+3.
-//  * Tiles are loaded global -> LDS directly (16 bytes per lane, no register
-//    staging), one tile ahead, into two LDS stages; the pool slot ids of each
-//    tile are fetched two tiles ahead into a small LDS ring.
-//  * Online softmax in the exp2 domain with fp32 statistics and a lazily moved
-//    reference max (accumulators are rescaled only when a row's max grows by
-//    more than 2^8, so in steady state there is no per-tile rescale); the
-//    probabilities are rounded to bf16 (round to nearest even) for the value product.  When a
-//    tile holds a key whose weight is a sizeable share of its row's running sum
-//    (concentrated attention, short contexts), the bf16 rounding residual of
-//    the probabilities goes through a second MFMA against the same value
-//    operand, which brings the value product to ~2^-16 relative accuracy.
+//    an M = Q*H by 576 query matrix against its shared keys.  A row tile is 128
+//    rows; keys stream in tiles of 32, loaded global -> LDS directly (16 bytes
+//    per lane, no register staging) one tile ahead into a ring of three stages,
+//    with the pool slot ids of each tile fetched two tiles ahead into a small
+//    LDS ring.  All products are 32x32x16 bf16 MFMAs (fp32 inputs: 32x32x2
+//    f32) with fp32 accumulation.
+//  * Three forms of the same computation:
+//     - wide (bf16 512+64, the default): four waves per workgroup, one per
+//       SIMD, each owning 32 rows with their whole query (36 operand
+//       registers) and whole output (the 256 accumulator registers), so both
+//       contractions and the softmax of a row stay inside one wave; the
+//       softmax of tile t runs while the value product of tile t-1 does;
+//     - narrow (bf16 512+64, very few row tiles, as at batch 1): four
+//       workgroups of 32 rows share each key range; inside one, the four waves
+//       split the score contraction and the output columns, and sum their
+//       partial scores in LDS;
+//     - paired-wave (64-wide latent rows, bf16 and fp32): two waves per 32
+//       rows, each with half of the query dimensions and half of the output
+//       columns, exchanging partial scores through LDS.
+//    Scores are computed transposed, S^T = K Q^T, so that in the accumulator
+//    layout each lane owns one row and 16 of the 32 keys -- the B operand
+//    layout of O^T = V^T P^T -- and probabilities never leave registers.  The
+//    V^T operand comes from the same key-major tile through the transposing
+//    LDS read (ds_read_b64_tr_b16).
+//  * Softmax in the exp2 domain with fp32 statistics.  The wide and narrow
+//    forms use a fixed reference per row (its first tile's max) and run a
+//    range again from its start, with the largest score seen as reference, in
+//    the rare case that a later score would overflow; the paired-wave form
+//    moves its reference when a row's max grows by more than 2^8.  The
+//    probabilities are rounded to bf16 for the value product; when a tile
+//    holds a key whose weight is a sizeable share of its row's running sum,
+//    the bf16 rounding residual goes through a second MFMA against the same
+//    value operand, which brings the value product to ~2^-16 relative
+//    accuracy.
 //  * The mask: prefix keys are always visible; a tree key k is visible when bit
 //    k of the row's node bitset is set; keys beyond the request or with a slot
 //    id outside the pool are invisible (their tile rows hold pool row 0, which
 //    a zero probability then ignores).
-//  * Work split: the (request, row tile, key tile) space is cut into equal
-//    contiguous ranges, one per workgroup of a grid sized to the chip, so
-//    ragged prefixes stay balanced.  A row tile whose key range is cut writes
-//    normalised partial outputs plus their log-sum-exp to the workspace and a
-//    merge kernel combines them; uncut tiles write the output directly.
-//    Logical workgroup ids are remapped so that consecutive ranges (same
-//    request, same keys) land on the same XCD and share its L2.  Uniform
-//    batches with at least one row tile per workgroup take an aligned split
-//    instead (twice the workgroups: whole row tiles first, then the leftover
-//    row tiles cut evenly), which leaves far fewer row tiles to merge.
+//  * Work split (attn_split.h): the (request, row tile, key tile) space is cut
+//    into equal contiguous ranges, one per workgroup of a grid sized to the
+//    chip, so ragged prefixes stay balanced; uniform batches with at least one
+//    row tile per workgroup take an aligned split instead (whole row tiles
+//    first, then the leftover row tiles cut evenly).  Logical workgroup ids are
+//    remapped so that consecutive ranges land on the same XCD and share its L2.
+//    A row tile whose key range is cut writes normalised partial outputs plus
+//    their log-sum-exp to the workspace, and a merge kernel combines them.
+//  * Output and partial rows are stored at device scope (write-through past the
+//    XCD's L2), so the kernel's end has no dirty lines to write back before the
+//    merge may start.
 #include <stdlib.h>
 
 #include <type_traits>
