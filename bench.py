@@ -587,6 +587,11 @@ def main():
                     help="headline workload (default: the batch-1 configuration)")
     ap.add_argument("--ceiling", action="store_true",
                     help="run the MFMA / attention-tile ceiling microbenchmark and exit")
+    ap.add_argument("--kernel-timing-only", action="store_true",
+                    help="run only the live kernel timing of the workload (the attention "
+                         "kernel, then the merge kernel, each launched --steps times back to "
+                         "back per repeat) and print it: a profiler's trace of this command "
+                         "holds exactly the launches the roofline's kernel time comes from")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="record the workload's HBM bytes per attention call from two "
                          "rocprofv3 --pmc output directories (FETCH_SIZE, WRITE_SIZE) and exit")
@@ -612,6 +617,13 @@ def main():
 
     primary = args.workload
     runner = StepRunner(primary, torch, ddt, workloads)
+    if args.kernel_timing_only:
+        runner.kernel_times(args.steps, repeats=1)  # warm-up
+        torch.cuda.synchronize()
+        t_kern, t_merge = runner.kernel_times(args.steps)
+        print(json.dumps({"workload": primary, "attn_kernel_us": t_kern.summary(),
+                          "merge_kernel_us": t_merge.summary()}))
+        return
     if args.copy_calibration:
         src = torch.empty((256 << 20,), dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
